@@ -1,0 +1,216 @@
+/*
+ * akv.h -- split-KV, two-tier decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * A key/value history is held in two tiers (ActiveKV, "Context beyond VRAM",
+ * section "What I built": recent context stays exact, older history is held in
+ * a compact form the GPU reads directly, and the two are merged with exact
+ * attention arithmetic):
+ *
+ *   exact tier       bfloat16 K and V, paged in 64-token blocks;
+ *   compressed tier  K and V rotated by the normalized Walsh-Hadamard matrix
+ *                    H_d/sqrt(d), cut into 32-element groups, each group stored
+ *                    as one fp16 RMS scale plus 4-bit indices into the 16-level
+ *                    Lloyd-Max table for N(0,1).  Because the rotation keeps dot
+ *                    products, the query is rotated once instead of inverse-
+ *                    rotating the blocks (QuantForge walkthrough, section 1,
+ *                    "Triton Fused Kernels").
+ *
+ * Each tier is attended in fixed-size token splits; every split yields a
+ * normalized partial output and its log-sum-exp (the attention statistic that
+ * "Bringing a serving stack up on new silicon", section "What I built", adds to
+ * the paged-attention path), and the partials are combined by an exact
+ * log-sum-exp merge in a fixed order, so repeated calls are bit-identical.
+ *
+ * Conventions for every entry point (the port described in "PyTorch",
+ * section "Native operators inside vLLM", kept shapes, dtypes, lifetimes, the
+ * caller's device stream and the order of error reports):
+ *   - all tensor pointers are DEVICE pointers unless stated; the caller owns
+ *     every buffer (including the workspace) and keeps it alive until the work
+ *     enqueued on `stream` has finished;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream);
+ *     the library only enqueues work on it, never synchronizes, never
+ *     allocates or frees device memory, and keeps no pointer after returning;
+ *   - arguments are validated on the host before anything is enqueued, in the
+ *     fixed order NULL -> SHAPE -> UNSUPPORTED -> ALIGN -> WORKSPACE; the first
+ *     failure is returned and nothing has been enqueued.  A request that cannot
+ *     be served is refused, never truncated (ActiveKV, "What I built":
+ *     unservable requests are refused);
+ *   - a HIP launch failure returns AKV_ERR_HIP; akv_last_error() then holds
+ *     the HIP error string.  akv_last_error() is thread-local.
+ *   - device-side data errors that the host cannot see (a block-table entry
+ *     outside [0, num_blocks), a length above 64*max_blocks) make the affected
+ *     (sequence, head) outputs NaN instead of faulting.
+ *
+ * ---------------------------------------------------------------- layouts
+ * Hkv = key/value heads, d = head dimension (64 or 128), G = Hq/Hkv <= 8;
+ * query head h reads key/value head h / G.  A block holds 64 tokens.
+ *
+ * Exact tier pools K, V: bf16, element (block p, kv head k, token r, dim t) at
+ *   ((p*Hkv + k)*64 + r)*d + t.
+ *
+ * Compressed tier: one slab of 32*d code bytes and one slab of 2*d fp16
+ * scales per (block p, kv head k), at byte offset (p*Hkv + k)*32*d and element
+ * offset (p*Hkv + k)*2*d.  Codes are 4-bit values 0..15; byte = lo | hi << 4.
+ *   K codes: token r owns bytes [r*d/2, (r+1)*d/2); inside that row, byte
+ *     (d/8)*a + 4*m + b  (a = 0..3, m = 0..d/32-1, b = 0..3) holds dims
+ *     32m + 8a + 2b (low nibble) and 32m + 8a + 2b + 1 (high nibble).
+ *   V codes: byte ((c*4 + a)*16 + i)*(d/4) + 4*t + b  (c = 0..1, a = 0..3,
+ *     i = 0..15, t = 0..d/16-1, b = 0..3) holds dim 16t + i of tokens
+ *     32c + 8a + 2b (low nibble) and 32c + 8a + 2b + 1 (high nibble).
+ *   K and V scales: fp16, element g*64 + r = group g (dims 32g..32g+31) of
+ *     token r.
+ * These orders put each lane's matrix-core operand in one contiguous load.
+ * Dequantized (rotated-space) value of dim t of a token: C[code] * scale(t/32),
+ * with C the Lloyd-Max table; the unrotated vector is (H_d/sqrt(d)) times it.
+ *
+ * Block tables: int32 [B][max_blocks]; entry j of row b is the pool block of
+ * tier-local tokens [64j, 64j+64) of sequence b.  Tier lengths: int32 [B].
+ * In the attended history of a sequence the compressed tier comes first
+ * (older), then the exact tier.
+ */
+#ifndef AKV_H
+#define AKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AKV_ABI_VERSION 1
+#define AKV_BLOCK_TOKENS 64
+#define AKV_GROUP 32
+/* Fixed split rule (a length-only rule, so repeated calls partition the
+ * history identically): a tier of n tokens is cut into ceil(n / P) splits of
+ * P tokens, the last one shorter.  P defaults below; a descriptor may pass
+ * another multiple of 64. */
+#define AKV_SPLIT_TOKENS_EXACT_DEFAULT 2048
+#define AKV_SPLIT_TOKENS_QUANT_DEFAULT 1024
+#define AKV_MAX_CHUNK 512
+
+typedef enum akv_status {
+  AKV_OK = 0,
+  AKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  AKV_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+  AKV_ERR_UNSUPPORTED = -3, /* a valid request this library does not serve */
+  AKV_ERR_ALIGN = -5,       /* a pointer is not aligned as required */
+  AKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required */
+  AKV_ERR_HIP = -6          /* HIP reported an error while enqueuing */
+} akv_status;
+
+/* Exact (bf16) tier of a batch.  Absent when max_blocks == 0 (then the
+ * pointers may be NULL and every sequence has 0 exact tokens). */
+typedef struct akv_exact_tier {
+  const uint16_t* k;           /* bf16 pool, layout above */
+  const uint16_t* v;           /* bf16 pool */
+  const int32_t* block_table;  /* [B][max_blocks] */
+  const int32_t* lengths;      /* [B], 0 <= len <= 64*max_blocks */
+  int32_t max_blocks;          /* row stride of block_table */
+  int32_t num_blocks;          /* blocks in each pool */
+} akv_exact_tier;
+
+/* Compressed (4-bit) tier of a batch.  Absent when max_blocks == 0. */
+typedef struct akv_quant_tier {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint16_t* k_scales;    /* fp16 */
+  const uint16_t* v_scales;    /* fp16 */
+  const int32_t* block_table;  /* [B][max_blocks] */
+  const int32_t* lengths;      /* [B] */
+  int32_t max_blocks;
+  int32_t num_blocks;
+} akv_quant_tier;
+
+/* One attention call over a batch.  For akv_attend_decode Tq must be 1.
+ * For akv_attend_chunk Tq = T (1..512) causal queries: the caller has already
+ * appended the chunk's own K/V as the last T exact-tier tokens, and query i
+ * (0-based) of a sequence sees the whole compressed tier, the exact tier up
+ * to and including exact token len_exact - T + i. */
+typedef struct akv_attn_desc {
+  uint32_t struct_size;        /* sizeof(akv_attn_desc) */
+  int32_t B, Hq, Hkv, d, Tq;
+  float softmax_scale;         /* 0 => 1/sqrt(d) */
+  const uint16_t* q;           /* bf16 [B][Tq][Hq][d], 4-byte aligned */
+  akv_exact_tier exact;
+  akv_quant_tier quant;
+  int32_t split_tokens_exact;  /* 0 => AKV_SPLIT_TOKENS_EXACT_DEFAULT */
+  int32_t split_tokens_quant;  /* 0 => AKV_SPLIT_TOKENS_QUANT_DEFAULT */
+  float* o;                    /* fp32 [B][Tq][Hq][d] normalized output */
+  float* lse;                  /* fp32 [B][Tq][Hq] natural-log sum of exp(scores) */
+} akv_attn_desc;
+
+typedef akv_attn_desc akv_decode_desc;
+typedef akv_attn_desc akv_chunk_desc;
+
+/* Move n_tokens tokens of one sequence from the exact tier into the
+ * compressed tier (ActiveKV's compact older history; encoding per the
+ * Walsh-Hadamard rotation of the QuantForge walkthrough, section 1).  For each
+ * token, kv head and K|V the bf16 vector is rotated by the unnormalized
+ * Walsh-Hadamard butterflies in fp32, scaled by RN(1/sqrt(d)), each 32-group
+ * gets scale = fp16(sqrt(mean of squares)) and every element the index of
+ * the nearest Lloyd-Max level to value/scale (exact ties to the lower index;
+ * all-zero groups give index 7).  Codes and scales are bit-exact functions of
+ * the input.  Source tokens [src_start, src_start+n_tokens) of the exact
+ * tier's block table land at compressed positions [dst_start, dst_start +
+ * n_tokens).  dst_start must be even (two tokens share a V byte); for odd
+ * n_tokens the unused half of the last V byte is written as 0. */
+typedef struct akv_compress_desc {
+  uint32_t struct_size;        /* sizeof(akv_compress_desc) */
+  int32_t Hkv, d;
+  const uint16_t* src_k;       /* bf16 exact-tier pools */
+  const uint16_t* src_v;
+  const int32_t* src_block_table;  /* [src_max_blocks] one sequence's row */
+  int32_t src_max_blocks, src_num_blocks;
+  int32_t src_start, n_tokens;
+  uint8_t* dst_k_codes;
+  uint8_t* dst_v_codes;
+  uint16_t* dst_k_scales;
+  uint16_t* dst_v_scales;
+  const int32_t* dst_block_table;  /* [dst_max_blocks] */
+  int32_t dst_max_blocks, dst_num_blocks;
+  int32_t dst_start;
+} akv_compress_desc;
+
+/* ABI version of the loaded library (AKV_ABI_VERSION at build time). */
+int akv_abi_version(void);
+
+/* Thread-local text for the last non-OK status returned on this thread. */
+const char* akv_last_error(void);
+
+/* Bytes of workspace akv_attend_decode / akv_attend_chunk need for `desc`
+ * (per-split partial outputs and statistics).  Returns 0 if desc is invalid. */
+size_t akv_decode_workspace_bytes(const akv_attn_desc* desc);
+size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc);
+
+/* Split-KV decode attention, one query token per sequence.
+ * Enqueues: one split kernel (both tiers; the compressed tier with the
+ * pre-rotated query and the value sum kept in rotated space) and one merge
+ * kernel (merge compressed-tier partials, inverse-rotate once per head, merge
+ * with the exact-tier partials).  ws must be 256-byte aligned and at least
+ * akv_decode_workspace_bytes(desc) bytes. */
+akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill-chunk attention: Tq causal queries per sequence over the two-tier
+ * history (matrix-core tiles), then the same merge.  ws as above with
+ * akv_chunk_workspace_bytes(desc). */
+akv_status akv_attend_chunk(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/* Exact log-sum-exp merge of P normalized partials of R rows of width d:
+ * o_parts [P][R][d], lse_parts [P][R] (natural log), outputs o_out [R][d],
+ * lse_out [R].  Per row: M = max_p lse_p; if M = -inf the row is empty and
+ * gets o = 0, lse = -inf; else w_p = exp(lse_p - M), W = sum_p w_p,
+ * lse = M + ln W and o = sum_p (w_p / W) o_p, summed in ascending p.  NaN
+ * inputs propagate; +inf is invalid input.  1 <= P <= 4096, 1 <= d <= 1024,
+ * all pointers 4-byte aligned. */
+akv_status akv_lse_merge(const float* o_parts, const float* lse_parts, int32_t P, int32_t R,
+                         int32_t d, float* o_out, float* lse_out, void* stream);
+
+/* Compress evicted exact-tier tokens into the compressed tier (see
+ * akv_compress_desc).  Enqueues one encode kernel. */
+akv_status akv_compress_evicted(const akv_compress_desc* desc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AKV_H */

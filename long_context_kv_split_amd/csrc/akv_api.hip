@@ -1,0 +1,233 @@
+// Host side of the akv C ABI: argument validation (fixed order NULL -> SHAPE
+// -> UNSUPPORTED -> ALIGN -> WORKSPACE, all before anything is enqueued, so a
+// refused request leaves the stream untouched -- ActiveKV, "Context beyond
+// VRAM", "What I built": requests that cannot be served are refused), the
+// fixed split rule, workspace layout and kernel launches on the caller's
+// stream.  No allocation, no synchronization, no retained pointers.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "akv_common.h"
+#include "akv_params.h"
+
+namespace akv {
+hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream);
+hipError_t launch_chunk(const AttnParams& p, int D, hipStream_t stream);
+hipError_t launch_lse_merge(const float* op, const float* lp, int P, int R, int d, float* o, float* lse,
+                            hipStream_t stream);
+hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream);
+}  // namespace akv
+
+
+
+namespace {
+
+thread_local std::string g_err;
+
+akv_status fail(akv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int split_tokens(int v, int dflt) { return v ? v : dflt; }
+
+struct Plan {
+  int G, Pe, Pq, Se, Sq;
+  size_t part_rows;  // partial rows = B * Hkv * (Sq+Se) * Tq * G
+  size_t ws_bytes;
+};
+
+// Validate an attention descriptor; on success fill the plan.
+akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan) {
+  // ---- NULL
+  if (!d) return fail(AKV_ERR_NULL, "descriptor is NULL");
+  if (d->struct_size < sizeof(akv_attn_desc))
+    return fail(AKV_ERR_SHAPE, "struct_size %u < %zu", d->struct_size, sizeof(akv_attn_desc));
+  if (!d->q || !d->o || !d->lse) return fail(AKV_ERR_NULL, "q, o or lse is NULL");
+  const akv_exact_tier& e = d->exact;
+  const akv_quant_tier& q = d->quant;
+  if (e.max_blocks > 0 && (!e.k || !e.v || !e.block_table || !e.lengths))
+    return fail(AKV_ERR_NULL, "exact tier present but a pointer is NULL");
+  if (q.max_blocks > 0 && (!q.k_codes || !q.v_codes || !q.k_scales || !q.v_scales || !q.block_table || !q.lengths))
+    return fail(AKV_ERR_NULL, "compressed tier present but a pointer is NULL");
+  // ---- SHAPE
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->d < 1 || d->Tq < 1)
+    return fail(AKV_ERR_SHAPE, "B, Hq, Hkv, d and Tq must be >= 1");
+  if (d->Hq % d->Hkv) return fail(AKV_ERR_SHAPE, "Hq (%d) is not a multiple of Hkv (%d)", d->Hq, d->Hkv);
+  if (e.max_blocks < 0 || q.max_blocks < 0) return fail(AKV_ERR_SHAPE, "max_blocks < 0");
+  if ((e.max_blocks > 0 && e.num_blocks < 1) || (q.max_blocks > 0 && q.num_blocks < 1))
+    return fail(AKV_ERR_SHAPE, "a present tier needs num_blocks >= 1");
+  if (e.max_blocks == 0 && q.max_blocks == 0) return fail(AKV_ERR_SHAPE, "both tiers are absent");
+  if (!(d->softmax_scale >= 0.0f) || !std::isfinite(d->softmax_scale))
+    return fail(AKV_ERR_SHAPE, "softmax_scale must be finite and >= 0");
+  if (d->split_tokens_exact < 0 || d->split_tokens_quant < 0 || d->split_tokens_exact % AKV_BLOCK_TOKENS ||
+      d->split_tokens_quant % AKV_BLOCK_TOKENS)
+    return fail(AKV_ERR_SHAPE, "split sizes must be non-negative multiples of %d", AKV_BLOCK_TOKENS);
+  // ---- UNSUPPORTED
+  if (d->d != 64 && d->d != 128) return fail(AKV_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  const int G = d->Hq / d->Hkv;
+  if (G > akv::kMaxG) return fail(AKV_ERR_UNSUPPORTED, "%d query heads per kv head (max %d)", G, akv::kMaxG);
+  if (!chunk && d->Tq != 1) return fail(AKV_ERR_UNSUPPORTED, "decode takes Tq = 1 (got %d)", d->Tq);
+  if (chunk && d->Tq > AKV_MAX_CHUNK) return fail(AKV_ERR_UNSUPPORTED, "chunk Tq %d > %d", d->Tq, AKV_MAX_CHUNK);
+  if (chunk && e.max_blocks == 0) return fail(AKV_ERR_UNSUPPORTED, "chunk needs the exact tier (it holds the chunk)");
+  if (d->B > 65535 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  const int Pe = split_tokens(d->split_tokens_exact, AKV_SPLIT_TOKENS_EXACT_DEFAULT);
+  const int Pq = split_tokens(d->split_tokens_quant, AKV_SPLIT_TOKENS_QUANT_DEFAULT);
+  if (Pe > (1 << 20) || Pq > (1 << 20)) return fail(AKV_ERR_UNSUPPORTED, "split size above 2^20 tokens");
+  const long long Se = ((long long)e.max_blocks * AKV_BLOCK_TOKENS + Pe - 1) / Pe;
+  const long long Sq = ((long long)q.max_blocks * AKV_BLOCK_TOKENS + Pq - 1) / Pq;
+  if (Se + Sq > (1LL << 24)) return fail(AKV_ERR_UNSUPPORTED, "too many splits (%lld)", Se + Sq);
+  if ((long long)d->Tq * d->Hq > (1LL << 30)) return fail(AKV_ERR_UNSUPPORTED, "Tq * Hq too large");
+  // ---- ALIGN
+  if (!aligned(d->q, 16)) return fail(AKV_ERR_ALIGN, "q must be 16-byte aligned");
+  if (!aligned(d->o, 4) || !aligned(d->lse, 4)) return fail(AKV_ERR_ALIGN, "o and lse must be 4-byte aligned");
+  if (e.max_blocks > 0 && (!aligned(e.k, 16) || !aligned(e.v, 16) || !aligned(e.block_table, 4) ||
+                           !aligned(e.lengths, 4)))
+    return fail(AKV_ERR_ALIGN, "exact pools must be 16-byte aligned, tables 4-byte");
+  if (q.max_blocks > 0 && (!aligned(q.k_codes, 16) || !aligned(q.v_codes, 16) || !aligned(q.k_scales, 16) ||
+                           !aligned(q.v_scales, 16) || !aligned(q.block_table, 4) || !aligned(q.lengths, 4)))
+    return fail(AKV_ERR_ALIGN, "compressed pools must be 16-byte aligned, tables 4-byte");
+  plan->G = G;
+  plan->Pe = Pe;
+  plan->Pq = Pq;
+  plan->Se = (int)Se;
+  plan->Sq = (int)Sq;
+  plan->part_rows = (size_t)d->B * d->Hkv * (size_t)(Se + Sq) * d->Tq * G;
+  size_t po = plan->part_rows * d->d * sizeof(float);
+  po = (po + 255) & ~(size_t)255;
+  plan->ws_bytes = po + plan->part_rows * sizeof(float);
+  return AKV_OK;
+}
+
+akv_status check_ws(const Plan& plan, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(AKV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.ws_bytes);
+  if (!aligned(ws, 256)) return fail(AKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < plan.ws_bytes)
+    return fail(AKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, plan.ws_bytes);
+  return AKV_OK;
+}
+
+akv::AttnParams make_params(const akv_attn_desc* d, const Plan& plan, void* ws) {
+  akv::AttnParams p{};
+  p.B = d->B;
+  p.Hq = d->Hq;
+  p.Hkv = d->Hkv;
+  p.G = plan.G;
+  p.Tq = d->Tq;
+  float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)d->d);
+  p.qscale2 = scale * akv::kLog2e;
+  p.q = d->q;
+  p.ek = d->exact.k;
+  p.ev = d->exact.v;
+  p.etab = d->exact.block_table;
+  p.elen = d->exact.lengths;
+  p.emax = d->exact.max_blocks;
+  p.enb = d->exact.num_blocks;
+  p.kc = d->quant.k_codes;
+  p.vc = d->quant.v_codes;
+  p.ks = d->quant.k_scales;
+  p.vs = d->quant.v_scales;
+  p.qtab = d->quant.block_table;
+  p.qlen = d->quant.lengths;
+  p.qmax = d->quant.max_blocks;
+  p.qnb = d->quant.num_blocks;
+  p.Pe = plan.Pe;
+  p.Pq = plan.Pq;
+  p.Se = plan.Se;
+  p.Sq = plan.Sq;
+  size_t po = plan.part_rows * d->d * sizeof(float);
+  po = (po + 255) & ~(size_t)255;
+  p.part_o = static_cast<float*>(ws);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + po);
+  p.o = d->o;
+  p.lse = d->lse;
+  return p;
+}
+
+akv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return AKV_OK;
+  return fail(AKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int akv_abi_version(void) { return AKV_ABI_VERSION; }
+
+const char* akv_last_error(void) { return g_err.c_str(); }
+
+size_t akv_decode_workspace_bytes(const akv_attn_desc* desc) {
+  Plan plan;
+  return check_attn(desc, false, &plan) == AKV_OK ? plan.ws_bytes : 0;
+}
+
+size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc) {
+  Plan plan;
+  return check_attn(desc, true, &plan) == AKV_OK ? plan.ws_bytes : 0;
+}
+
+akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream) {
+  Plan plan;
+  akv_status s = check_attn(desc, false, &plan);
+  if (s != AKV_OK) return s;
+  if ((s = check_ws(plan, ws, ws_bytes)) != AKV_OK) return s;
+  akv::AttnParams p = make_params(desc, plan, ws);
+  return hip_status(akv::launch_decode(p, desc->d, static_cast<hipStream_t>(stream)), "akv_attend_decode");
+}
+
+akv_status akv_attend_chunk(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream) {
+  Plan plan;
+  akv_status s = check_attn(desc, true, &plan);
+  if (s != AKV_OK) return s;
+  if ((s = check_ws(plan, ws, ws_bytes)) != AKV_OK) return s;
+  akv::AttnParams p = make_params(desc, plan, ws);
+  return hip_status(akv::launch_chunk(p, desc->d, static_cast<hipStream_t>(stream)), "akv_attend_chunk");
+}
+
+akv_status akv_lse_merge(const float* o_parts, const float* lse_parts, int32_t P, int32_t R, int32_t d,
+                         float* o_out, float* lse_out, void* stream) {
+  if (!o_parts || !lse_parts || !o_out || !lse_out) return fail(AKV_ERR_NULL, "a merge pointer is NULL");
+  if (P < 1 || R < 0 || d < 1) return fail(AKV_ERR_SHAPE, "need P >= 1, R >= 0, d >= 1");
+  if (P > 4096 || d > 1024) return fail(AKV_ERR_UNSUPPORTED, "P <= 4096 and d <= 1024 are served");
+  if (!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(o_out, 4) || !aligned(lse_out, 4))
+    return fail(AKV_ERR_ALIGN, "merge buffers must be 4-byte aligned");
+  if (R == 0) return AKV_OK;
+  return hip_status(akv::launch_lse_merge(o_parts, lse_parts, P, R, d, o_out, lse_out,
+                                          static_cast<hipStream_t>(stream)),
+                    "akv_lse_merge");
+}
+
+akv_status akv_compress_evicted(const akv_compress_desc* d, void* stream) {
+  if (!d) return fail(AKV_ERR_NULL, "descriptor is NULL");
+  if (d->struct_size < sizeof(akv_compress_desc))
+    return fail(AKV_ERR_SHAPE, "struct_size %u < %zu", d->struct_size, sizeof(akv_compress_desc));
+  if (!d->src_k || !d->src_v || !d->src_block_table || !d->dst_k_codes || !d->dst_v_codes || !d->dst_k_scales ||
+      !d->dst_v_scales || !d->dst_block_table)
+    return fail(AKV_ERR_NULL, "a compress pointer is NULL");
+  if (d->Hkv < 1 || d->d < 1 || d->n_tokens < 0 || d->src_start < 0 || d->dst_start < 0 || d->src_max_blocks < 1 ||
+      d->dst_max_blocks < 1 || d->src_num_blocks < 1 || d->dst_num_blocks < 1)
+    return fail(AKV_ERR_SHAPE, "compress sizes out of range");
+  if ((long long)d->src_start + d->n_tokens > (long long)d->src_max_blocks * AKV_BLOCK_TOKENS ||
+      (long long)d->dst_start + d->n_tokens > (long long)d->dst_max_blocks * AKV_BLOCK_TOKENS)
+    return fail(AKV_ERR_SHAPE, "token range exceeds a block table");
+  if (d->d != 64 && d->d != 128) return fail(AKV_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  if (d->dst_start & 1) return fail(AKV_ERR_UNSUPPORTED, "dst_start must be even");
+  if (d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "Hkv must be <= 65535");
+  if (!aligned(d->src_k, 2) || !aligned(d->src_v, 2) || !aligned(d->dst_k_scales, 2) ||
+      !aligned(d->dst_v_scales, 2) || !aligned(d->src_block_table, 4) || !aligned(d->dst_block_table, 4))
+    return fail(AKV_ERR_ALIGN, "compress buffers misaligned");
+  if (d->n_tokens == 0) return AKV_OK;
+  return hip_status(akv::launch_compress(d, static_cast<hipStream_t>(stream)), "akv_compress_evicted");
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+// Compress evicted exact-tier tokens into the 4-bit tier.
+//
+// For every (token, kv head, K|V) vector of d bf16 values (ActiveKV, "Context
+// beyond VRAM", "What I built": older history held in a compact form; the
+// rotation is the Walsh-Hadamard rotation of the QuantForge walkthrough,
+// section 1):
+//   E1 x = float(bf16)                                   exact
+//   E2 unnormalized Sylvester butterflies, h = 1, 2, ..., d/2 ascending:
+//      (x[i], x[i+h]) <- (x[i] + x[i+h], x[i] - x[i+h])  for i & h == 0
+//   E3 y = x * RN(1/sqrt(d))
+//   E4 per 32-group: sq = y*y, pairwise tree (off = 16, 8, 4, 2, 1:
+//      v[i] += v[i+off]), ms = sum / 32, s32 = sqrt(ms) (correctly rounded)
+//   E5 s16 = fp16 round-to-nearest-even (saturating at 65504) -- the stored scale
+//   E6 s = float(s16); s == 0 -> every code of the group is 7
+//   E7 u = y / s (correctly rounded)
+//   E8 code = #{k : u > T_k}   (nearest Lloyd-Max level, ties to lower index)
+//   E9 two codes per byte, storage order as documented in akv.h
+// Every step is one IEEE float32 operation with round-to-nearest-even and
+// nothing is contracted into a fused multiply-add, so codes and scales are
+// bit-exact functions of the input.
+//
+// One wavefront per (token pair, kv head, K|V): lane l holds elements
+// l + 64k of both tokens; butterflies with h < 64 exchange across lanes.
+#include "akv_common.h"
+
+#pragma clang fp contract(off)
+
+namespace akv {
+
+struct CompressParams {
+  int Hkv;
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  const int32_t* src_table;
+  int src_num_blocks, src_start, n_tokens;
+  uint8_t* dst_kc;
+  uint8_t* dst_vc;
+  uint16_t* dst_ks;
+  uint16_t* dst_vs;
+  const int32_t* dst_table;
+  int dst_num_blocks, dst_start;
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void compress_kernel(CompressParams p) {
+  constexpr int E = D / 64;  // elements per lane per token
+  const int pair = blockIdx.x, kv = blockIdx.y, isv = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int first = 2 * pair;
+  const int ntok = min(2, p.n_tokens - first);
+  const float rd = inv_sqrt_d(D);
+
+  float y[2][E];
+  int code[2][E];
+  uint16_t s16[2][E];
+  bool ok[2] = {false, false};
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk) {
+    float x[E];
+    const uint16_t* src = nullptr;
+    if (tk < ntok) {
+      int s = p.src_start + first + tk;
+      int blk = p.src_table[s >> 6];
+      if (blk >= 0 && blk < p.src_num_blocks) {
+        src = (isv ? p.src_v : p.src_k) + ((size_t)(blk * p.Hkv + kv) * kBlock + (s & 63)) * D;
+        ok[tk] = true;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = src ? bf16_bits_to_float(src[lane + 64 * e]) : 0.0f;  // E1
+    // E2: butterflies across lanes for h < 64, inside the lane for h = 64
+#pragma unroll
+    for (int h = 1; h < 64 && h < D; h <<= 1) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float o = __shfl_xor(x[e], h);
+        x[e] = (lane & h) ? (o - x[e]) : (x[e] + o);
+      }
+    }
+    if (E == 2) {
+      float a = x[0], b = x[E - 1];
+      x[0] = a + b;
+      x[E - 1] = a - b;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      y[tk][e] = x[e] * rd;                                 // E3
+      float v = y[tk][e] * y[tk][e];                        // E4
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) {
+        float o = __shfl_down(v, off, 32);
+        v = v + o;
+      }
+      float ms = v * 0.03125f;
+      float s32 = __builtin_sqrtf(ms);
+      __half hs = __float2half_rn(fminf(s32, 65504.0f));    // E5
+      uint16_t hb = __half_as_ushort(hs);
+      hb = (uint16_t)__shfl((int)hb, lane & 32);            // broadcast group scale
+      s16[tk][e] = hb;
+      float s = __half2float(__ushort_as_half(hb));         // E6
+      int c = 7;
+      if (s != 0.0f) {
+        float u = y[tk][e] / s;                             // E7
+        c = 0;
+#pragma unroll
+        for (int k = 0; k < 15; ++k) c += (u > __builtin_bit_cast(float, kThreshBits[k])) ? 1 : 0;  // E8
+      }
+      code[tk][e] = c;
+    }
+  }
+
+  // E9: store
+  const int pos0 = p.dst_start + first;   // even
+  const int dblk = p.dst_table[pos0 >> 6];
+  if (dblk < 0 || dblk >= p.dst_num_blocks) return;
+  const int r0 = pos0 & 63;
+  const size_t slab = (size_t)dblk * p.Hkv + kv;
+  uint16_t* scales = (isv ? p.dst_vs : p.dst_ks) + slab * (2 * D);
+  if (!isv) {
+    uint8_t* codes = p.dst_kc + slab * (32 * D);
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        int hi = __shfl_down(code[tk][e], 1);
+        int dim = lane + 64 * e;
+        if (tk < ntok && ok[tk] && !(lane & 1))
+          codes[(r0 + tk) * (D / 2) + kcode_byte(D, dim)] = (uint8_t)(code[tk][e] | (hi << 4));
+        if (tk < ntok && ok[tk] && (lane & 31) == 0)
+          scales[(dim >> 5) * kBlock + r0 + tk] = s16[tk][e];
+      }
+    }
+  } else {
+    uint8_t* codes = p.dst_vc + slab * (32 * D);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      int dim = lane + 64 * e;
+      int c0 = ok[0] ? code[0][e] : 0;
+      int c1 = (ntok > 1 && ok[1]) ? code[1][e] : 0;
+      codes[vcode_byte(D, r0, dim)] = (uint8_t)(c0 | (c1 << 4));
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk)
+        if (tk < ntok && ok[tk] && (lane & 31) == 0) scales[(dim >> 5) * kBlock + r0 + tk] = s16[tk][e];
+    }
+  }
+}
+
+hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream) {
+  CompressParams p;
+  p.Hkv = d->Hkv;
+  p.src_k = d->src_k;
+  p.src_v = d->src_v;
+  p.src_table = d->src_block_table;
+  p.src_num_blocks = d->src_num_blocks;
+  p.src_start = d->src_start;
+  p.n_tokens = d->n_tokens;
+  p.dst_kc = d->dst_k_codes;
+  p.dst_vc = d->dst_v_codes;
+  p.dst_ks = d->dst_k_scales;
+  p.dst_vs = d->dst_v_scales;
+  p.dst_table = d->dst_block_table;
+  p.dst_num_blocks = d->dst_num_blocks;
+  p.dst_start = d->dst_start;
+  dim3 grid((d->n_tokens + 1) / 2, d->Hkv, 2);
+  if (d->d == 64)
+    hipLaunchKernelGGL(compress_kernel<64>, grid, dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace akv

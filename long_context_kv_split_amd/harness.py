@@ -1,0 +1,211 @@
+"""Device-side harness: paged pools in HBM for a synth.Workload, calls through the C ABI.
+
+PyTorch is used only to own device memory and streams.  The compressed tier
+is produced on the GPU by ``akv_compress_evicted`` from the workload's bf16
+source values (staged once in an exact-tier-format pool), exactly as an
+eviction would produce it.  Nothing here computes any part of the method:
+the helpers only scatter/gather bytes according to the layouts documented in
+include/akv.h.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import akv
+from .synth import BLOCK, Workload
+
+
+# ------------------------------------------------------------------ layouts
+
+def kcode_byte(d: int, dim: np.ndarray) -> np.ndarray:
+    """Byte (inside a token's K-code row) holding dim `dim` (include/akv.h)."""
+    m, a, b = dim >> 5, (dim >> 3) & 3, (dim >> 1) & 3
+    return (d >> 3) * a + 4 * m + b
+
+
+def vcode_byte(d: int, tok: np.ndarray, dim: np.ndarray) -> np.ndarray:
+    """Byte (inside a V-code slab) holding token `tok` (in-block) of dim `dim`."""
+    c, a, b = tok >> 5, (tok >> 3) & 3, (tok >> 1) & 3
+    t, i = dim >> 4, dim & 15
+    return ((c * 4 + a) * 16 + i) * (d >> 2) + 4 * t + b
+
+
+def pages_from_tokens(x: np.ndarray, n_blocks_pool: int, table_row: np.ndarray, out: np.ndarray) -> None:
+    """Scatter token-major x [n, Hkv, d] into a pool [blocks, Hkv, 64, d] by a table row."""
+    n, hkv, d = x.shape
+    nb = -(-n // BLOCK)
+    if nb == 0:
+        return
+    pad = np.zeros((nb * BLOCK, hkv, d), dtype=x.dtype)
+    pad[:n] = x
+    out[table_row[:nb]] = pad.reshape(nb, BLOCK, hkv, d).transpose(0, 2, 1, 3)
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+@dataclass
+class Pools:
+    """One replica of every per-call input that a decode call streams."""
+    ek: Optional[torch.Tensor]
+    ev: Optional[torch.Tensor]
+    kc: Optional[torch.Tensor]
+    vc: Optional[torch.Tensor]
+    ks: Optional[torch.Tensor]
+    vs: Optional[torch.Tensor]
+
+
+class DeviceWorkload:
+    """A workload resident in HBM, ready for akv_attend_decode / akv_attend_chunk."""
+
+    def __init__(self, w: Workload, device: str = "cuda", fill_quant: bool = True):
+        self.w = w
+        self.device = device
+        d, hkv = w.d, w.Hkv
+        self.q = _dev(w.q, device)
+        self.exact_len = _dev(w.exact_len, device)
+        self.quant_len = _dev(w.quant_len, device)
+        self.exact_table = _dev(w.exact_table, device)
+        self.quant_table = _dev(w.quant_table, device)
+        self.emax = w.exact_table.shape[1] if w.exact_len.max(initial=0) > 0 else 0
+        self.qmax = w.quant_table.shape[1] if (w.quant_len.max(initial=0) > 0 or w.evict) else 0
+        ek = np.zeros((max(1, w.exact_pool_blocks), hkv, BLOCK, d), dtype=np.uint16)
+        ev = np.zeros_like(ek)
+        for b in range(w.B):
+            pages_from_tokens(w.exact_k[b], w.exact_pool_blocks, w.exact_table[b], ek)
+            pages_from_tokens(w.exact_v[b], w.exact_pool_blocks, w.exact_table[b], ev)
+        qnb = max(1, w.quant_pool_blocks)
+        self.pools = [Pools(
+            _dev(ek, device), _dev(ev, device),
+            torch.zeros((qnb, hkv, 32 * d), dtype=torch.uint8, device=device),
+            torch.zeros((qnb, hkv, 32 * d), dtype=torch.uint8, device=device),
+            torch.zeros((qnb, hkv, 2 * d), dtype=torch.int16, device=device),
+            torch.zeros((qnb, hkv, 2 * d), dtype=torch.int16, device=device))]
+        B, Tq, Hq = w.B, w.Tq, w.Hq
+        self.o = torch.full((B, Tq, Hq, d), float("nan"), dtype=torch.float32, device=device)
+        self.lse = torch.full((B, Tq, Hq), float("nan"), dtype=torch.float32, device=device)
+        self.ws = None
+        self.ws_bytes = 0
+        if fill_quant:
+            self.fill_quant_tier()
+
+    # ----------------------------------------------------------- compressed tier
+    def fill_quant_tier(self, stream: int = 0) -> None:
+        """Encode every sequence's compressed-tier source into the pools (GPU)."""
+        w = self.w
+        if w.quant_len.max(initial=0) == 0:
+            return
+        for b in range(w.B):
+            n = int(w.quant_len[b])
+            if n == 0:
+                continue
+            nb = -(-n // BLOCK)
+            sk = np.zeros((nb, w.Hkv, BLOCK, w.d), dtype=np.uint16)
+            sv = np.zeros_like(sk)
+            ident = np.arange(nb, dtype=np.int32)
+            pages_from_tokens(w.quant_k_src[b], nb, ident, sk)
+            pages_from_tokens(w.quant_v_src[b], nb, ident, sv)
+            dk, dv, dt = _dev(sk, self.device), _dev(sv, self.device), _dev(ident, self.device)
+            dst_t = self.quant_table[b]
+            desc = akv.CompressDesc(
+                Hkv=w.Hkv, d=w.d, src_k=ptr(dk), src_v=ptr(dv), src_block_table=ptr(dt),
+                src_max_blocks=nb, src_num_blocks=nb, src_start=0, n_tokens=n,
+                dst_k_codes=ptr(self.pools[0].kc), dst_v_codes=ptr(self.pools[0].vc),
+                dst_k_scales=ptr(self.pools[0].ks), dst_v_scales=ptr(self.pools[0].vs),
+                dst_block_table=ptr(dst_t), dst_max_blocks=w.quant_table.shape[1],
+                dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=0)
+            akv.check(akv.akv_compress_evicted(desc, stream or stream_handle()))
+            torch.cuda.synchronize()
+            del dk, dv, dt
+
+    def compress_desc(self, b: int, src_start: int, n: int, dst_start: int, replica: int = 0) -> akv.CompressDesc:
+        """Descriptor moving exact tokens [src_start, +n) of sequence b to compressed [dst_start, +n)."""
+        w, P = self.w, self.pools[replica]
+        return akv.CompressDesc(
+            Hkv=w.Hkv, d=w.d, src_k=ptr(P.ek), src_v=ptr(P.ev), src_block_table=ptr(self.exact_table[b]),
+            src_max_blocks=w.exact_table.shape[1], src_num_blocks=max(1, w.exact_pool_blocks),
+            src_start=src_start, n_tokens=n,
+            dst_k_codes=ptr(P.kc), dst_v_codes=ptr(P.vc), dst_k_scales=ptr(P.ks), dst_v_scales=ptr(P.vs),
+            dst_block_table=ptr(self.quant_table[b]), dst_max_blocks=w.quant_table.shape[1],
+            dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=dst_start)
+
+    def read_codes(self, b: int, start: int = 0, n: Optional[int] = None, replica: int = 0):
+        """Logical (codes, scales) of compressed tokens [start, start+n) of sequence b.
+
+        Returns kcodes [n, Hkv, d] u8, kscales [n, Hkv, d/32] u16 bits, vcodes, vscales.
+        """
+        w, P = self.w, self.pools[replica]
+        d = w.d
+        n = int(w.quant_len[b]) - start if n is None else n
+        tok = np.arange(start, start + n)
+        blocks = w.quant_table[b][tok // BLOCK].astype(np.int64)
+        r = tok % BLOCK
+        kc = P.kc.cpu().numpy().reshape(P.kc.shape[0], w.Hkv, BLOCK, d // 2)
+        vc = P.vc.cpu().numpy()
+        ks = P.ks.cpu().numpy().view(np.uint16).reshape(-1, w.Hkv, d // 32, BLOCK)
+        vs = P.vs.cpu().numpy().view(np.uint16).reshape(-1, w.Hkv, d // 32, BLOCK)
+        dims = np.arange(d)
+        kb = kcode_byte(d, dims)
+        krow = kc[blocks, :, r, :]                                    # [n, Hkv, d/2]
+        kcodes = (krow[:, :, kb] >> (4 * (dims & 1))[None, None, :]) & 15
+        vb = vcode_byte(d, (r & ~1)[:, None], dims[None, :])          # [n, d]
+        vbytes = vc[blocks[:, None, None], np.arange(w.Hkv)[None, :, None], vb[:, None, :]]
+        vcodes = (vbytes >> (4 * (r & 1))[:, None, None]) & 15
+        kscales = ks[blocks, :, :, r]
+        vscales = vs[blocks, :, :, r]
+        return (kcodes.astype(np.uint8), kscales.copy(), vcodes.astype(np.uint8), vscales.copy())
+
+    # ------------------------------------------------------------- attention
+    def add_replicas(self, n_total: int) -> None:
+        """Clone the pools so that timed calls can rotate through n_total copies."""
+        base = self.pools[0]
+        while len(self.pools) < n_total:
+            self.pools.append(Pools(*[None if t is None else t.clone() for t in
+                                      (base.ek, base.ev, base.kc, base.vc, base.ks, base.vs)]))
+
+    def desc(self, replica: int = 0, split_exact: Optional[int] = None, split_quant: Optional[int] = None,
+             tables=None) -> akv.AttnDesc:
+        w, P = self.w, self.pools[replica]
+        et, qt = (self.exact_table, self.quant_table) if tables is None else tables
+        exact = akv.ExactTier(k=ptr(P.ek), v=ptr(P.ev), block_table=ptr(et), lengths=ptr(self.exact_len),
+                              max_blocks=self.emax, num_blocks=max(1, w.exact_pool_blocks))
+        quant = akv.QuantTier(k_codes=ptr(P.kc), v_codes=ptr(P.vc), k_scales=ptr(P.ks), v_scales=ptr(P.vs),
+                              block_table=ptr(qt), lengths=ptr(self.quant_len), max_blocks=self.qmax,
+                              num_blocks=max(1, w.quant_pool_blocks))
+        se = w.split_tokens_exact if split_exact is None else split_exact
+        sq = w.split_tokens_quant if split_quant is None else split_quant
+        return akv.AttnDesc(B=w.B, Hq=w.Hq, Hkv=w.Hkv, d=w.d, Tq=w.Tq, softmax_scale=0.0, q=ptr(self.q),
+                            exact=exact, quant=quant, split_tokens_exact=se, split_tokens_quant=sq,
+                            o=ptr(self.o), lse=ptr(self.lse))
+
+    def ensure_ws(self, desc: akv.AttnDesc, chunk: bool = False) -> None:
+        need = (akv.akv_chunk_workspace_bytes if chunk else akv.akv_decode_workspace_bytes)(desc)
+        if need == 0:
+            raise akv.AKVError(akv.AKV_ERR_SHAPE, akv.akv_last_error())
+        if need > self.ws_bytes:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self.ws_bytes = need
+
+    def attend(self, replica: int = 0, stream: Optional[int] = None, **kw) -> int:
+        chunk = self.w.causal_tail > 0
+        d = self.desc(replica, **kw)
+        self.ensure_ws(d, chunk)
+        fn = akv.akv_attend_chunk if chunk else akv.akv_attend_decode
+        return fn(d, ptr(self.ws), self.ws_bytes, stream_handle() if stream is None else stream)

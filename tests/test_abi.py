@@ -1,0 +1,172 @@
+"""C-ABI contract tests that need no GPU.
+
+The library validates every argument on the host before anything is
+enqueued, in the fixed order NULL -> SHAPE -> UNSUPPORTED -> ALIGN ->
+WORKSPACE, so each refusal here returns without any HIP call.  Pointers are
+fake (never dereferenced on the host).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from long_context_kv_split_amd import akv
+
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def good_desc(**over):
+    e = akv.ExactTier(k=FAKE, v=FAKE + 0x1000000, block_table=FAKE + 0x2000000, lengths=FAKE + 0x2100000,
+                      max_blocks=64, num_blocks=64)
+    q = akv.QuantTier(k_codes=FAKE + 0x3000000, v_codes=FAKE + 0x4000000, k_scales=FAKE + 0x5000000,
+                      v_scales=FAKE + 0x5800000, block_table=FAKE + 0x6000000, lengths=FAKE + 0x6100000,
+                      max_blocks=1936, num_blocks=1936)
+    kw = dict(B=1, Hq=32, Hkv=4, d=128, Tq=1, softmax_scale=0.0, q=FAKE + 0x7000000, exact=e, quant=q,
+              split_tokens_exact=0, split_tokens_quant=0, o=FAKE + 0x8000000, lse=FAKE + 0x9000000)
+    kw.update(over)
+    return akv.AttnDesc(**kw)
+
+
+def call(desc, ws=FAKE + 0xA000000, ws_bytes=None, chunk=False):
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    fn = akv.akv_attend_chunk if chunk else akv.akv_attend_decode
+    return fn(desc, ws, ws_bytes, 0)
+
+
+def test_abi_version_and_exports():
+    assert akv.akv_abi_version() == 1
+    names = akv.header_functions()
+    assert set(names) == {"akv_abi_version", "akv_last_error", "akv_decode_workspace_bytes",
+                          "akv_chunk_workspace_bytes", "akv_attend_decode", "akv_attend_chunk",
+                          "akv_lse_merge", "akv_compress_evicted"}
+    for n in names:
+        assert hasattr(akv.LIB, n), n
+
+
+def test_exports_via_nm():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", akv.LIB_PATH], capture_output=True, text=True).stdout
+    syms = set(re.findall(r"\bT (akv_\w+)", out))
+    assert set(akv.header_functions()) <= syms
+
+
+def test_workspace_bytes_hybrid128k_shape():
+    d = good_desc()
+    # splits: exact 64*64/2048 = 2, quant ceil(1936*64/1024) = 121 -> 123 splits
+    rows = 1 * 4 * 123 * 1 * 8
+    po = (rows * 128 * 4 + 255) // 256 * 256
+    assert akv.akv_decode_workspace_bytes(d) == po + rows * 4
+    assert akv.akv_decode_workspace_bytes(good_desc(d=96)) == 0
+
+
+def test_null_checks_first():
+    assert akv.LIB.akv_attend_decode(None, None, 0, None) == akv.AKV_ERR_NULL
+    assert call(good_desc(q=0)) == akv.AKV_ERR_NULL
+    assert "q, o or lse" in akv.akv_last_error()
+    e = good_desc().exact
+    e.k = 0
+    assert call(good_desc(exact=e)) == akv.AKV_ERR_NULL
+    # NULL beats SHAPE beats UNSUPPORTED
+    assert call(good_desc(q=0, Hq=33, d=96)) == akv.AKV_ERR_NULL
+    assert call(good_desc(Hq=33, d=96)) == akv.AKV_ERR_SHAPE
+    assert call(good_desc(d=96, q=FAKE + 2)) == akv.AKV_ERR_UNSUPPORTED
+
+
+def test_absent_tier_may_be_null():
+    q = akv.QuantTier()  # all zero: absent
+    d = good_desc(quant=q)
+    assert call(d, ws=0) == akv.AKV_ERR_WORKSPACE  # everything else valid
+
+
+def test_shape_errors():
+    for over in (dict(B=0), dict(Hq=0), dict(Hkv=0), dict(Tq=0), dict(Hq=30), dict(softmax_scale=-1.0),
+                 dict(softmax_scale=float("inf")), dict(split_tokens_exact=100), dict(split_tokens_quant=-64)):
+        assert call(good_desc(**over)) == akv.AKV_ERR_SHAPE, over
+    assert call(good_desc(exact=akv.ExactTier(), quant=akv.QuantTier())) == akv.AKV_ERR_SHAPE
+    d = good_desc()
+    d.struct_size = 8
+    assert call(d) == akv.AKV_ERR_SHAPE
+
+
+def test_unsupported():
+    assert call(good_desc(d=256)) == akv.AKV_ERR_UNSUPPORTED
+    assert call(good_desc(Hq=64, Hkv=4)) == akv.AKV_ERR_UNSUPPORTED  # G = 16
+    assert call(good_desc(Tq=2)) == akv.AKV_ERR_UNSUPPORTED          # decode is one query
+    assert call(good_desc(Tq=513), chunk=True) == akv.AKV_ERR_UNSUPPORTED
+    assert call(good_desc(Tq=4, exact=akv.ExactTier()), chunk=True) == akv.AKV_ERR_UNSUPPORTED
+
+
+def test_alignment():
+    assert call(good_desc(q=FAKE + 8)) == akv.AKV_ERR_ALIGN
+    assert call(good_desc(o=FAKE + 2)) == akv.AKV_ERR_ALIGN
+    e = good_desc().exact
+    e.v = FAKE + 4
+    assert call(good_desc(exact=e)) == akv.AKV_ERR_ALIGN
+    q = good_desc().quant
+    q.k_scales = FAKE + 8
+    assert call(good_desc(quant=q)) == akv.AKV_ERR_ALIGN
+
+
+def test_workspace_last():
+    d = good_desc()
+    need = akv.akv_decode_workspace_bytes(d)
+    assert call(d, ws=0) == akv.AKV_ERR_WORKSPACE
+    assert call(d, ws=FAKE + 16) == akv.AKV_ERR_WORKSPACE
+    assert call(d, ws_bytes=need - 1) == akv.AKV_ERR_WORKSPACE
+    assert "needed" in akv.akv_last_error()
+    # an alignment problem is reported before the workspace problem
+    assert call(good_desc(q=FAKE + 8), ws=0) == akv.AKV_ERR_ALIGN
+
+
+def test_lse_merge_validation():
+    f = akv.akv_lse_merge
+    assert f(0, FAKE, 2, 3, 4, FAKE, FAKE, 0) == akv.AKV_ERR_NULL
+    assert f(FAKE, FAKE, 0, 3, 4, FAKE, FAKE, 0) == akv.AKV_ERR_SHAPE
+    assert f(FAKE, FAKE, 5000, 3, 4, FAKE, FAKE, 0) == akv.AKV_ERR_UNSUPPORTED
+    assert f(FAKE + 2, FAKE, 2, 3, 4, FAKE, FAKE, 0) == akv.AKV_ERR_ALIGN
+    assert f(FAKE, FAKE, 2, 0, 4, FAKE, FAKE, 0) == akv.AKV_OK  # no rows: nothing to do
+
+
+def compress_desc(**over):
+    kw = dict(Hkv=4, d=128, src_k=FAKE, src_v=FAKE + 0x100000, src_block_table=FAKE + 0x200000,
+              src_max_blocks=72, src_num_blocks=72, src_start=0, n_tokens=512, dst_k_codes=FAKE + 0x300000,
+              dst_v_codes=FAKE + 0x400000, dst_k_scales=FAKE + 0x500000, dst_v_scales=FAKE + 0x600000,
+              dst_block_table=FAKE + 0x700000, dst_max_blocks=456, dst_num_blocks=456, dst_start=28672)
+    kw.update(over)
+    return akv.CompressDesc(**kw)
+
+
+def test_compress_validation():
+    f = akv.akv_compress_evicted
+    assert akv.LIB.akv_compress_evicted(None, None) == akv.AKV_ERR_NULL
+    assert f(compress_desc(src_k=0)) == akv.AKV_ERR_NULL
+    assert f(compress_desc(n_tokens=-1)) == akv.AKV_ERR_SHAPE
+    assert f(compress_desc(src_start=72 * 64 - 511)) == akv.AKV_ERR_SHAPE
+    assert f(compress_desc(dst_start=456 * 64 - 510)) == akv.AKV_ERR_SHAPE
+    assert f(compress_desc(d=32)) == akv.AKV_ERR_UNSUPPORTED
+    assert f(compress_desc(dst_start=28671)) == akv.AKV_ERR_UNSUPPORTED
+    assert f(compress_desc(dst_k_scales=FAKE + 0x500001)) == akv.AKV_ERR_ALIGN
+    assert f(compress_desc(n_tokens=0)) == akv.AKV_OK
+
+
+def test_ctypes_struct_sizes_match_header():
+    # the library rejects a struct_size smaller than its own sizeof, so a
+    # ctypes mirror that is too small shows up as SHAPE
+    assert call(good_desc(), ws=0) == akv.AKV_ERR_WORKSPACE
+    assert akv.akv_compress_evicted(compress_desc(src_k=0)) == akv.AKV_ERR_NULL
+
+
+def test_frozen_device_constants_match_oracle():
+    from oracle import akv_oracle as O
+    src = open(os.path.join(os.path.dirname(akv.HERE), "long_context_kv_split_amd", "csrc", "akv_common.h")).read()
+
+    def table(name):
+        body = re.search(name + r"\[\d+\] = \{(.*?)\};", src, re.S).group(1)
+        return np.array([int(x, 16) for x in re.findall(r"0x([0-9A-Fa-f]+)u", body)], dtype=np.uint32)
+
+    assert np.array_equal(table("kLevelBits"), O.centroids_f32().view(np.uint32))
+    assert np.array_equal(table("kThreshBits"), O.thresholds_f32().view(np.uint32))
+    assert "0x3DB504F3u" in src and O.inv_sqrt_f32(128).view(np.uint32) == 0x3DB504F3

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Tolerances (fixed by the method's contract): 4-bit codes and fp16 scales
+bit-exact; every |lse - lse_ref| <= 1e-4; every |o - o_ref| <= 2e-3 *
+max|o_ref| + 1e-3 with the max over the whole output tensor of the case.
+Determinism: repeated calls are bit-identical, and a random (paged) block
+table gives the same bytes as the contiguous ("resident") layout.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import akv_oracle as O
+from long_context_kv_split_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = 1e-4
+
+
+def _mods():
+    from long_context_kv_split_amd import akv, harness
+    return akv, harness
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    _mods()   # the library must load; no fallback exists
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def assert_attention(o, lse, o_ref, lse_ref, label):
+    o = np.asarray(o, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    m = np.isfinite(lse_ref)
+    assert np.all(np.isfinite(lse[m])), f"{label}: non-finite lse"
+    dl = np.max(np.abs(lse[m] - lse_ref[m]))
+    tol_o = 2e-3 * np.max(np.abs(o_ref)) + 1e-3
+    do = np.max(np.abs(o - o_ref))
+    _say(f"{label}: max|dlse|={dl:.3e} max|do|={do:.3e} (tol {tol_o:.3e})")
+    assert dl <= LSE_TOL, f"{label}: lse error {dl}"
+    assert do <= tol_o, f"{label}: o error {do} > {tol_o}"
+
+
+def run_case(w, **kw):
+    akv, harness = _mods()
+    _say(f"case {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} quant={list(w.quant_len)[:4]} "
+         f"exact={list(w.exact_len)[:4]}")
+    dw = harness.DeviceWorkload(w)
+    akv.check(dw.attend(**kw))
+    torch.cuda.synchronize()
+    return dw
+
+
+def oracle_case(w, dw=None, seqs=None):
+    enc_k, enc_v = {}, {}
+    for b in (range(w.B) if seqs is None else seqs):
+        enc_k[b] = O.encode(w.quant_k_src[b])
+        enc_v[b] = O.encode(w.quant_v_src[b])
+    ek = [enc_k.get(b) for b in range(w.B)]
+    ev = [enc_v.get(b) for b in range(w.B)]
+    o, lse = O.reference_outputs(w, ek, ev, seqs=seqs)
+    return o, lse, enc_k, enc_v
+
+
+def assert_codes(dw, w, enc_k, enc_v, label):
+    for b, (kc, ks) in enc_k.items():
+        vc, vs = enc_v[b]
+        gk, gks, gv, gvs = dw.read_codes(b)
+        assert np.array_equal(gk, kc), f"{label} seq {b}: K codes differ ({int((gk != kc).sum())})"
+        assert np.array_equal(gks, ks), f"{label} seq {b}: K scales differ ({int((gks != ks).sum())})"
+        assert np.array_equal(gv, vc), f"{label} seq {b}: V codes differ ({int((gv != vc).sum())})"
+        assert np.array_equal(gvs, vs), f"{label} seq {b}: V scales differ ({int((gvs != vs).sum())})"
+    _say(f"{label}: codes and scales bit-exact for {len(enc_k)} sequence(s)")
+
+
+# ------------------------------------------------------------------ encoder
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_compress_bit_exact_ragged(d):
+    w = synth.make_small("enc", B=2, Hq=8, Hkv=2, d=d, quant=[1000, 777], exact=[64, 64], outlier_frac=0.02)
+    akv, harness = _mods()
+    dw = harness.DeviceWorkload(w)
+    torch.cuda.synchronize()
+    enc_k = {b: O.encode(w.quant_k_src[b]) for b in range(2)}
+    enc_v = {b: O.encode(w.quant_v_src[b]) for b in range(2)}
+    assert_codes(dw, w, enc_k, enc_v, f"compress d={d}")
+
+
+def test_compress_crafted_ties():
+    """x = H y / 16: u is exactly 0 where y is 0 -> code 7; all-zero vectors -> codes 7, scale 0."""
+    d, n = 128, 64
+    h = O.sylvester_hadamard(d)
+    rng = np.random.default_rng(7)
+    vals = np.zeros((n, 1, d))
+    for t in range(n - 4):
+        y = rng.integers(-3, 4, size=d)
+        y[rng.choice(d, 20, replace=False)] = 0
+        vals[t, 0] = (h @ y) / 16.0
+    bits = synth.f64_to_bf16_bits(vals)
+    assert np.array_equal(O.bf16_to_f64(bits), vals)
+    w = synth.make_small("ties", B=1, Hq=1, Hkv=1, d=d, quant=[n], exact=[64])
+    w.quant_k_src[0] = bits
+    w.quant_v_src[0] = bits
+    akv, harness = _mods()
+    dw = harness.DeviceWorkload(w)
+    torch.cuda.synchronize()
+    enc = O.encode(bits)
+    assert_codes(dw, w, {0: enc}, {0: enc}, "crafted ties")
+    gk = dw.read_codes(0)[0]
+    assert np.all(gk[-4:] == 7)
+
+
+def test_compress_eviction_into_pool():
+    """Evict exact tokens [0, 512) of a chunk-shaped workload into compressed positions 448*64.."""
+    akv, harness = _mods()
+    w = synth.make_small("ev", B=1, Hq=8, Hkv=2, d=128, quant=[448 * 64 // 8], exact=[640])
+    # place the destination right after the existing compressed tokens (even start)
+    n_q = int(w.quant_len[0])
+    w.quant_table = np.concatenate([w.quant_table, np.full((1, 8), -1, np.int32)], axis=1)
+    extra = np.arange(w.quant_pool_blocks, w.quant_pool_blocks + 8, dtype=np.int32)
+    nb_used = -(-n_q // 64)
+    w.quant_table[0, nb_used:nb_used + 8] = extra
+    w.quant_pool_blocks += 8
+    w.evict = 512
+    dw = harness.DeviceWorkload(w)
+    start = nb_used * 64
+    akv.check(akv.akv_compress_evicted(dw.compress_desc(0, 0, 512, start), harness.stream_handle()))
+    torch.cuda.synchronize()
+    kc, ks = O.encode(w.exact_k[0][:512])
+    vc, vs = O.encode(w.exact_v[0][:512])
+    gk, gks, gv, gvs = dw.read_codes(0, start, 512)
+    assert np.array_equal(gk, kc) and np.array_equal(gks, ks)
+    assert np.array_equal(gv, vc) and np.array_equal(gvs, vs)
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("cfg", [
+    dict(B=2, Hq=32, Hkv=4, d=128, quant=[1000, 2500], exact=[300, 77], split_exact=128, split_quant=256),
+    dict(B=3, Hq=32, Hkv=4, d=128, quant=[0, 130, 4000], exact=[1, 64, 700], split_exact=0, split_quant=0,
+         outlier_frac=0.01),
+    dict(B=2, Hq=4, Hkv=1, d=64, quant=[383, 64], exact=[129, 0], split_exact=64, split_quant=128),
+    dict(B=1, Hq=12, Hkv=2, d=128, quant=[777], exact=[65], split_exact=64, split_quant=192),
+])
+def test_decode_small(cfg):
+    w = synth.make_small("small", **cfg)
+    dw = run_case(w)
+    o_ref, lse_ref, ek, ev = oracle_case(w)
+    assert_codes(dw, w, {b: ek[b] for b in range(w.B) if w.quant_len[b]},
+                 {b: ev[b] for b in range(w.B) if w.quant_len[b]}, "small")
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, f"small {cfg}")
+
+
+def test_tiny_two_splits():
+    w = synth.make("tiny")
+    dw = run_case(w)
+    o_ref, lse_ref, ek, ev = oracle_case(w)
+    assert_codes(dw, w, ek, ev, "tiny")
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "tiny")
+
+
+@pytest.fixture(scope="module")
+def exact32k():
+    w = synth.make("exact32k")
+    dw = run_case(w, split_exact=2048)
+    o_ref, lse_ref, _, _ = oracle_case(w)
+    return w, dw, o_ref, lse_ref
+
+
+def test_exact32k_parity(exact32k):
+    w, dw, o_ref, lse_ref = exact32k
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "exact32k (16 splits)")
+
+
+def test_exact32k_bit_identical_run_to_run(exact32k):
+    akv, harness = _mods()
+    w, dw, _, _ = exact32k
+    o0, l0 = dw.o.clone(), dw.lse.clone()
+    for _ in range(10):
+        akv.check(dw.attend(split_exact=2048))
+    torch.cuda.synchronize()
+    assert torch.equal(dw.o, o0) and torch.equal(dw.lse, l0)
+
+
+def test_exact32k_paged_equals_contiguous(exact32k):
+    akv, harness = _mods()
+    w, dw, _, _ = exact32k
+    o0, l0 = dw.o.clone(), dw.lse.clone()
+    wc = synth.contiguous(w)
+    dc = harness.DeviceWorkload(wc)
+    akv.check(dc.attend(split_exact=2048))
+    torch.cuda.synchronize()
+    assert torch.equal(dc.o, o0) and torch.equal(dc.lse, l0)
+
+
+def test_exact32k_single_split_within_tolerance(exact32k):
+    akv, harness = _mods()
+    w, dw, o_ref, lse_ref = exact32k
+    akv.check(dw.attend(split_exact=32768))
+    torch.cuda.synchronize()
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "exact32k (1 split)")
+
+
+@pytest.mark.slow
+def test_hybrid128k():
+    w = synth.make("hybrid128k")
+    dw = run_case(w)
+    o_ref, lse_ref, ek, ev = oracle_case(w)
+    assert_codes(dw, w, ek, ev, "hybrid128k")
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "hybrid128k")
+
+
+@pytest.mark.slow
+def test_ragged_sampled():
+    w = synth.make("ragged")
+    dw = run_case(w)
+    L = w.quant_len + w.exact_len
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 5, 17})
+    o_ref, lse_ref, ek, ev = oracle_case(w, seqs=seqs)
+    assert_codes(dw, w, ek, ev, "ragged")
+    o, lse = dw.o.cpu().numpy(), dw.lse.cpu().numpy()
+    assert_attention(o[seqs], lse[seqs], o_ref[seqs], lse_ref[seqs], f"ragged seqs {seqs}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# ------------------------------------------------------------------ merge
+
+def test_lse_merge_random_and_special():
+    akv, harness = _mods()
+    rng = np.random.default_rng(3)
+    for P, R, d in [(1, 5, 64), (3, 100, 128), (17, 7, 33), (64, 3, 256)]:
+        lp = rng.normal(0, 5, (P, R))
+        specials = np.array([-np.inf, 80.0, -80.0, 1e4, -1e4, 0.0])
+        mask = rng.random((P, R)) < 0.3
+        lp[mask] = rng.choice(specials, mask.sum())
+        lp[:, 0] = -np.inf            # an all-empty row
+        op = rng.normal(0, 1, (P, R, d))
+        op[np.isinf(lp)] = 0.0
+        o_ref, l_ref = O.lse_merge(op, lp)
+        top = torch.tensor(op, dtype=torch.float32, device="cuda")
+        tlp = torch.tensor(lp, dtype=torch.float32, device="cuda")
+        oo = torch.empty((R, d), dtype=torch.float32, device="cuda")
+        ll = torch.empty((R,), dtype=torch.float32, device="cuda")
+        akv.check(akv.akv_lse_merge(top.data_ptr(), tlp.data_ptr(), P, R, d, oo.data_ptr(), ll.data_ptr(),
+                                    harness.stream_handle()))
+        torch.cuda.synchronize()
+        lg = ll.cpu().numpy().astype(np.float64)
+        og = oo.cpu().numpy().astype(np.float64)
+        assert lg[0] == -np.inf and np.all(og[0] == 0)
+        fin = np.isfinite(l_ref)
+        assert np.array_equal(np.isfinite(lg), fin)
+        # fp32 merge of |lse| up to 1e4: allow the float32 spacing of the inputs
+        assert np.max(np.abs(lg[fin] - l_ref[fin]) / np.maximum(1.0, np.abs(l_ref[fin]))) < 2e-6
+        assert np.max(np.abs(og - o_ref)) < 1e-5 * max(1.0, np.max(np.abs(o_ref)))
