@@ -110,7 +110,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "seconds_per_call": per_call}
 
 
-def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None):
+def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None, split_quant=None, split_exact=None):
     import torch
     from long_context_kv_split_amd import akv, harness, synth
     w = synth.make(name) if w is None else w
@@ -118,7 +118,7 @@ def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None):
     kv_bytes = w.kv_bytes()
     n_rep = max(1, -(-min_bytes // kv_bytes))
     dw.add_replicas(n_rep)
-    descs = [dw.desc(r) for r in range(n_rep)]
+    descs = [dw.desc(r, split_exact=split_exact, split_quant=split_quant) for r in range(n_rep)]
     dw.ensure_ws(descs[0])
     h = stream.cuda_stream
     ws, wsb = harness.ptr(dw.ws), dw.ws_bytes
@@ -139,6 +139,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--aux", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--split-quant", type=int, default=0, help="compressed-tier split tokens (0 = library default)")
+    ap.add_argument("--split-exact", type=int, default=0, help="exact-tier split tokens (0 = library default)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the method's hot path runs on one GPU's share "
@@ -151,7 +155,9 @@ def main():
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         log("bench: building hybrid128k workload")
-        w, dw, kv_bytes, n_rep, ev_ms, wall_ms = bench_decode("hybrid128k", args.steps, args.warmup, stream)
+        w, dw, kv_bytes, n_rep, ev_ms, wall_ms = bench_decode("hybrid128k", args.steps, args.warmup, stream,
+                                                              split_quant=args.split_quant or None,
+                                                              split_exact=args.split_exact or None)
         log(f"bench: hybrid128k {ev_ms * 1e3:.2f} us/call (events), {wall_ms * 1e3:.2f} us/call (wall)")
         aux = {}
         if args.aux:
@@ -161,6 +167,13 @@ def main():
                              "kv_gbps": b2 / (e2 * 1e-3) / 1e9, "replicas": r2,
                              "decode_tokens_per_s": w2.B / (e2 * 1e-3)}
                 log(f"bench: {name} {e2 * 1e3:.2f} us/call")
+        if args.copy_mb:
+            src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"bench: copied {args.copy_mb} MiB x3 (counter calibration)")
     t_s = ev_ms * 1e-3
     gbps = kv_bytes / t_s / 1e9
     hist = int(w.quant_len.sum() + w.exact_len.sum())
@@ -189,7 +202,8 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16, 1% x8 outlier channels)",
         "config": {"workload": "hybrid128k", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "history_tokens": hist, "compressed_tokens": int(w.quant_len[0]),
-                   "exact_tokens": int(w.exact_len[0]), "split_tokens_quant": 1024, "split_tokens_exact": 2048,
+                   "exact_tokens": int(w.exact_len[0]), "split_tokens_quant": args.split_quant or 1024,
+                   "split_tokens_exact": args.split_exact or 1024,
                    "input_replicas": n_rep, "replica_bytes": kv_bytes * n_rep},
         "kv_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,

@@ -85,8 +85,10 @@ extern "C" {
  * history identically): a tier of n tokens is cut into ceil(n / P) splits of
  * P tokens, the last one shorter.  P defaults below; a descriptor may pass
  * another multiple of 64. */
-#define AKV_SPLIT_TOKENS_EXACT_DEFAULT 2048
+#define AKV_SPLIT_TOKENS_EXACT_DEFAULT 1024
 #define AKV_SPLIT_TOKENS_QUANT_DEFAULT 1024
+#define AKV_MAX_SPLIT_TOKENS 32768   /* largest split size served */
+#define AKV_MAX_SPLITS 2048          /* largest (compressed + exact) splits per sequence */
 #define AKV_MAX_CHUNK 512
 
 typedef enum akv_status {
@@ -184,11 +186,16 @@ size_t akv_decode_workspace_bytes(const akv_attn_desc* desc);
 size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc);
 
 /* Split-KV decode attention, one query token per sequence.
- * Enqueues: one split kernel (both tiers; the compressed tier with the
- * pre-rotated query and the value sum kept in rotated space) and one merge
- * kernel (merge compressed-tier partials, inverse-rotate once per head, merge
- * with the exact-tier partials).  ws must be 256-byte aligned and at least
- * akv_decode_workspace_bytes(desc) bytes. */
+ * Enqueues two kernels: a split kernel in which every (split, kv head,
+ * sequence) workgroup attends its split (the compressed tier with the
+ * pre-rotated query and the value sum kept in rotated space) and writes a
+ * partial, then a merge kernel that, per (sequence, query head), merges the
+ * compressed-tier partials, inverse-rotates once and merges with the
+ * exact-tier partials.  The merge uses a fixed reduction tree, so repeated
+ * calls give identical bytes.  ws (scratch for the partials; no state is
+ * kept between calls) must be 256-byte aligned and at least
+ * akv_decode_workspace_bytes(desc) bytes; calls that overlap in time on one
+ * workspace race. */
 akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill-chunk attention: Tq causal queries per sequence over the two-tier

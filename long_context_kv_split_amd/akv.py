@@ -29,8 +29,10 @@ STATUS_NAMES = {0: "AKV_OK", -1: "AKV_ERR_NULL", -2: "AKV_ERR_SHAPE", -3: "AKV_E
 
 BLOCK_TOKENS = 64
 GROUP = 32
-SPLIT_TOKENS_EXACT_DEFAULT = 2048
+SPLIT_TOKENS_EXACT_DEFAULT = 1024
 SPLIT_TOKENS_QUANT_DEFAULT = 1024
+MAX_SPLIT_TOKENS = 32768
+MAX_SPLITS = 2048
 MAX_CHUNK = 512
 
 

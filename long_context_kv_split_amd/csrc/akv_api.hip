@@ -82,10 +82,13 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan) {
   if (d->B > 65535 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
   const int Pe = split_tokens(d->split_tokens_exact, AKV_SPLIT_TOKENS_EXACT_DEFAULT);
   const int Pq = split_tokens(d->split_tokens_quant, AKV_SPLIT_TOKENS_QUANT_DEFAULT);
-  if (Pe > (1 << 20) || Pq > (1 << 20)) return fail(AKV_ERR_UNSUPPORTED, "split size above 2^20 tokens");
+  if (Pe > AKV_MAX_SPLIT_TOKENS || Pq > AKV_MAX_SPLIT_TOKENS)
+    return fail(AKV_ERR_UNSUPPORTED, "split size above %d tokens", AKV_MAX_SPLIT_TOKENS);
   const long long Se = ((long long)e.max_blocks * AKV_BLOCK_TOKENS + Pe - 1) / Pe;
   const long long Sq = ((long long)q.max_blocks * AKV_BLOCK_TOKENS + Pq - 1) / Pq;
-  if (Se + Sq > (1LL << 24)) return fail(AKV_ERR_UNSUPPORTED, "too many splits (%lld)", Se + Sq);
+  if (Se + Sq > AKV_MAX_SPLITS)
+    return fail(AKV_ERR_UNSUPPORTED, "%lld splits per sequence (max %d): use larger splits", Se + Sq,
+                AKV_MAX_SPLITS);
   if ((long long)d->Tq * d->Hq > (1LL << 30)) return fail(AKV_ERR_UNSUPPORTED, "Tq * Hq too large");
   // ---- ALIGN
   if (!aligned(d->q, 16)) return fail(AKV_ERR_ALIGN, "q must be 16-byte aligned");
@@ -146,8 +149,9 @@ akv::AttnParams make_params(const akv_attn_desc* d, const Plan& plan, void* ws) 
   p.Sq = plan.Sq;
   size_t po = plan.part_rows * d->d * sizeof(float);
   po = (po + 255) & ~(size_t)255;
-  p.part_o = static_cast<float*>(ws);
-  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + po);
+  char* base = static_cast<char*>(ws);
+  p.part_o = reinterpret_cast<float*>(base);
+  p.part_lse = reinterpret_cast<float*>(base + po);
   p.o = d->o;
   p.lse = d->lse;
   return p;

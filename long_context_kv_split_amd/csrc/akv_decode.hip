@@ -1,37 +1,46 @@
 // Split-KV decode attention over a two-tier history, and the exact
-// log-sum-exp merge (ActiveKV, "Context beyond VRAM", "What I built": exact
-// and compact tiers merged with exact attention arithmetic; the statistic
-// each partial carries is the log-sum-exp added to the paged-attention path in
-// "Bringing a serving stack up on new silicon", "What I built").
+// log-sum-exp merge (ActiveKV, "Context beyond VRAM", "What I built": exact and compact tiers merged with exact attention
+// arithmetic; each partial carries the log-sum-exp statistic that "Bringing a
+// serving stack up on new silicon", "What I built", adds to the
+// paged-attention path).
 //
 // One workgroup (4 waves) per (split, kv head, sequence).  A split is a fixed
 // run of P tokens of one tier; the waves take its 64-token blocks round-robin
-// and stream them in 32-token halves.  The G <= 8 query heads sharing the kv
-// head are the columns of 16x16x32 matrix-core tiles:
+// and stream them in 32-token units, loading the next unit while computing
+// the current one.  The G <= 8 query heads sharing the kv head are the columns
+// of 16x16x32 matrix-core tiles:
 //   scores:  D[token][col] = K_tile[token][dims] x Q[dims][col]
 //   values:  O^T[dim][col] += V^T[dim][tokens] x P^T[tokens][col]
 // Compressed tier (QuantForge walkthrough, section 1: the query is rotated
 // once instead of inverse-rotating blocks): the query is rotated by the
-// Walsh-Hadamard butterflies in fp32 and split into fp16 hi + lo halves
-// occupying columns 0..7 and 8..15, so the score keeps ~fp32 precision;
-// K codes are expanded through an LDS table into fp16 hi and lo parts of the
-// Lloyd-Max levels (two tiles per group), the fp16 group scale is applied to
-// the fp32 group partial score; V codes are expanded to fp16 level x scale.
-// The value sum stays in rotated space; the merge kernel inverse-rotates it.
-// Exact tier: bf16 K and q go straight into bf16 tiles (exact products);
-// V is staged in LDS to form the transposed operand.
-// Each wave keeps an online softmax (base-2, running max and sum); the four
-// waves merge in a fixed order, so repeated runs are bit-identical.
+// Walsh-Hadamard butterflies in fp32 and split into fp16 hi + lo parts held
+// in columns 0..7 and 8..15, so the score keeps ~fp32 precision; K codes are
+// expanded through an LDS table into fp16 hi and lo parts of the Lloyd-Max
+// levels (two tiles per group) and the fp16 group scale multiplies the fp32
+// group partial score; V codes are expanded to fp16 level x scale.  The table
+// has one 256-byte row per code byte: 32 copies of the (level, level) fp16 hi
+// pair, then 32 copies of the lo pair; lane l reads copy l % 32, which keeps
+// the random-row lookups of a wave free of bank conflicts.  The value
+// sum stays in rotated space.  Exact tier: bf16 K and q feed bf16 tiles
+// directly (exact products); V is staged in LDS to form the transposed
+// operand.  Each wave keeps an online softmax (base 2); the four waves merge
+// in a fixed order.
+//
+// A second kernel merges each (sequence, query head)'s partials: compressed-
+// tier splits (rotated space), one inverse rotation per head, exact-tier
+// splits, then the two tiers.  Its reduction tree is fixed, so repeated runs
+// are bit-identical.
 #include "akv_common.h"
 #include "akv_params.h"
 
 namespace akv {
 
-
-
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLdsBytes = 65536;
+constexpr int kMainLds = 65536;               // LUT / V staging / merge scratch
+constexpr int kMaxWaveBlocks = 128;           // blocks per wave per split (P <= 32768)
+constexpr int kScaleStage = 1024;             // per wave: one unit's K and V scales (512 B used)
+constexpr int kLdsBytes = kMainLds + kWaves * kScaleStage;
 constexpr int kVPitch = 260;  // bytes per staged exact-tier V row (bank spread)
 
 __device__ inline float4v mfma16(half8 a, half8 b, float4v c) {
@@ -49,19 +58,38 @@ __device__ inline float row_swap8(float x) {
 __device__ inline half2v u32_as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
 __device__ inline uint32_t h2_as_u32(half2v x) { return __builtin_bit_cast(uint32_t, x); }
 
+// LDS byte address of the level-table row of code byte k of w, plus off:
+// (byte k of w) * 256 + off, built with one byte permute.
+template <int k>
+__device__ inline uint32_t lut_addr(uint32_t w, uint32_t off) {
+  return __builtin_amdgcn_perm(w, off, 0x0C0C0000u | ((4u + k) << 8));
+}
+
 struct SoftmaxState {
   float m;  // running max (log2 units)
   float l;  // this lane's share of the running sum
 };
 
+// Value held by lane (l ^ 32) / lane (l ^ 16), through the gfx950 lane-swap
+// instructions (VALU, no LDS traffic).
+__device__ inline float xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ inline float xor16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+
 // Online-softmax step on 8 scores of one head held by this lane; the running
 // max is shared by the 4 lanes (rows 0..3 of 16) with the same column.
+// Returns the factor the running output must be scaled by.
 __device__ inline float softmax_step(SoftmaxState& st, float (&s)[8], float (&p)[8]) {
-  float mx = s[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  mx = fmaxf(mx, xor16(mx));
+  mx = fmaxf(mx, xor32(mx));
   float mnew = fmaxf(st.m, mx);
   float muse = (mnew == neg_inf()) ? 0.0f : mnew;
   float alpha = __builtin_amdgcn_exp2f(st.m - muse);
@@ -76,21 +104,62 @@ __device__ inline float softmax_step(SoftmaxState& st, float (&s)[8], float (&p)
   return alpha;
 }
 
+// Scale the running output unless no lane's running max moved.
+template <int NT>
+__device__ inline void rescale(float4v (&O)[NT], float alpha) {
+  if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) O[t] *= alpha;
+  }
+}
+
+struct Lds {
+  unsigned char* main;   // kMainLds bytes
+  unsigned char* stage;  // kWaves x kScaleStage scale staging
+};
+
+__device__ inline Lds lds_layout(unsigned char* smem) {
+  Lds L;
+  L.main = smem;
+  L.stage = smem + kMainLds;
+  return L;
+}
+
+// This wave's pool block ids: lane k holds the id of the wave's blocks k and
+// k + 64 (the wave takes blocks w, w + 4, ... of the split).
+struct WaveBlocks {
+  int lo, hi;
+  __device__ inline int get(int i) const {
+    return i < 64 ? __builtin_amdgcn_readlane(lo, i) : __builtin_amdgcn_readlane(hi, i - 64);
+  }
+};
+
+__device__ inline WaveBlocks load_wave_blocks(const int* table, int blk0, int nblk_w, int w, int lane) {
+  WaveBlocks wb;
+  wb.lo = lane < nblk_w ? table[blk0 + w + kWaves * lane] : -1;
+  wb.hi = lane + 64 < nblk_w ? table[blk0 + w + kWaves * (lane + 64)] : -1;
+  return wb;
+}
+
+__device__ inline size_t part_row(const AttnParams& p, int b, int kv, int sx) {
+  return ((size_t)(b * p.Hkv + kv) * (p.Sq + p.Se) + sx) * p.G;  // Tq = 1
+}
+
 // ------------------------------------------------------------------ epilogue
 // Merge the 4 waves' (m, l, O) of this workgroup and write the split partial.
 template <int D>
-__device__ void split_epilogue(const AttnParams& p, unsigned char* smem, int b, int kv, int sx,
-                               const SoftmaxState& st, const float4v (&O)[D / 16], bool poison) {
+__device__ void split_epilogue(const AttnParams& p, const Lds& L, int b, int kv, int sx, const SoftmaxState& st,
+                               const float4v (&O)[D / 16], bool poison) {
   constexpr int NT = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, qq = lane >> 4;
-  float* sm_m = reinterpret_cast<float*>(smem);           // [4][8]
-  float* sm_l = sm_m + kWaves * 8;                         // [4][8]
-  int* sm_bad = reinterpret_cast<int*>(sm_l + kWaves * 8); // [4]
-  float* sm_o = reinterpret_cast<float*>(smem + 512);      // [4][8][D]
+  float* sm_m = reinterpret_cast<float*>(L.main);          // [4][8]
+  float* sm_l = sm_m + kWaves * 8;                          // [4][8]
+  int* sm_bad = reinterpret_cast<int*>(sm_l + kWaves * 8);  // [4]
+  float* sm_o = reinterpret_cast<float*>(L.main + 512);     // [4][8][D]
   float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l += xor16(l);
+  l += xor32(l);
   __syncthreads();  // everyone is done with the LUT / staging region
   if (j < 8) {
 #pragma unroll
@@ -104,9 +173,9 @@ __device__ void split_epilogue(const AttnParams& p, unsigned char* smem, int b, 
   }
   if (lane == 0) sm_bad[w] = poison ? 1 : 0;
   __syncthreads();
-  const int G = p.G, S = p.Sq + p.Se;
+  const int G = p.G;
   const bool bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
-  const size_t prow = ((size_t)(b * p.Hkv + kv) * S + sx) * G;  // Tq = 1
+  const size_t prow = part_row(p, b, kv, sx);
   for (int idx = tid; idx < G * D; idx += kThreads) {
     int g = idx / D, t = idx - g * D;
     float M = neg_inf();
@@ -120,15 +189,15 @@ __device__ void split_epilogue(const AttnParams& p, unsigned char* smem, int b, 
       o = 0.0f;
       lse = neg_inf();
     } else {
-      float L = 0.0f, acc = 0.0f;
+      float Lsum = 0.0f, acc = 0.0f;
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
         float wv = __builtin_amdgcn_exp2f(sm_m[v * 8 + g] - M);
-        L += wv * sm_l[v * 8 + g];
+        Lsum += wv * sm_l[v * 8 + g];
         acc += wv * sm_o[(v * 8 + g) * D + t];
       }
-      o = acc / L;
-      lse = (M + __builtin_log2f(L)) * kLn2;
+      o = acc / Lsum;
+      lse = (M + __builtin_log2f(Lsum)) * kLn2;
     }
     p.part_o[(prow + g) * D + t] = o;
     if (t == 0) p.part_lse[prow + g] = lse;
@@ -137,30 +206,215 @@ __device__ void split_epilogue(const AttnParams& p, unsigned char* smem, int b, 
 
 // ------------------------------------------------------------- quant tier
 template <int D>
-__device__ void quant_split(const AttnParams& p, unsigned char* smem, int b, int kv, int sx, int start,
-                            int end) {
+struct QUnit {
+  uint32_t kw[2][D / 32];  // K code dwords: [tile][group]
+  uint32_t vw[D / 16];     // V code dwords: [value tile]
+  u32x4 sc;                // this lane's 16-byte slice of the unit's K|V scales
+};
+
+// Issue the loads of one 32-token unit (half c of pool block pb).
+template <int D>
+__device__ inline void quant_load(QUnit<D>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq, int lane) {
+  constexpr int M = D / 32, NT = D / 16;
+  const size_t slab = (size_t)pb * p.Hkv + kv;
+  const unsigned char* kcs = p.kc + slab * (32 * D);
+  const unsigned char* vcs = p.vc + slab * (32 * D);
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    int row = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
+    const unsigned char* src = kcs + row * (D / 2) + (D / 8) * qq;
+    if constexpr (M == 4) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(src);
+      u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1]; u.kw[tp][2] = x[2]; u.kw[tp][3] = x[3];
+    } else {
+      u32x2 x = *reinterpret_cast<const u32x2*>(src);
+      u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1];
+    }
+  }
+  const u32x4* vsrc = reinterpret_cast<const u32x4*>(vcs + ((c * 4 + qq) * 16 + j) * (D / 4));
+#pragma unroll
+  for (int v = 0; v < NT / 4; ++v) {
+    u32x4 x = vsrc[v];
+    u.vw[4 * v] = x[0]; u.vw[4 * v + 1] = x[1]; u.vw[4 * v + 2] = x[2]; u.vw[4 * v + 3] = x[3];
+  }
+  // scales of the unit: M K-groups then M V-groups, 64 bytes (32 tokens) each;
+  // lane (seg, part) carries bytes [16 part, 16 part + 16) of segment seg
+  const int lm = lane & (8 * M - 1), seg = lm >> 2, g = seg % M;
+  const uint16_t* sb = (seg < M ? p.ks : p.vs) + slab * (2 * D) + g * 64 + 32 * c + 8 * (lane & 3);
+  u.sc = *reinterpret_cast<const u32x4*>(sb);
+}
+
+template <int D, bool PARTIAL>
+__device__ inline void quant_compute(const QUnit<D>& u, int nvalid, const half8 (&Q)[D / 32],
+                                     const unsigned char* lut, unsigned char* stage, uint32_t loff, int qq,
+                                     int lane, SoftmaxState& st, float4v (&O)[D / 16]) {
+  constexpr int M = D / 32, NT = D / 16;
+  // scales: lanes < 8M hold the unit's 2M 64-byte segments; park them in LDS
+  // and read back this lane's 8 tokens per group (LDS ops of a wave run in order)
+  __builtin_amdgcn_wave_barrier();
+  if (lane < 8 * M) *reinterpret_cast<u32x4*>(stage + 16 * lane) = u.sc;
+  __builtin_amdgcn_wave_barrier();
+  u32x4 ksc[M], vsc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    ksc[m] = *reinterpret_cast<const u32x4*>(stage + 64 * m + 16 * qq);
+    vsc[m] = *reinterpret_cast<const u32x4*>(stage + 64 * (M + m) + 16 * qq);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (PARTIAL) {
+    // zero the value scales of missing tokens so 0 * garbage cannot appear
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        int t0 = 8 * qq + 2 * q2;
+        uint32_t x = vsc[m][q2];
+        if (t0 >= nvalid) x = 0;
+        else if (t0 + 1 >= nvalid) x &= 0xFFFFu;
+        vsc[m][q2] = x;
+      }
+  }
+  // ---- scores
+  float s[8];
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    float acc[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint32_t w = u.kw[tp][m];
+      const unsigned char* r0 = lut + lut_addr<0>(w, loff);
+      const unsigned char* r1 = lut + lut_addr<1>(w, loff);
+      const unsigned char* r2 = lut + lut_addr<2>(w, loff);
+      const unsigned char* r3 = lut + lut_addr<3>(w, loff);
+      half8 khi = __builtin_bit_cast(half8, u32x4{*reinterpret_cast<const uint32_t*>(r0),
+                                                  *reinterpret_cast<const uint32_t*>(r1),
+                                                  *reinterpret_cast<const uint32_t*>(r2),
+                                                  *reinterpret_cast<const uint32_t*>(r3)});
+      // keep the hi and lo reads as separate 32-bit reads (a paired read is slower here)
+      asm volatile("" ::: "memory");
+      half8 klo = __builtin_bit_cast(half8, u32x4{*reinterpret_cast<const uint32_t*>(r0 + 128),
+                                                  *reinterpret_cast<const uint32_t*>(r1 + 128),
+                                                  *reinterpret_cast<const uint32_t*>(r2 + 128),
+                                                  *reinterpret_cast<const uint32_t*>(r3 + 128)});
+      float4v dm = mfma16(khi, Q[m], float4v{0, 0, 0, 0});
+      dm = mfma16(klo, Q[m], dm);
+      // group scales of this lane's rows: tokens 8qq + 4tp + r (r = 0..3)
+      half2v s01 = u32_as_h2(ksc[m][2 * tp]), s23 = u32_as_h2(ksc[m][2 * tp + 1]);
+      acc[0] = fmaf((float)s01[0], dm[0], acc[0]);
+      acc[1] = fmaf((float)s01[1], dm[1], acc[1]);
+      acc[2] = fmaf((float)s23[0], dm[2], acc[2]);
+      acc[3] = fmaf((float)s23[1], dm[3], acc[3]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[4 * tp + r] = acc[r];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s[e] += row_swap8(s[e]);  // hi-column + lo-column partial scores
+    if (PARTIAL && 8 * qq + e >= nvalid) s[e] = neg_inf();
+  }
+  float pr[8];
+  rescale(O, softmax_step(st, s, pr));
+  half8 pb8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pb8[e] = (_Float16)pr[e];
+  // ---- values: V'^T[dim][token] = C16[code] * scale
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int g = t >> 1;
+    const uint32_t w = u.vw[t];
+    half2v l0 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<0>(w, loff)));
+    half2v l1 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<1>(w, loff)));
+    half2v l2 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<2>(w, loff)));
+    half2v l3 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<3>(w, loff)));
+    half2v x0 = l0 * u32_as_h2(vsc[g][0]);
+    half2v x1 = l1 * u32_as_h2(vsc[g][1]);
+    half2v x2 = l2 * u32_as_h2(vsc[g][2]);
+    half2v x3 = l3 * u32_as_h2(vsc[g][3]);
+    half8 a = __builtin_bit_cast(half8, u32x4{h2_as_u32(x0), h2_as_u32(x1), h2_as_u32(x2), h2_as_u32(x3)});
+    O[t] = mfma16(a, pb8, O[t]);
+  }
+}
+
+template <int D>
+__device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, int sx, int start, int end) {
   constexpr int M = D / 32;   // groups = score tiles per token tile
   constexpr int NT = D / 16;  // value tiles
+  constexpr int QV = D / 32;  // query values per lane in the rotation
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, qq = lane >> 4;
   const int G = p.G;
+  unsigned char* smem = L.main;
 
-  // --- rotated, pre-scaled query in LDS: q' = H q * (RN(1/sqrt d) * scale * log2 e)
-  float* qf = reinterpret_cast<float*>(smem);
-  const uint16_t* qsrc = p.q + ((size_t)b * p.Hq + kv * G) * D;
-  for (int i = tid; i < G * D; i += kThreads) qf[i] = bf16_bits_to_float(qsrc[i]);
-  __syncthreads();
-  for (int h = 1; h < D; h <<= 1) {
-    for (int i = tid; i < G * D / 2; i += kThreads) {
-      int g = i / (D / 2), r = i - g * (D / 2);
-      int lo = ((r & ~(h - 1)) << 1) | (r & (h - 1));
-      float a = qf[g * D + lo], c = qf[g * D + lo + h];
-      qf[g * D + lo] = a + c;
-      qf[g * D + lo + h] = a - c;
-    }
-    __syncthreads();
+  // requests first: this wave's block ids and this lane's query values
+  const int blk0 = start >> 6;
+  const int nblk = ((end + 63) >> 6) - blk0;
+  const int nblk_w = (nblk - w + kWaves - 1) / kWaves;
+  const int nunits = 2 * nblk_w;  // unit u = half (u & 1) of this wave's block u >> 1
+  const WaveBlocks wb = load_wave_blocks(p.qtab + (size_t)b * p.qmax, blk0, nblk_w, w, lane);
+  // rotation work split: wave w takes heads 2w, 2w+1; lane holds dims QV*(lane%32).. of head 2w + lane/32
+  const int rh = 2 * w + (lane >> 5), rd0 = QV * (lane & 31);
+  float qv[QV];
+  {
+    const uint16_t* qsrc = p.q + ((size_t)b * p.Hq + kv * G + min(rh, G - 1)) * D + rd0;
+#pragma unroll
+    for (int e = 0; e < QV; ++e) qv[e] = bf16_bits_to_float(qsrc[e]);
   }
+
+  // level table (needs nothing loaded): row e (code byte) = 256 B: 32 x hi pair | 32 x lo pair
+  {
+    const int e = tid;  // 256 threads, 256 rows
+    float c0 = __builtin_bit_cast(float, kLevelBits[e & 15]);
+    float c1 = __builtin_bit_cast(float, kLevelBits[e >> 4]);
+    _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+    _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+    const uint32_t hip = h2_as_u32(half2v{h0, h1});
+    const uint32_t lop = h2_as_u32(half2v{l0, l1});
+    uint32_t* row = reinterpret_cast<uint32_t*>(smem) + e * 64;
+    for (int k = 0; k < 32; ++k) {
+      const int slot = (k + e) & 31;  // rotate so that a wave's stores spread over banks
+      row[slot] = hip;
+      row[32 + slot] = lop;
+    }
+  }
+
+  // first two units' loads as soon as the block ids are in
+  auto block_of = [&](int u, bool& ok) {
+    int pb = wb.get(u >> 1);
+    ok = pb >= 0 && pb < p.qnb;
+    return ok ? pb : 0;
+  };
+  QUnit<D> u0, u1, u2;
+  bool ok0 = false, ok1 = false, ok2 = false;
+  if (nunits > 0) quant_load<D>(u0, p, block_of(0, ok0), kv, 0, j, qq, lane);
+  if (nunits > 1) quant_load<D>(u1, p, block_of(1, ok1), kv, 1, j, qq, lane);
+
+  // rotated, pre-scaled query q' = H q * (RN(1/sqrt d) * scale * log2 e):
+  // butterflies inside the lane for h < QV, across lanes (xor h/QV) above
+#pragma unroll
+  for (int h = 1; h < QV; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < QV; ++e)
+      if (!(e & h)) {
+        float a = qv[e], c = qv[e + h];
+        qv[e] = a + c;
+        qv[e + h] = a - c;
+      }
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < QV; ++e) {
+      float o = __shfl_xor(qv[e], h);
+      qv[e] = (lane & h) ? (o - qv[e]) : (qv[e] + o);
+    }
   const float qmul = inv_sqrt_d(D) * p.qscale2;
+  float* qf = reinterpret_cast<float*>(L.stage);  // [8][D] floats, reuses the scale stage area
+  static_assert(kWaves * kScaleStage >= 8 * 128 * 4, "query staging does not fit");
+  if (rh < G) {
+#pragma unroll
+    for (int e = 0; e < QV; ++e) qf[rh * D + rd0 + e] = qv[e] * qmul;
+  }
+  __syncthreads();
   half8 Q[M];
   {
     const int hj = j & 7;
@@ -169,168 +423,120 @@ __device__ void quant_split(const AttnParams& p, unsigned char* smem, int b, int
     for (int m = 0; m < M; ++m)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float v = hj < G ? qf[hj * D + 32 * m + 8 * qq + e] * qmul : 0.0f;
+        float v = hj < G ? qf[hj * D + 32 * m + 8 * qq + e] : 0.0f;
         _Float16 hi = (_Float16)v;
         _Float16 lo = (_Float16)(v - (float)hi);
         Q[m][e] = lopart ? lo : hi;
       }
   }
-  __syncthreads();
-
-  // --- level table: row e (code byte) = 256 B: 16 x (hi pair, lo pair) | 32 x hi pair
-  {
-    const int e = tid;  // 256 threads, 256 rows
-    float c0 = __builtin_bit_cast(float, kLevelBits[e & 15]);
-    float c1 = __builtin_bit_cast(float, kLevelBits[e >> 4]);
-    _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-    _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
-    uint32_t hip = h2_as_u32(half2v{h0, h1});
-    uint32_t lop = h2_as_u32(half2v{l0, l1});
-    uint32_t* row = reinterpret_cast<uint32_t*>(smem) + e * 64;
-    for (int k = 0; k < 64; ++k) {
-      int slot = (k + e) & 63;
-      row[slot] = (slot < 32 && (slot & 1)) ? lop : hip;
-    }
-  }
-  __syncthreads();
-  const unsigned char* lut = smem;
-  const int koff = 8 * j;                 // K copy of this lane
-  const int voff = 128 + 4 * (lane & 31); // V copy of this lane
+  __syncthreads();  // the query area becomes the scale stage
+  const uint32_t loff = 4 * (lane & 31);  // this lane's table copy
 
   SoftmaxState st{neg_inf(), 0.0f};
   float4v O[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) O[t] = float4v{0, 0, 0, 0};
   bool poison = false;
-
-  const int blk0 = start >> 6;
-  const int nblk = ((end + 63) >> 6) - blk0;
-  const int* table = p.qtab + (size_t)b * p.qmax;
-  for (int i = w; i < nblk; i += kWaves) {
-    const int blk = blk0 + i;
-    const int pb = table[blk];
-    if (pb < 0 || pb >= p.qnb) {
+  unsigned char* stage = L.stage + w * kScaleStage;
+  auto process = [&](const QUnit<D>& u, bool ok, int un) {
+    const int tb = (blk0 + w + kWaves * (un >> 1)) * 64 + 32 * (un & 1);
+    if (tb >= end) return;
+    if (!ok) {
       poison = true;
-      continue;
+      return;
     }
-    const size_t slab = (size_t)pb * p.Hkv + kv;
-    const unsigned char* kcs = p.kc + slab * (32 * D);
-    const unsigned char* vcs = p.vc + slab * (32 * D);
-    const uint16_t* kss = p.ks + slab * (2 * D);
-    const uint16_t* vss = p.vs + slab * (2 * D);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int tb = blk * 64 + 32 * c;  // first tier token of this half
-      if (tb >= end) break;
-      // ---- loads
-      uint32_t kw[2][M];
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        int row = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(kcs + row * (D / 2) + (D / 8) * qq);
-        if constexpr (M == 4) {
-          u32x4 x = *reinterpret_cast<const u32x4*>(src);
-          kw[tp][0] = x[0]; kw[tp][1] = x[1]; kw[tp][2] = x[2]; kw[tp][3] = x[3];
-        } else {
-          u32x2 x = *reinterpret_cast<const u32x2*>(src);
-          kw[tp][0] = x[0]; kw[tp][1] = x[1];
-        }
-      }
-      u32x4 ksc[M], vsc[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        ksc[m] = *reinterpret_cast<const u32x4*>(kss + m * 64 + 32 * c + 8 * qq);
-        vsc[m] = *reinterpret_cast<const u32x4*>(vss + m * 64 + 32 * c + 8 * qq);
-      }
-      uint32_t vw[NT];
-      {
-        const u32x4* src = reinterpret_cast<const u32x4*>(vcs + ((c * 4 + qq) * 16 + j) * (D / 4));
-#pragma unroll
-        for (int v = 0; v < NT / 4; ++v) {
-          u32x4 x = src[v];
-          vw[4 * v] = x[0]; vw[4 * v + 1] = x[1]; vw[4 * v + 2] = x[2]; vw[4 * v + 3] = x[3];
-        }
-      }
-      const int nvalid = end - tb;  // tokens of this half that exist (may exceed 32)
-      if (nvalid < 32) {
-        // zero the value scales of missing tokens so 0 * garbage cannot appear
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            int t0 = 8 * qq + 2 * q2;
-            uint32_t x = vsc[m][q2];
-            if (t0 >= nvalid) x = 0;
-            else if (t0 + 1 >= nvalid) x &= 0xFFFFu;
-            vsc[m][q2] = x;
-          }
-      }
-      // ---- scores
-      float s[8];
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        float acc[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          half8 khi, klo;
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            uint32_t e = (kw[tp][m] >> (8 * bb)) & 0xFFu;
-            u32x2 pr = *reinterpret_cast<const u32x2*>(lut + e * 256 + koff);
-            half2v h = u32_as_h2(pr[0]), l = u32_as_h2(pr[1]);
-            khi[2 * bb] = h[0]; khi[2 * bb + 1] = h[1];
-            klo[2 * bb] = l[0]; klo[2 * bb + 1] = l[1];
-          }
-          float4v dm = mfma16(khi, Q[m], float4v{0, 0, 0, 0});
-          dm = mfma16(klo, Q[m], dm);
-          // group scales of this lane's rows: tokens 8qq + 4tp + r (r = 0..3)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            int e2 = 4 * tp + r;
-            half2v sp = u32_as_h2(ksc[m][e2 >> 1]);
-            float sc = (float)sp[e2 & 1];
-            acc[r] = fmaf(sc, dm[r], acc[r]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[4 * tp + r] = acc[r];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s[e] += row_swap8(s[e]);  // hi-column + lo-column partial scores
-        if (8 * qq + e >= nvalid) s[e] = neg_inf();
-      }
-      float pr[8];
-      float alpha = softmax_step(st, s, pr);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) O[t] *= alpha;
-      half8 pb8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb8[e] = (_Float16)pr[e];
-      // ---- values: V'^T[dim][token] = C16[code] * scale
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int g = t >> 1;
-        half8 a;
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          uint32_t e = (vw[t] >> (8 * bb)) & 0xFFu;
-          half2v lv = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + e * 256 + voff));
-          half2v sv = u32_as_h2(vsc[g][bb]);
-          half2v x = lv * sv;
-          a[2 * bb] = x[0]; a[2 * bb + 1] = x[1];
-        }
-        O[t] = mfma16(a, pb8, O[t]);
-      }
-    }
+    if (end - tb >= 32)
+      quant_compute<D, false>(u, 32, Q, smem, stage, loff, qq, lane, st, O);
+    else
+      quant_compute<D, true>(u, end - tb, Q, smem, stage, loff, qq, lane, st, O);
+  };
+  // three unit buffers in a ring: unit u + 2 is in flight while unit u is computed
+  for (int un = 0; un < nunits; un += 3) {
+    if (un + 2 < nunits) quant_load<D>(u2, p, block_of(un + 2, ok2), kv, (un + 2) & 1, j, qq, lane);
+    process(u0, ok0, un);
+    if (un + 1 >= nunits) break;
+    if (un + 3 < nunits) quant_load<D>(u0, p, block_of(un + 3, ok0), kv, (un + 3) & 1, j, qq, lane);
+    process(u1, ok1, un + 1);
+    if (un + 2 >= nunits) break;
+    if (un + 4 < nunits) quant_load<D>(u1, p, block_of(un + 4, ok1), kv, (un + 4) & 1, j, qq, lane);
+    process(u2, ok2, un + 2);
   }
-  split_epilogue<D>(p, smem, b, kv, sx, st, O, poison);
+  split_epilogue<D>(p, L, b, kv, sx, st, O, poison);
 }
 
 // ------------------------------------------------------------- exact tier
 template <int D>
-__device__ void exact_split(const AttnParams& p, unsigned char* smem, int b, int kv, int sx, int start,
-                            int end) {
+struct EUnit {
+  u32x4 kx[2][D / 32];     // K rows of both 16-token tiles
+  u32x4 vx[32 * D / 512];  // V rows (16-byte chunks) of the 32 tokens
+};
+
+template <int D>
+__device__ inline void exact_load(EUnit<D>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq, int lane) {
+  constexpr int MK = D / 32, PER = 32 * D / 512;
+  const uint16_t* kslab = p.ek + ((size_t)pb * p.Hkv + kv) * kBlock * D;
+  const uint16_t* vslab = p.ev + ((size_t)pb * p.Hkv + kv) * kBlock * D;
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    int row = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
+    const u32x4* src = reinterpret_cast<const u32x4*>(kslab + row * D + qq * (D / 4));
+#pragma unroll
+    for (int m = 0; m < MK; ++m) u.kx[tp][m] = src[m];
+  }
+  const u32x4* vsrc = reinterpret_cast<const u32x4*>(vslab + 32 * c * D);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) u.vx[k] = vsrc[lane + 64 * k];
+}
+
+template <int D, bool PARTIAL>
+__device__ inline void exact_compute(const EUnit<D>& u, int nvalid, const bf16x8 (&Q)[D / 32], unsigned char* vst,
+                                     float qscale2, int j, int qq, int lane, SoftmaxState& st,
+                                     float4v (&O)[D / 16]) {
+  constexpr int MK = D / 32, NT = D / 16, CH = D / 8, PER = 32 * D / 512;
+  // ---- stage V rows (zeros for missing tokens); LDS ops of one wave run in order
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    int ci = lane + 64 * k, row = ci / CH, col = ci - row * CH;
+    u32x4 x = (!PARTIAL || row < nvalid) ? u.vx[k] : u32x4{0, 0, 0, 0};
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vst + row * kVPitch + col * 16);
+    dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
+  }
+  __builtin_amdgcn_wave_barrier();
+  // ---- scores
+  float s[8];
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    float4v dm = float4v{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < MK; ++m) dm = mfma16bf(__builtin_bit_cast(bf16x8, u.kx[tp][m]), Q[m], dm);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[4 * tp + r] = dm[r] * qscale2;
+  }
+  if (PARTIAL) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (8 * qq + e >= nvalid) s[e] = neg_inf();
+  }
+  float pr[8];
+  rescale(O, softmax_step(st, s, pr));
+  bf16x8 pb8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pb8[e] = (__bf16)pr[e];
+  // ---- values: V^T[dim 16t + j][token 8qq + e] from the staged rows
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    bf16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      a[e] = *reinterpret_cast<const __bf16*>(vst + (8 * qq + e) * kVPitch + (16 * t + j) * 2);
+    O[t] = mfma16bf(a, pb8, O[t]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int D>
+__device__ void exact_split(const AttnParams& p, const Lds& L, int b, int kv, int sx, int start, int end) {
   constexpr int MK = D / 32;  // score tiles per token tile
   constexpr int NT = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -349,7 +555,7 @@ __device__ void exact_split(const AttnParams& p, unsigned char* smem, int b, int
       Q[m] = __builtin_bit_cast(bf16x8, x);
     }
   }
-  unsigned char* vst = smem + w * (32 * kVPitch + 64);  // this wave's V staging rows
+  unsigned char* vst = L.main + w * (32 * kVPitch + 64);  // this wave's V staging rows
 
   SoftmaxState st{neg_inf(), 0.0f};
   float4v O[NT];
@@ -359,102 +565,235 @@ __device__ void exact_split(const AttnParams& p, unsigned char* smem, int b, int
 
   const int blk0 = start >> 6;
   const int nblk = ((end + 63) >> 6) - blk0;
-  const int* table = p.etab + (size_t)b * p.emax;
-  for (int i = w; i < nblk; i += kWaves) {
-    const int blk = blk0 + i;
-    const int pb = table[blk];
-    if (pb < 0 || pb >= p.enb) {
-      poison = true;
-      continue;
-    }
-    const uint16_t* kslab = p.ek + ((size_t)pb * p.Hkv + kv) * kBlock * D;
-    const uint16_t* vslab = p.ev + ((size_t)pb * p.Hkv + kv) * kBlock * D;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int tb = blk * 64 + 32 * c;
-      if (tb >= end) break;
-      const int nvalid = end - tb;
-      // ---- loads: K rows of both tiles; V half (32 rows)
-      u32x4 kx[2][MK];
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        int row = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
-        const u32x4* src = reinterpret_cast<const u32x4*>(kslab + row * D + qq * (D / 4));
-#pragma unroll
-        for (int m = 0; m < MK; ++m) kx[tp][m] = src[m];
-      }
-      constexpr int CH = D / 8;             // 16-byte chunks per row
-      constexpr int PER = 32 * CH / 64;     // chunks per lane
-      u32x4 vx[PER];
-      const u32x4* vsrc = reinterpret_cast<const u32x4*>(vslab + 32 * c * D);
-#pragma unroll
-      for (int k = 0; k < PER; ++k) vx[k] = vsrc[lane + 64 * k];
-      // ---- stage V rows (zeros for missing tokens); LDS ops of one wave run in order
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        int ci = lane + 64 * k, row = ci / CH, col = ci - row * CH;
-        u32x4 x = (row < nvalid) ? vx[k] : u32x4{0, 0, 0, 0};
-        uint32_t* dst = reinterpret_cast<uint32_t*>(vst + row * kVPitch + col * 16);
-        dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
-      }
-      __builtin_amdgcn_wave_barrier();
-      // ---- scores
-      float s[8];
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        float4v dm = float4v{0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < MK; ++m) dm = mfma16bf(__builtin_bit_cast(bf16x8, kx[tp][m]), Q[m], dm);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[4 * tp + r] = dm[r] * p.qscale2;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (8 * qq + e >= nvalid) s[e] = neg_inf();
-      float pr[8];
-      float alpha = softmax_step(st, s, pr);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) O[t] *= alpha;
-      bf16x8 pb8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb8[e] = (__bf16)pr[e];
-      // ---- values: V^T[dim 16t + j][token 8qq + e] from the staged rows
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        bf16x8 a;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          a[e] = *reinterpret_cast<const __bf16*>(vst + (8 * qq + e) * kVPitch + (16 * t + j) * 2);
-        O[t] = mfma16bf(a, pb8, O[t]);
-      }
-    }
+  const int nblk_w = (nblk - w + kWaves - 1) / kWaves;
+  const WaveBlocks wb = load_wave_blocks(p.etab + (size_t)b * p.emax, blk0, nblk_w, w, lane);
+  auto block_of = [&](int i, bool& ok) {
+    int pb = wb.get(i);
+    ok = pb >= 0 && pb < p.enb;
+    return ok ? pb : 0;
+  };
+  EUnit<D> ua, ub;
+  bool oka = false, okb = false;
+  if (nblk_w > 0) exact_load<D>(ua, p, block_of(0, oka), kv, 0, j, qq, lane);
+  for (int i = 0; i < nblk_w; ++i) {
+    int pb = block_of(i, okb);
+    exact_load<D>(ub, p, pb, kv, 1, j, qq, lane);
+    const int tb = (blk0 + w + kWaves * i) * 64;
+    if (!oka) poison = true;
+    else if (end - tb >= 32) exact_compute<D, false>(ua, 32, Q, vst, p.qscale2, j, qq, lane, st, O);
+    else exact_compute<D, true>(ua, end - tb, Q, vst, p.qscale2, j, qq, lane, st, O);
+    if (i + 1 < nblk_w) exact_load<D>(ua, p, block_of(i + 1, oka), kv, 0, j, qq, lane);
+    if (okb && end - tb >= 64) exact_compute<D, false>(ub, 32, Q, vst, p.qscale2, j, qq, lane, st, O);
+    else if (okb && end - tb > 32) exact_compute<D, true>(ub, end - tb - 32, Q, vst, p.qscale2, j, qq, lane, st, O);
   }
-  split_epilogue<D>(p, smem, b, kv, sx, st, O, poison);
+  split_epilogue<D>(p, L, b, kv, sx, st, O, poison);
+}
+
+// --------------------------------------------------------------- merging
+__device__ inline void merge_two(float oa, float la, float ob, float lb, float& o, float& lse) {
+  if (la != la || lb != lb) {
+    o = lse = __builtin_nanf("");
+    return;
+  }
+  float M = fmaxf(la, lb);
+  if (M == neg_inf()) {
+    o = 0.0f;
+    lse = neg_inf();
+    return;
+  }
+  float wa = __expf(la - M), wb = __expf(lb - M);
+  float W = wa + wb;
+  o = (wa / W) * oa + (wb / W) * ob;
+  lse = M + __logf(W);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  const Lds L = lds_layout(smem);
   const int sx = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int ql = p.qmax ? p.qlen[b] : 0;
+  const int el = p.emax ? p.elen[b] : 0;
+  if (ql < 0 || ql > p.qmax * 64 || el < 0 || el > p.emax * 64) return;  // merge reports NaN
   const bool quant = sx < p.Sq;
   const int s = quant ? sx : sx - p.Sq;
   const int P = quant ? p.Pq : p.Pe;
-  const int maxb = quant ? p.qmax : p.emax;
-  const int len = maxb ? (quant ? p.qlen[b] : p.elen[b]) : 0;
-  if (len < 0 || len > maxb * 64) return;  // merge reports the sequence as NaN
+  const int len = quant ? ql : el;
   const int start = s * P;
-  if (start >= len) return;
+  if (start >= len) return;  // idle split of a shorter sequence
   const int end = min(start + P, len);
   if (quant)
-    quant_split<D>(p, smem, b, kv, sx, start, end);
+    quant_split<D>(p, L, b, kv, sx, start, end);
   else
-    exact_split<D>(p, smem, b, kv, sx, start, end);
+    exact_split<D>(p, L, b, kv, sx, start, end);
 }
 
-// --------------------------------------------------------------- merging
-// Merge partials [first, first + n) (stride in partial rows) of one row in
-// ascending order; returns this thread's output element and the row lse.
+// Running merge of this thread's partials of one tier: (max, sum of weights,
+// weighted sum of outputs), all relative to the running max.
+struct MergeAcc {
+  float m, w;
+  float4v o;
+  bool nan;
+};
+
+__device__ inline void merge_acc_add(MergeAcc& a, float lse, float4v o) {
+  if (lse != lse) {
+    a.nan = true;
+    return;
+  }
+  if (lse == neg_inf()) return;
+  if (lse > a.m) {
+    const float r = (a.m == neg_inf()) ? 0.0f : __expf(a.m - lse);
+    a.w *= r;
+    a.o *= r;
+    a.m = lse;
+  }
+  const float e = __expf(lse - a.m);
+  a.w += e;
+  a.o += e * o;
+}
+
+// Fold this thread's share (splits ph, ph + PH, ...) of both tiers' partials
+// into aq / ae.  Each round issues the loads of up to 8 splits per tier
+// before using any of them.
+// Addresses use the allocated split counts aq_n / ae_n (known before the
+// lengths arrive), so the loads do not wait for the lengths; nq / ne mask.
+template <int D, int PH>
+__device__ inline void merge_scan(const AttnParams& p, size_t fq, int nq, size_t fe, int ne, size_t stride, int ph,
+                                  int c4, MergeAcc& aq, MergeAcc& ae) {
+  constexpr int K = 8;
+  const int sq_n = p.Sq, se_n = p.Se;
+  const int n = sq_n > se_n ? sq_n : se_n;
+  for (int s0 = ph; s0 < n; s0 += K * PH) {
+    float lq[K], le[K];
+    float4v xq[K], xe[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int s = s0 + k * PH;
+      const size_t rq = fq + (size_t)(s < sq_n ? s : 0) * stride;
+      const size_t re = fe + (size_t)(s < se_n ? s : 0) * stride;
+      lq[k] = p.part_lse[rq];
+      xq[k] = *reinterpret_cast<const float4v*>(p.part_o + rq * D + 4 * c4);
+      le[k] = p.part_lse[re];
+      xe[k] = *reinterpret_cast<const float4v*>(p.part_o + re * D + 4 * c4);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (s0 + k * PH < nq) merge_acc_add(aq, lq[k], xq[k]);
+      if (s0 + k * PH < ne) merge_acc_add(ae, le[k], xe[k]);
+    }
+  }
+}
+
+constexpr int kMergeThreads = 512;
+
+// Combine the PH per-phase accumulators of a tier (fixed order): writes the
+// phase-scaled outputs to phase[], returns (M, W, nan) through red[].
+template <int D, int PH>
+__device__ inline void merge_publish(const MergeAcc& acc, int ph, int c4, float* red, float* phase) {
+  if (c4 == 0) {
+    red[3 * ph + 0] = acc.m;
+    red[3 * ph + 1] = acc.w;
+    red[3 * ph + 2] = acc.nan ? 1.0f : 0.0f;
+  }
+  *reinterpret_cast<float4v*>(phase + ph * D + 4 * c4) = acc.o;
+}
+
+template <int PH>
+__device__ inline float merge_stats(const float* red, float* scale) {
+  float M = neg_inf(), nan = 0.0f;
+#pragma unroll
+  for (int k = 0; k < PH; ++k) {
+    M = fmaxf(M, red[3 * k]);
+    nan = fmaxf(nan, red[3 * k + 2]);
+  }
+  float W = 0.0f;
+#pragma unroll
+  for (int k = 0; k < PH; ++k) {
+    scale[k] = (M == neg_inf() || red[3 * k] == neg_inf()) ? 0.0f : __expf(red[3 * k] - M);
+    W += scale[k] * red[3 * k + 1];
+  }
+  if (nan != 0.0f) return __builtin_nanf("");
+  if (M == neg_inf()) return neg_inf();
+#pragma unroll
+  for (int k = 0; k < PH; ++k) scale[k] /= W;
+  return M + __logf(W);
+}
+
+// One workgroup per (query token, query head, sequence): (i) merge the
+// compressed-tier partials (rotated space), (ii) inverse-rotate once,
+// (iii) merge the exact-tier partials, (iv) merge the two tiers.  Thread
+// (phase, column) scans splits phase, phase + PH, ... of both tiers; the
+// phases are then combined in a fixed order.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
+  constexpr int C4 = D / 4, PH = kMergeThreads / C4, E = D / 64;
+  __shared__ float red[2][3 * PH];
+  __shared__ __attribute__((aligned(16))) float phase[2][PH * D];
+  const int row = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int tau = row / p.Hq, h = row - tau * p.Hq;
+  const int G = p.G, kv = h / G, g = h - kv * G;
+  const int S = p.Sq + p.Se;
+  float* out = p.o + (((size_t)b * p.Tq + tau) * p.Hq + h) * D;
+  float* lout = p.lse + ((size_t)b * p.Tq + tau) * p.Hq + h;
+  const size_t stride = (size_t)p.Tq * G;  // partial rows per split
+  const size_t base = ((size_t)(b * p.Hkv + kv) * S) * stride + (size_t)tau * G + g;
+  const int c4 = tid % C4, ph = tid / C4;
+  // the lengths and the partials are requested together: partials of splits
+  // this sequence does not have are loaded too (in bounds) and then ignored
+  const int ql = p.qmax ? p.qlen[b] : 0;
+  const int el = p.emax ? p.elen[b] : 0;
+  const bool bad = ql < 0 || ql > 64 * p.qmax || el < 0 || el > 64 * p.emax;
+  const int nq = bad ? 0 : (ql + p.Pq - 1) / p.Pq, ne = bad ? 0 : (el + p.Pe - 1) / p.Pe;
+  MergeAcc aq{neg_inf(), 0.0f, float4v{0, 0, 0, 0}, bad};
+  MergeAcc ae{neg_inf(), 0.0f, float4v{0, 0, 0, 0}, bad};
+  merge_scan<D, PH>(p, base, nq, base + (size_t)p.Sq * stride, ne, stride, ph, c4, aq, ae);
+  merge_publish<D, PH>(aq, ph, c4, red[0], phase[0]);
+  merge_publish<D, PH>(ae, ph, c4, red[1], phase[1]);
+  __syncthreads();
+  if (tid >= 64) return;
+  // wave 0: lane l owns dims l + 64 e
+  float sq[PH], se[PH];
+  const float lq = merge_stats<PH>(red[0], sq);
+  const float le = merge_stats<PH>(red[1], se);
+  float oq[E], oe[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int t = tid + 64 * e;
+    float vq = 0.0f, ve = 0.0f;
+#pragma unroll
+    for (int k = 0; k < PH; ++k) {
+      vq += sq[k] * phase[0][k * D + t];
+      ve += se[k] * phase[1][k * D + t];
+    }
+    oq[e] = vq;
+    oe[e] = ve;
+  }
+  // inverse rotation of the compressed-tier output: (H o_rot) * RN(1/sqrt d)
+#pragma unroll
+  for (int hh = 1; hh < 64 && hh < D; hh <<= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float o = __shfl_xor(oq[e], hh);
+      oq[e] = (tid & hh) ? (o - oq[e]) : (oq[e] + o);
+    }
+  if (E == 2) {
+    float a = oq[0], c = oq[E - 1];
+    oq[0] = a + c;
+    oq[E - 1] = a - c;
+  }
+  const float rd = inv_sqrt_d(D);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float o, lse;
+    merge_two(oq[e] * rd, lq, oe[e], le, o, lse);
+    out[tid + 64 * e] = o;
+    if (tid == 0 && e == 0) *lout = lse;
+  }
+}
+
+// --------------------------------------------------------------- standalone merge
+// Ascending-order merge of n partials of one row (akv_lse_merge).
 __device__ inline void merge_run(const float* po, const float* pl, size_t first, size_t stride, int n, int D,
                                  int t, float& o, float& lse) {
   float M = neg_inf();
@@ -484,65 +823,6 @@ __device__ inline void merge_run(const float* po, const float* pl, size_t first,
   lse = M + __logf(W);
 }
 
-__device__ inline void merge_two(float oa, float la, float ob, float lb, float& o, float& lse) {
-  if (la != la || lb != lb) {
-    o = lse = __builtin_nanf("");
-    return;
-  }
-  float M = fmaxf(la, lb);
-  if (M == neg_inf()) {
-    o = 0.0f;
-    lse = neg_inf();
-    return;
-  }
-  float wa = __expf(la - M), wb = __expf(lb - M);
-  float W = wa + wb;
-  o = (wa / W) * oa + (wb / W) * ob;
-  lse = M + __logf(W);
-}
-
-template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(AttnParams p) {
-  __shared__ float buf[D];
-  const int row = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int tau = row / p.Hq, h = row - tau * p.Hq;
-  const int G = p.G, kv = h / G, g = h - kv * G;
-  const int S = p.Sq + p.Se;
-  const int ql = p.qmax ? p.qlen[b] : 0;
-  const int el = p.emax ? p.elen[b] : 0;
-  float* out = p.o + (((size_t)b * p.Tq + tau) * p.Hq + h) * D;
-  float* lout = p.lse + ((size_t)b * p.Tq + tau) * p.Hq + h;
-  if (ql < 0 || ql > 64 * p.qmax || el < 0 || el > 64 * p.emax) {
-    out[t] = __builtin_nanf("");
-    if (t == 0) *lout = __builtin_nanf("");
-    return;
-  }
-  const int nq = (ql + p.Pq - 1) / p.Pq, ne = (el + p.Pe - 1) / p.Pe;
-  const size_t stride = (size_t)p.Tq * G;                               // partial rows per split
-  const size_t base = ((size_t)(b * p.Hkv + kv) * S) * stride + (size_t)tau * G + g;
-  // (i) compressed-tier partials, rotated space
-  float oq, lq;
-  merge_run(p.part_o, p.part_lse, base, stride, nq, D, t, oq, lq);
-  // (ii) inverse rotation once per head: o = (H o_rot) * RN(1/sqrt d)
-  buf[t] = oq;
-  __syncthreads();
-  for (int hh = 1; hh < D; hh <<= 1) {
-    float a = buf[t], c = buf[t ^ hh];
-    __syncthreads();
-    buf[t] = (t & hh) ? (c - a) : (a + c);
-    __syncthreads();
-  }
-  oq = buf[t] * inv_sqrt_d(D);
-  // (iii) exact-tier partials
-  float oe, le;
-  merge_run(p.part_o, p.part_lse, base + (size_t)p.Sq * stride, stride, ne, D, t, oe, le);
-  // (iv) both tiers
-  float o, lse;
-  merge_two(oq, lq, oe, le, o, lse);
-  out[t] = o;
-  if (t == 0) *lout = lse;
-}
-
 __global__ __launch_bounds__(256) void lse_merge_kernel(const float* op, const float* lp, int P, int R, int d,
                                                         float* o, float* lse) {
   const int r = blockIdx.x;
@@ -559,11 +839,21 @@ hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream) {
   dim3 mgrid(p.Tq * p.Hq, p.B);
   if (D == 64) {
     hipLaunchKernelGGL(split_decode_kernel<64>, grid, dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);
   } else {
     hipLaunchKernelGGL(split_decode_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
   }
+  return hipGetLastError();
+}
+
+// Merge kernel alone, for partials written by another split kernel (chunk).
+hipError_t launch_merge(const AttnParams& p, int D, hipStream_t stream) {
+  dim3 mgrid(p.Tq * p.Hq, p.B);
+  if (D == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -55,8 +55,8 @@ def test_exports_via_nm():
 
 def test_workspace_bytes_hybrid128k_shape():
     d = good_desc()
-    # splits: exact 64*64/2048 = 2, quant ceil(1936*64/1024) = 121 -> 123 splits
-    rows = 1 * 4 * 123 * 1 * 8
+    # splits: exact 64*64/1024 = 4, quant ceil(1936*64/1024) = 121 -> 125 splits
+    rows = 1 * 4 * 125 * 1 * 8
     po = (rows * 128 * 4 + 255) // 256 * 256
     assert akv.akv_decode_workspace_bytes(d) == po + rows * 4
     assert akv.akv_decode_workspace_bytes(good_desc(d=96)) == 0
@@ -93,6 +93,13 @@ def test_shape_errors():
 
 def test_unsupported():
     assert call(good_desc(d=256)) == akv.AKV_ERR_UNSUPPORTED
+    assert call(good_desc(split_tokens_quant=65536)) == akv.AKV_ERR_UNSUPPORTED
+    assert call(good_desc(split_tokens_quant=64), ws=0) == akv.AKV_ERR_WORKSPACE  # 1940 splits: served
+    q = good_desc().quant
+    q.max_blocks = 2100
+    q.num_blocks = 2100
+    assert call(good_desc(quant=q, split_tokens_quant=64)) == akv.AKV_ERR_UNSUPPORTED  # 2104 splits
+
     assert call(good_desc(Hq=64, Hkv=4)) == akv.AKV_ERR_UNSUPPORTED  # G = 16
     assert call(good_desc(Tq=2)) == akv.AKV_ERR_UNSUPPORTED          # decode is one query
     assert call(good_desc(Tq=513), chunk=True) == akv.AKV_ERR_UNSUPPORTED
