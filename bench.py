@@ -132,6 +132,45 @@ def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None, 
     return w, dw, kv_bytes, n_rep, ev_ms, wall_ms
 
 
+def chunk_flops(w) -> float:
+    """QK^T + PV multiply-adds x 2 of one chunk call: every query sees the whole
+    history before the chunk plus, causally, (Tq + 1) / 2 chunk tokens on average."""
+    hist = float(w.quant_len.sum() + w.exact_len.sum() - w.B * w.Tq)
+    return 4.0 * w.Tq * w.Hq * w.d * (hist / w.B + (w.Tq + 1) / 2.0) * w.B
+
+
+def bench_chunk(steps, warmup, stream, min_bytes=2 * MALL_BYTES):
+    """akv_attend_chunk on the 512-query chunk over a 32,768-token hybrid history."""
+    from long_context_kv_split_amd import akv, harness, synth
+    w = synth.make("chunk")
+    dw = harness.DeviceWorkload(w)
+    kv_bytes = w.kv_bytes()
+    n_rep = max(1, -(-min_bytes // kv_bytes))
+    dw.add_replicas(n_rep)
+    descs = [dw.desc(r) for r in range(n_rep)]
+    dw.ensure_ws(descs[0], chunk=True)
+    h = stream.cuda_stream
+    ws, wsb = harness.ptr(dw.ws), dw.ws_bytes
+
+    def call(r):
+        st = akv.akv_attend_chunk(descs[r], ws, wsb, h)
+        if st:
+            akv.check(st)
+
+    ev_ms, wall_ms = time_calls(call, n_rep, warmup, steps, stream)
+    flops = chunk_flops(w)
+    tflops = flops / (ev_ms * 1e-3) / 1e12
+    return {"workload": "chunk512 over 28,672 compressed + 4,096 exact + 512 chunk tokens, "
+                        "Hq 32 / Hkv 4, d 128",
+            "us_per_call": ev_ms * 1e3, "wall_us_per_call": wall_ms * 1e3, "steps": steps,
+            "query_tokens_per_s": w.B * w.Tq / (ev_ms * 1e-3), "kv_bytes": kv_bytes,
+            "kv_gbps": kv_bytes / (ev_ms * 1e-3) / 1e9, "replicas": n_rep,
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS["f16"],
+                         "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None,
+                         "kernel": "akv_attend_chunk (split + merge kernels, one call)",
+                         "algorithmic_flops_per_launch": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +178,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--aux", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the prefill-chunk line")
     ap.add_argument("--split-quant", type=int, default=0, help="compressed-tier split tokens (0 = library default)")
     ap.add_argument("--split-exact", type=int, default=0, help="exact-tier split tokens (0 = library default)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -167,6 +207,11 @@ def main():
                              "kv_gbps": b2 / (e2 * 1e-3) / 1e9, "replicas": r2,
                              "decode_tokens_per_s": w2.B / (e2 * 1e-3)}
                 log(f"bench: {name} {e2 * 1e3:.2f} us/call")
+        chunk = None
+        if not args.no_chunk:
+            log("bench: building chunk workload")
+            chunk = bench_chunk(max(20, args.steps // 20), 5, stream)
+            log(f"bench: chunk {chunk['us_per_call']:.1f} us/call, {chunk['roofline']['achieved']:.1f} TFLOP/s")
         if args.copy_mb:
             src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")
             dst = torch.empty_like(src)
@@ -213,6 +258,8 @@ def main():
         "cpu_baseline": cpu,
         "kernel_source_hash": khash,
     }
+    if chunk:
+        out["chunk"] = chunk
     if aux:
         out["aux"] = aux
     print(json.dumps(out), flush=True)

@@ -87,6 +87,12 @@ extern "C" {
  * another multiple of 64. */
 #define AKV_SPLIT_TOKENS_EXACT_DEFAULT 1024
 #define AKV_SPLIT_TOKENS_QUANT_DEFAULT 1024
+/* akv_attend_chunk's default instead: with Tq*G rows per kv head taken in
+ * row groups of AKV_CHUNK_ROWS, a tier of max_blocks blocks is cut into
+ * want = ceil(AKV_CHUNK_TARGET_WORKGROUPS / (B * Hkv * row groups)) runs of
+ * P = 64 * ceil(max_blocks / want) tokens (at most AKV_MAX_SPLIT_TOKENS). */
+#define AKV_CHUNK_ROWS 128
+#define AKV_CHUNK_TARGET_WORKGROUPS 512
 #define AKV_MAX_SPLIT_TOKENS 32768   /* largest split size served */
 #define AKV_MAX_SPLITS 2048          /* largest (compressed + exact) splits per sequence */
 #define AKV_MAX_CHUNK 512
@@ -136,8 +142,8 @@ typedef struct akv_attn_desc {
   const uint16_t* q;           /* bf16 [B][Tq][Hq][d], 4-byte aligned */
   akv_exact_tier exact;
   akv_quant_tier quant;
-  int32_t split_tokens_exact;  /* 0 => AKV_SPLIT_TOKENS_EXACT_DEFAULT */
-  int32_t split_tokens_quant;  /* 0 => AKV_SPLIT_TOKENS_QUANT_DEFAULT */
+  int32_t split_tokens_exact;  /* 0 => default (decode: AKV_SPLIT_TOKENS_EXACT_DEFAULT) */
+  int32_t split_tokens_quant;  /* 0 => default (decode: AKV_SPLIT_TOKENS_QUANT_DEFAULT) */
   float* o;                    /* fp32 [B][Tq][Hq][d] normalized output */
   float* lse;                  /* fp32 [B][Tq][Hq] natural-log sum of exp(scores) */
 } akv_attn_desc;
@@ -199,8 +205,18 @@ size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc);
 akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill-chunk attention: Tq causal queries per sequence over the two-tier
- * history (matrix-core tiles), then the same merge.  ws as above with
- * akv_chunk_workspace_bytes(desc). */
+ * history (the prefill side of ActiveKV's two-tier cache; causal rule in the
+ * akv_attn_desc comment).  Enqueues two kernels: a split kernel on 16x16x32
+ * matrix-core tiles in which every (128 (query, head) rows of a kv head,
+ * split, sequence) workgroup expands each block of its split into LDS once
+ * (compressed K as fp16 hi + lo parts against a hi + lo rotated query; exact
+ * K/V as bf16) and writes one partial per row, then a merge kernel that per
+ * (sequence, query, head) merges the partials in ascending split order,
+ * inverse-rotates the compressed-tier result once and merges the tiers.
+ * Repeated calls give identical bytes.  A sequence whose exact length is
+ * below Tq (the chunk must be in the exact tier) or whose lengths are out of
+ * range gets NaN outputs.  ws as for decode, with
+ * akv_chunk_workspace_bytes(desc) bytes. */
 akv_status akv_attend_chunk(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
 /* Exact log-sum-exp merge of P normalized partials of R rows of width d:

@@ -4,6 +4,7 @@
 // VRAM", "What I built": requests that cannot be served are refused), the
 // fixed split rule, workspace layout and kernel launches on the caller's
 // stream.  No allocation, no synchronization, no retained pointers.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -80,8 +81,21 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan) {
   if (chunk && d->Tq > AKV_MAX_CHUNK) return fail(AKV_ERR_UNSUPPORTED, "chunk Tq %d > %d", d->Tq, AKV_MAX_CHUNK);
   if (chunk && e.max_blocks == 0) return fail(AKV_ERR_UNSUPPORTED, "chunk needs the exact tier (it holds the chunk)");
   if (d->B > 65535 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
-  const int Pe = split_tokens(d->split_tokens_exact, AKV_SPLIT_TOKENS_EXACT_DEFAULT);
-  const int Pq = split_tokens(d->split_tokens_quant, AKV_SPLIT_TOKENS_QUANT_DEFAULT);
+  int Pe = split_tokens(d->split_tokens_exact, AKV_SPLIT_TOKENS_EXACT_DEFAULT);
+  int Pq = split_tokens(d->split_tokens_quant, AKV_SPLIT_TOKENS_QUANT_DEFAULT);
+  if (chunk) {
+    // each tier in about AKV_CHUNK_TARGET_WORKGROUPS / (B * Hkv * row groups)
+    // equal runs of whole blocks (a shape-only rule, like the decode one)
+    const long long nrg = ((long long)d->Tq * G + AKV_CHUNK_ROWS - 1) / AKV_CHUNK_ROWS;
+    const long long units = (long long)d->B * d->Hkv * nrg;
+    const long long want = std::max(1LL, (AKV_CHUNK_TARGET_WORKGROUPS + units - 1) / units);
+    auto dflt = [&](int max_blocks) {
+      const long long blocks = std::max(1LL, (max_blocks + want - 1) / want);
+      return (int)std::min<long long>(blocks * AKV_BLOCK_TOKENS, AKV_MAX_SPLIT_TOKENS);
+    };
+    Pe = split_tokens(d->split_tokens_exact, dflt(e.max_blocks));
+    Pq = split_tokens(d->split_tokens_quant, dflt(q.max_blocks));
+  }
   if (Pe > AKV_MAX_SPLIT_TOKENS || Pq > AKV_MAX_SPLIT_TOKENS)
     return fail(AKV_ERR_UNSUPPORTED, "split size above %d tokens", AKV_MAX_SPLIT_TOKENS);
   const long long Se = ((long long)e.max_blocks * AKV_BLOCK_TOKENS + Pe - 1) / Pe;

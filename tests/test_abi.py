@@ -62,6 +62,29 @@ def test_workspace_bytes_hybrid128k_shape():
     assert akv.akv_decode_workspace_bytes(good_desc(d=96)) == 0
 
 
+def test_chunk_split_planner_c5_shape():
+    # 512 queries x 8 heads per kv head = 32 row groups of 128; 4 kv heads ->
+    # 128 units, so each tier is cut into ceil(512 / 128) = 4 runs of blocks
+    e = akv.ExactTier(k=FAKE, v=FAKE + 0x1000000, block_table=FAKE + 0x2000000, lengths=FAKE + 0x2100000,
+                      max_blocks=72, num_blocks=72)
+    q = good_desc().quant
+    q.max_blocks = q.num_blocks = 456
+    d = good_desc(Tq=512, exact=e, quant=q)
+    # exact: 18 blocks = 1152 tokens -> 4 splits; compressed: 114 blocks = 7296 -> 4 splits
+    rows = 1 * 4 * (4 + 4) * 512 * 8
+    assert akv.akv_chunk_workspace_bytes(d) == rows * 128 * 4 + rows * 4
+    # explicit sizes still win
+    d2 = good_desc(Tq=512, exact=e, quant=q, split_tokens_exact=4608, split_tokens_quant=29184)
+    rows = 1 * 4 * 2 * 512 * 8
+    assert akv.akv_chunk_workspace_bytes(d2) == rows * 128 * 4 + rows * 4
+    # the decode rule is unchanged (1024-token splits)
+    assert akv.akv_decode_workspace_bytes(good_desc(exact=e, quant=q)) == (4 * (5 + 29) * 8) * 516
+    # a small chunk still gets whole-block splits, never above the maximum
+    d3 = good_desc(Tq=1, Hq=4, Hkv=1, exact=e, quant=q)
+    rows = 1 * 1 * (72 + 456) * 1 * 4      # 512 units wanted -> one block per split
+    assert akv.akv_chunk_workspace_bytes(d3) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+
+
 def test_null_checks_first():
     assert akv.LIB.akv_attend_decode(None, None, 0, None) == akv.AKV_ERR_NULL
     assert call(good_desc(q=0)) == akv.AKV_ERR_NULL
