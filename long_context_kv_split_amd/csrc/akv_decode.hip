@@ -39,7 +39,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMainLds = 65536;               // LUT / V staging / merge scratch
 constexpr int kMaxWaveBlocks = 128;           // blocks per wave per split (P <= 32768)
-constexpr int kScaleStage = 1024;             // per wave: one unit's K and V scales (512 B used)
+constexpr int kScaleStage = 1056;             // per wave: one unit's K and V scales (512 B used)
 constexpr int kLdsBytes = kMainLds + kWaves * kScaleStage;
 constexpr int kVPitch = 260;  // bytes per staged exact-tier V row (bank spread)
 
@@ -50,10 +50,23 @@ __device__ inline float4v mfma16bf(bf16x8 a, bf16x8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// value of lane (l ^ 8) within each row of 16 lanes
-__device__ inline float row_swap8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
+// Lane exchanges inside rows of 16 lanes through DPP (VALU, no LDS):
+// quad_perm [1,0,3,2] / [2,3,0,1] give lane l ^ 1 / l ^ 2; row_ror:r gives
+// lane (l - r) mod 16, so l ^ 4 is row_ror:4 on lanes with bit 2 set and
+// row_ror:12 on the others, and l ^ 8 is row_ror:8.
+template <int CTRL>
+__device__ inline float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
+__device__ inline float xor1(float x) { return dpp_mov<0xB1>(x); }
+__device__ inline float xor2(float x) { return dpp_mov<0x4E>(x); }
+__device__ inline float xor4(float x) {
+  const float a = dpp_mov<0x124>(x), b = dpp_mov<0x12C>(x);
+  return (threadIdx.x & 4) ? a : b;
+}
+__device__ inline float xor8(float x) { return dpp_mov<0x128>(x); }
+// value of lane (l ^ 8) within each row of 16 lanes
+__device__ inline float row_swap8(float x) { return xor8(x); }
 
 __device__ inline half2v u32_as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
 __device__ inline uint32_t h2_as_u32(half2v x) { return __builtin_bit_cast(uint32_t, x); }
@@ -81,6 +94,25 @@ __device__ inline float xor16(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+// Value held by lane l ^ h (h a power of two below 64), all on the VALU.
+template <int H>
+__device__ inline float lane_xor(float x) {
+  if constexpr (H == 1) return xor1(x);
+  else if constexpr (H == 2) return xor2(x);
+  else if constexpr (H == 4) return xor4(x);
+  else if constexpr (H == 8) return xor8(x);
+  else if constexpr (H == 16) return xor16(x);
+  else return xor32(x);
+}
+
+// One butterfly stage across lanes: (a, b) -> (a + b, a - b) with a on the
+// lane whose bit H is clear.
+template <int H>
+__device__ inline float lane_butterfly(float x, int lane) {
+  const float o = lane_xor<H>(x);
+  return (lane & H) ? (o - x) : (x + o);
 }
 
 // Online-softmax step on 8 scores of one head held by this lane; the running
@@ -141,8 +173,10 @@ __device__ inline WaveBlocks load_wave_blocks(const int* table, int blk0, int nb
   return wb;
 }
 
-__device__ inline size_t part_row(const AttnParams& p, int b, int kv, int sx) {
-  return ((size_t)(b * p.Hkv + kv) * (p.Sq + p.Se) + sx) * p.G;  // Tq = 1
+// Decode partials are laid out per query head: row ((b * Hkv + kv) * G + g)
+// * (Sq + Se) + split, so one head's splits are contiguous for the merge.
+__device__ inline size_t part_row(const AttnParams& p, int b, int kv, int g, int sx) {
+  return ((size_t)(b * p.Hkv + kv) * p.G + g) * (p.Sq + p.Se) + sx;
 }
 
 // ------------------------------------------------------------------ epilogue
@@ -150,22 +184,22 @@ __device__ inline size_t part_row(const AttnParams& p, int b, int kv, int sx) {
 template <int D>
 __device__ void split_epilogue(const AttnParams& p, const Lds& L, int b, int kv, int sx, const SoftmaxState& st,
                                const float4v (&O)[D / 16], bool poison) {
-  constexpr int NT = D / 16;
+  constexpr int NT = D / 16, C4 = D / 4;
+  constexpr int OP = D + 4;  // padded rows: the 8 heads' float4 stores of one wave hit distinct banks
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, qq = lane >> 4;
   float* sm_m = reinterpret_cast<float*>(L.main);          // [4][8]
   float* sm_l = sm_m + kWaves * 8;                          // [4][8]
   int* sm_bad = reinterpret_cast<int*>(sm_l + kWaves * 8);  // [4]
-  float* sm_o = reinterpret_cast<float*>(L.main + 512);     // [4][8][D]
+  float* sm_o = reinterpret_cast<float*>(L.main + 512);     // [4][8][OP]
   float l = st.l;
   l += xor16(l);
   l += xor32(l);
   __syncthreads();  // everyone is done with the LUT / staging region
   if (j < 8) {
+    // lane (col j, qq) holds O^T[16t + 4qq + r][j]: one float4 of head j per t
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[(w * 8 + j) * D + 16 * t + 4 * qq + r] = O[t][r];
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<float4v*>(sm_o + (w * 8 + j) * OP + 16 * t + 4 * qq) = O[t];
     if (qq == 0) {
       sm_m[w * 8 + j] = st.m;
       sm_l[w * 8 + j] = l;
@@ -175,32 +209,34 @@ __device__ void split_epilogue(const AttnParams& p, const Lds& L, int b, int kv,
   __syncthreads();
   const int G = p.G;
   const bool bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
-  const size_t prow = part_row(p, b, kv, sx);
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    int g = idx / D, t = idx - g * D;
+  for (int idx = tid; idx < G * C4; idx += kThreads) {
+    const int g = idx / C4, c4 = idx - g * C4;
     float M = neg_inf();
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v * 8 + g]);
-    float o, lse;
+    float4v o;
+    float lse;
     if (bad) {
-      o = __builtin_nanf("");
-      lse = o;
+      lse = __builtin_nanf("");
+      o = float4v{1, 1, 1, 1} * lse;
     } else if (M == neg_inf()) {
-      o = 0.0f;
+      o = float4v{0, 0, 0, 0};
       lse = neg_inf();
     } else {
-      float Lsum = 0.0f, acc = 0.0f;
+      float Lsum = 0.0f;
+      float4v acc = float4v{0, 0, 0, 0};
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
-        float wv = __builtin_amdgcn_exp2f(sm_m[v * 8 + g] - M);
+        const float wv = __builtin_amdgcn_exp2f(sm_m[v * 8 + g] - M);
         Lsum += wv * sm_l[v * 8 + g];
-        acc += wv * sm_o[(v * 8 + g) * D + t];
+        acc += wv * *reinterpret_cast<const float4v*>(sm_o + (v * 8 + g) * OP + 4 * c4);
       }
-      o = acc / Lsum;
+      o = acc * (1.0f / Lsum);
       lse = (M + __builtin_log2f(Lsum)) * kLn2;
     }
-    p.part_o[(prow + g) * D + t] = o;
-    if (t == 0) p.part_lse[prow + g] = lse;
+    const size_t prow = part_row(p, b, kv, g, sx);
+    *reinterpret_cast<float4v*>(p.part_o + prow * D + 4 * c4) = o;
+    if (c4 == 0) p.part_lse[prow] = lse;
   }
 }
 
@@ -371,10 +407,12 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
     const uint32_t hip = h2_as_u32(half2v{h0, h1});
     const uint32_t lop = h2_as_u32(half2v{l0, l1});
     uint32_t* row = reinterpret_cast<uint32_t*>(smem) + e * 64;
-    for (int k = 0; k < 32; ++k) {
-      const int slot = (k + e) & 31;  // rotate so that a wave's stores spread over banks
-      row[slot] = hip;
-      row[32 + slot] = lop;
+    const u32x4 h4 = u32x4{hip, hip, hip, hip}, l4 = u32x4{lop, lop, lop, lop};
+#pragma unroll
+    for (int k = 0; k < 32; k += 4) {
+      const int slot = (k + 4 * (e & 7)) & 31;  // 8 consecutive rows' stores start in distinct banks
+      *reinterpret_cast<u32x4*>(row + slot) = h4;
+      *reinterpret_cast<u32x4*>(row + 32 + slot) = l4;
     }
   }
 
@@ -401,18 +439,26 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
         qv[e + h] = a - c;
       }
 #pragma unroll
-  for (int h = 1; h < 32; h <<= 1)
-#pragma unroll
-    for (int e = 0; e < QV; ++e) {
-      float o = __shfl_xor(qv[e], h);
-      qv[e] = (lane & h) ? (o - qv[e]) : (qv[e] + o);
-    }
+  for (int e = 0; e < QV; ++e) {
+    qv[e] = lane_butterfly<1>(qv[e], lane);
+    qv[e] = lane_butterfly<2>(qv[e], lane);
+    qv[e] = lane_butterfly<4>(qv[e], lane);
+    qv[e] = lane_butterfly<8>(qv[e], lane);
+    qv[e] = lane_butterfly<16>(qv[e], lane);
+  }
   const float qmul = inv_sqrt_d(D) * p.qscale2;
-  float* qf = reinterpret_cast<float*>(L.stage);  // [8][D] floats, reuses the scale stage area
-  static_assert(kWaves * kScaleStage >= 8 * 128 * 4, "query staging does not fit");
+  // staged q' rows of D + 4 floats: the 8 rows read by one 128-bit LDS read
+  // start in distinct banks
+  constexpr int QP = D + 4;
+  float* qf = reinterpret_cast<float*>(L.stage);  // [8][QP] floats, reuses the scale stage area
+  static_assert(kWaves * kScaleStage >= 8 * (128 + 4) * 4, "query staging does not fit");
   if (rh < G) {
+    float* dst = qf + rh * QP + rd0;
+    if constexpr (QV == 4)
+      *reinterpret_cast<float4v*>(dst) = float4v{qv[0] * qmul, qv[1] * qmul, qv[2] * qmul, qv[3] * qmul};
+    else
 #pragma unroll
-    for (int e = 0; e < QV; ++e) qf[rh * D + rd0 + e] = qv[e] * qmul;
+      for (int e = 0; e < QV; ++e) dst[e] = qv[e] * qmul;
   }
   __syncthreads();
   half8 Q[M];
@@ -420,14 +466,19 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
     const int hj = j & 7;
     const bool lopart = j >= 8;
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+    for (int m = 0; m < M; ++m) {
+      const float* src = qf + hj * QP + 32 * m + 8 * qq;
+      float4v a = *reinterpret_cast<const float4v*>(src);
+      float4v c = *reinterpret_cast<const float4v*>(src + 4);
+      if (hj >= G) a = c = float4v{0, 0, 0, 0};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float v = hj < G ? qf[hj * D + 32 * m + 8 * qq + e] : 0.0f;
+        const float v = e < 4 ? a[e] : c[e - 4];
         _Float16 hi = (_Float16)v;
         _Float16 lo = (_Float16)(v - (float)hi);
         Q[m][e] = lopart ? lo : hi;
       }
+    }
   }
   __syncthreads();  // the query area becomes the scale stage
   const uint32_t loff = 4 * (lane & 31);  // this lane's table copy
@@ -603,7 +654,8 @@ __device__ inline void merge_two(float oa, float la, float ob, float lb, float& 
   }
   float wa = __expf(la - M), wb = __expf(lb - M);
   float W = wa + wb;
-  o = (wa / W) * oa + (wb / W) * ob;
+  const float rW = 1.0f / W;
+  o = (wa * rW) * oa + (wb * rW) * ob;
   lse = M + __logf(W);
 }
 
@@ -628,134 +680,116 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(AttnParams p)
     exact_split<D>(p, L, b, kv, sx, start, end);
 }
 
-// Running merge of this thread's partials of one tier: (max, sum of weights,
-// weighted sum of outputs), all relative to the running max.
-struct MergeAcc {
-  float m, w;
-  float4v o;
-  bool nan;
-};
-
-__device__ inline void merge_acc_add(MergeAcc& a, float lse, float4v o) {
-  if (lse != lse) {
-    a.nan = true;
-    return;
-  }
-  if (lse == neg_inf()) return;
-  if (lse > a.m) {
-    const float r = (a.m == neg_inf()) ? 0.0f : __expf(a.m - lse);
-    a.w *= r;
-    a.o *= r;
-    a.m = lse;
-  }
-  const float e = __expf(lse - a.m);
-  a.w += e;
-  a.o += e * o;
-}
-
-// Fold this thread's share (splits ph, ph + PH, ...) of both tiers' partials
-// into aq / ae.  Each round issues the loads of up to 8 splits per tier
-// before using any of them.
-// Addresses use the allocated split counts aq_n / ae_n (known before the
-// lengths arrive), so the loads do not wait for the lengths; nq / ne mask.
-template <int D, int PH>
-__device__ inline void merge_scan(const AttnParams& p, size_t fq, int nq, size_t fe, int ne, size_t stride, int ph,
-                                  int c4, MergeAcc& aq, MergeAcc& ae) {
-  constexpr int K = 8;
-  const int sq_n = p.Sq, se_n = p.Se;
-  const int n = sq_n > se_n ? sq_n : se_n;
-  for (int s0 = ph; s0 < n; s0 += K * PH) {
-    float lq[K], le[K];
-    float4v xq[K], xe[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int s = s0 + k * PH;
-      const size_t rq = fq + (size_t)(s < sq_n ? s : 0) * stride;
-      const size_t re = fe + (size_t)(s < se_n ? s : 0) * stride;
-      lq[k] = p.part_lse[rq];
-      xq[k] = *reinterpret_cast<const float4v*>(p.part_o + rq * D + 4 * c4);
-      le[k] = p.part_lse[re];
-      xe[k] = *reinterpret_cast<const float4v*>(p.part_o + re * D + 4 * c4);
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (s0 + k * PH < nq) merge_acc_add(aq, lq[k], xq[k]);
-      if (s0 + k * PH < ne) merge_acc_add(ae, le[k], xe[k]);
-    }
-  }
-}
-
 constexpr int kMergeThreads = 512;
 
-// Combine the PH per-phase accumulators of a tier (fixed order): writes the
-// phase-scaled outputs to phase[], returns (M, W, nan) through red[].
-template <int D, int PH>
-__device__ inline void merge_publish(const MergeAcc& acc, int ph, int c4, float* red, float* phase) {
-  if (c4 == 0) {
-    red[3 * ph + 0] = acc.m;
-    red[3 * ph + 1] = acc.w;
-    red[3 * ph + 2] = acc.nan ? 1.0f : 0.0f;
-  }
-  *reinterpret_cast<float4v*>(phase + ph * D + 4 * c4) = acc.o;
+// Sum / max over the 64 lanes of a wave in a fixed butterfly order (every
+// lane ends with the same value).
+__device__ inline float wave_sum(float x) {
+  x += xor1(x);
+  x += xor2(x);
+  x += xor4(x);
+  x += xor8(x);
+  x += xor16(x);
+  x += xor32(x);
+  return x;
+}
+__device__ inline float wave_max(float x) {
+  x = fmaxf(x, xor1(x));
+  x = fmaxf(x, xor2(x));
+  x = fmaxf(x, xor4(x));
+  x = fmaxf(x, xor8(x));
+  x = fmaxf(x, xor16(x));
+  x = fmaxf(x, xor32(x));
+  return x;
 }
 
-template <int PH>
-__device__ inline float merge_stats(const float* red, float* scale) {
-  float M = neg_inf(), nan = 0.0f;
-#pragma unroll
-  for (int k = 0; k < PH; ++k) {
-    M = fmaxf(M, red[3 * k]);
-    nan = fmaxf(nan, red[3 * k + 2]);
-  }
-  float W = 0.0f;
-#pragma unroll
-  for (int k = 0; k < PH; ++k) {
-    scale[k] = (M == neg_inf() || red[3 * k] == neg_inf()) ? 0.0f : __expf(red[3 * k] - M);
-    W += scale[k] * red[3 * k + 1];
-  }
-  if (nan != 0.0f) return __builtin_nanf("");
-  if (M == neg_inf()) return neg_inf();
-#pragma unroll
-  for (int k = 0; k < PH; ++k) scale[k] /= W;
-  return M + __logf(W);
-}
-
-// One workgroup per (query token, query head, sequence): (i) merge the
-// compressed-tier partials (rotated space), (ii) inverse-rotate once,
-// (iii) merge the exact-tier partials, (iv) merge the two tiers.  Thread
-// (phase, column) scans splits phase, phase + PH, ... of both tiers; the
-// phases are then combined in a fixed order.
+// One workgroup per (query head, sequence):
+//   (1) every split's lse goes to LDS while the partial outputs are requested;
+//   (2) wave 0 (compressed tier) and wave 1 (exact tier) turn the lse values
+//       into weights w_s = exp(lse_s - M) / W, lse = M + ln W (fixed order);
+//   (3) thread (phase, float4 column) sums w_s o_s over splits phase,
+//       phase + PH, ... with plain FMAs, the phases are added in order;
+//   (4) wave 0 inverse-rotates the compressed-tier output (once per head) and
+//       merges the two tiers.
+// Inactive splits (past a sequence's length) are skipped, never multiplied,
+// so whatever their workspace rows hold cannot leak in.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
-  constexpr int C4 = D / 4, PH = kMergeThreads / C4, E = D / 64;
-  __shared__ float red[2][3 * PH];
-  __shared__ __attribute__((aligned(16))) float phase[2][PH * D];
-  const int row = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int tau = row / p.Hq, h = row - tau * p.Hq;
+  constexpr int C4 = D / 4, PH = kMergeThreads / C4, E = D / 64, K = 8;
+  __shared__ float wsh[AKV_MAX_SPLITS];
+  __shared__ float stats[2][3];  // per tier: lse, nan flag, empty flag
+  __shared__ __attribute__((aligned(16))) float4v phase[2][PH * C4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = p.G, kv = h / G, g = h - kv * G;
-  const int S = p.Sq + p.Se;
-  float* out = p.o + (((size_t)b * p.Tq + tau) * p.Hq + h) * D;
-  float* lout = p.lse + ((size_t)b * p.Tq + tau) * p.Hq + h;
-  const size_t stride = (size_t)p.Tq * G;  // partial rows per split
-  const size_t base = ((size_t)(b * p.Hkv + kv) * S) * stride + (size_t)tau * G + g;
+  const int Sq = p.Sq, S = p.Sq + p.Se;
+  float* out = p.o + ((size_t)b * p.Hq + h) * D;
+  float* lout = p.lse + (size_t)b * p.Hq + h;
+  const size_t base = part_row(p, b, kv, g, 0);
   const int c4 = tid % C4, ph = tid / C4;
-  // the lengths and the partials are requested together: partials of splits
-  // this sequence does not have are loaded too (in bounds) and then ignored
   const int ql = p.qmax ? p.qlen[b] : 0;
   const int el = p.emax ? p.elen[b] : 0;
   const bool bad = ql < 0 || ql > 64 * p.qmax || el < 0 || el > 64 * p.emax;
   const int nq = bad ? 0 : (ql + p.Pq - 1) / p.Pq, ne = bad ? 0 : (el + p.Pe - 1) / p.Pe;
-  MergeAcc aq{neg_inf(), 0.0f, float4v{0, 0, 0, 0}, bad};
-  MergeAcc ae{neg_inf(), 0.0f, float4v{0, 0, 0, 0}, bad};
-  merge_scan<D, PH>(p, base, nq, base + (size_t)p.Sq * stride, ne, stride, ph, c4, aq, ae);
-  merge_publish<D, PH>(aq, ph, c4, red[0], phase[0]);
-  merge_publish<D, PH>(ae, ph, c4, red[1], phase[1]);
+  // (1)
+  for (int s = tid; s < S; s += kMergeThreads) wsh[s] = p.part_lse[base + s];
+  float4v xo[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int s = ph + k * PH;
+    xo[k] = *reinterpret_cast<const float4v*>(p.part_o + (base + (s < S ? s : 0)) * D + 4 * c4);
+  }
+  __syncthreads();
+  // (2)
+  if (w < 2) {
+    const int s0 = w ? Sq : 0, n = w ? ne : nq;
+    float m = neg_inf(), nan = 0.0f;
+    for (int i = lane; i < n; i += 64) {
+      const float l = wsh[s0 + i];
+      if (l != l) nan = 1.0f;
+      else m = fmaxf(m, l);
+    }
+    m = wave_max(m);
+    nan = wave_max(nan);
+    float sum = 0.0f;
+    for (int i = lane; i < n; i += 64) {
+      const float l = wsh[s0 + i];
+      const float e = (m == neg_inf() || l != l) ? 0.0f : __expf(l - m);
+      wsh[s0 + i] = e;
+      sum += e;
+    }
+    sum = wave_sum(sum);
+    const float r = sum > 0.0f ? 1.0f / sum : 0.0f;
+    for (int i = lane; i < n; i += 64) wsh[s0 + i] *= r;
+    if (lane == 0) {
+      stats[w][0] = (m == neg_inf()) ? neg_inf() : m + __logf(sum);
+      stats[w][1] = (bad || nan != 0.0f) ? 1.0f : 0.0f;
+    }
+  }
+  __syncthreads();
+  // (3)
+  float4v aq = float4v{0, 0, 0, 0}, ae = float4v{0, 0, 0, 0};
+  for (int s0 = 0; s0 < S; s0 += K * PH) {
+    if (s0) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int s = s0 + ph + k * PH;
+        xo[k] = *reinterpret_cast<const float4v*>(p.part_o + (base + (s < S ? s : 0)) * D + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int s = s0 + ph + k * PH;
+      if (s < nq) aq += wsh[s] * xo[k];
+      else if (s >= Sq && s - Sq < ne) ae += wsh[s] * xo[k];
+    }
+  }
+  phase[0][ph * C4 + c4] = aq;
+  phase[1][ph * C4 + c4] = ae;
   __syncthreads();
   if (tid >= 64) return;
-  // wave 0: lane l owns dims l + 64 e
-  float sq[PH], se[PH];
-  const float lq = merge_stats<PH>(red[0], sq);
-  const float le = merge_stats<PH>(red[1], se);
+  // (4) wave 0: lane l owns dims l + 64 e
+  const float* fq = reinterpret_cast<const float*>(phase[0]);
+  const float* fe = reinterpret_cast<const float*>(phase[1]);
   float oq[E], oe[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -763,26 +797,31 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
     float vq = 0.0f, ve = 0.0f;
 #pragma unroll
     for (int k = 0; k < PH; ++k) {
-      vq += sq[k] * phase[0][k * D + t];
-      ve += se[k] * phase[1][k * D + t];
+      vq += fq[k * D + t];
+      ve += fe[k * D + t];
     }
     oq[e] = vq;
     oe[e] = ve;
   }
   // inverse rotation of the compressed-tier output: (H o_rot) * RN(1/sqrt d)
 #pragma unroll
-  for (int hh = 1; hh < 64 && hh < D; hh <<= 1)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float o = __shfl_xor(oq[e], hh);
-      oq[e] = (tid & hh) ? (o - oq[e]) : (oq[e] + o);
-    }
+  for (int e = 0; e < E; ++e) {
+    oq[e] = lane_butterfly<1>(oq[e], tid);
+    oq[e] = lane_butterfly<2>(oq[e], tid);
+    oq[e] = lane_butterfly<4>(oq[e], tid);
+    oq[e] = lane_butterfly<8>(oq[e], tid);
+    oq[e] = lane_butterfly<16>(oq[e], tid);
+    oq[e] = lane_butterfly<32>(oq[e], tid);
+  }
   if (E == 2) {
     float a = oq[0], c = oq[E - 1];
     oq[0] = a + c;
     oq[E - 1] = a - c;
   }
   const float rd = inv_sqrt_d(D);
+  const bool nanq = stats[0][1] != 0.0f, nane = stats[1][1] != 0.0f;
+  const float lq = nanq ? __builtin_nanf("") : stats[0][0];
+  const float le = nane ? __builtin_nanf("") : stats[1][0];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     float o, lse;
@@ -836,7 +875,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* op, const f
 
 hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream) {
   dim3 grid(p.Sq + p.Se, p.Hkv, p.B);
-  dim3 mgrid(p.Tq * p.Hq, p.B);
+  dim3 mgrid(p.Hq, p.B);
   if (D == 64) {
     hipLaunchKernelGGL(split_decode_kernel<64>, grid, dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);
@@ -844,16 +883,6 @@ hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream) {
     hipLaunchKernelGGL(split_decode_kernel<128>, grid, dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
   }
-  return hipGetLastError();
-}
-
-// Merge kernel alone, for partials written by another split kernel (chunk).
-hipError_t launch_merge(const AttnParams& p, int D, hipStream_t stream) {
-  dim3 mgrid(p.Tq * p.Hq, p.B);
-  if (D == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
