@@ -158,6 +158,18 @@ def bench_chunk(steps, warmup, stream, min_bytes=2 * MALL_BYTES):
             akv.check(st)
 
     ev_ms, wall_ms = time_calls(call, n_rep, warmup, steps, stream)
+    # the eviction that follows the chunk: the 512 oldest exact tokens per kv
+    # head into the compressed tier (rewrites the same codes on every call)
+    start = int(w.quant_len[0])
+    cds = [dw.compress_desc(0, 0, w.evict, start, replica=r) for r in range(n_rep)]
+
+    def evict(r):
+        st = akv.akv_compress_evicted(cds[r], h)
+        if st:
+            akv.check(st)
+
+    ev_c, wall_c = time_calls(evict, n_rep, warmup, steps, stream)
+    evict_bytes = w.Hkv * w.evict * (2 * 2 * w.d + 2 * (w.d // 2 + 2 * (w.d // 32)))
     flops = chunk_flops(w)
     tflops = flops / (ev_ms * 1e-3) / 1e12
     return {"workload": "chunk512 over 28,672 compressed + 4,096 exact + 512 chunk tokens, "
@@ -165,6 +177,8 @@ def bench_chunk(steps, warmup, stream, min_bytes=2 * MALL_BYTES):
             "us_per_call": ev_ms * 1e3, "wall_us_per_call": wall_ms * 1e3, "steps": steps,
             "query_tokens_per_s": w.B * w.Tq / (ev_ms * 1e-3), "kv_bytes": kv_bytes,
             "kv_gbps": kv_bytes / (ev_ms * 1e-3) / 1e9, "replicas": n_rep,
+            "evict": {"tokens_per_kv_head": w.evict, "us_per_call": ev_c * 1e3, "wall_us_per_call": wall_c * 1e3,
+                      "bytes": evict_bytes, "gbps": evict_bytes / (ev_c * 1e-3) / 1e9},
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS["f16"],
                          "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None,
                          "kernel": "akv_attend_chunk (split + merge kernels, one call)",

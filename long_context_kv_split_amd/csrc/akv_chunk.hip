@@ -5,24 +5,29 @@
 // of the QuantForge walkthrough, section 1).
 //
 // Rows of one kv head are (query, head) pairs r = tau * G + g.  A workgroup
-// (4 waves x 32 rows) takes 128 consecutive rows and one split (a run of
-// whole blocks of one tier).  Each 64-token block is expanded once into LDS
-// and used by all 128 rows:
+// (4 waves x 32 rows; two workgroups per CU) takes
+// 128 consecutive rows and one split (a run of whole blocks of one tier).
+// Each 64-token block is expanded once into LDS and used by all 128 rows:
 //   compressed tier: K[token][dim] = C[code] * scale in fp32, stored as fp16
-//     hi + lo parts, and the transposed V^T[dim][token] = fp16(C[code] *
-//     scale).  The query is rotated by the Walsh-Hadamard butterflies in fp32
-//     and split into fp16 hi + lo parts; a score is Khi.Qhi + Khi.Qlo +
-//     Klo.Qhi (three tiles), about 22 significant bits, so the log-sum-exp
-//     keeps fp32-like accuracy on short or outlier-heavy histories;
+//     hi + lo parts, and the transposed V^T[dim][token] = fp16(C16[code] x
+//     scale) (packed fp16 product).  The query is rotated by the Walsh-
+//     Hadamard butterflies in fp32 and split into fp16 hi + lo parts; a score
+//     is Khi.Qhi + Khi.Qlo + Klo.Qhi (three tiles), about 22 significant
+//     bits, so the log-sum-exp keeps fp32-like accuracy on short or
+//     outlier-heavy histories;
 //   exact tier: bf16 K rows and transposed bf16 V with the bf16 query (exact
 //     products, fp32 sums); the last Tq exact tokens are the chunk itself and
 //     query tau sees chunk tokens <= tau.
 // Per wave:  S^T[token][row] = K_tile x Q^T  and  O^T[dim][row] += V^T x P^T,
-// with an online softmax per row; every wave owns its rows, so a split's
-// partial (normalized output, log-sum-exp) is written straight from
-// registers.  A second kernel merges each row's splits in ascending order:
-// compressed-tier splits in rotated space, one inverse rotation, exact-tier
-// splits, then both tiers.
+// with an online softmax per row.
+// Pipeline: one LDS block buffer per workgroup (two workgroups share a CU)
+// and one register set: a block is expanded from registers into LDS, the
+// next block is requested from HBM into the registers, and the block is
+// computed while those loads are in flight.
+// Every wave owns its rows, so a split's partial (normalized output,
+// log-sum-exp) is written straight from registers.  A second kernel merges
+// each row's splits in ascending order: compressed-tier splits in rotated
+// space, one inverse rotation, exact-tier splits, then both tiers.
 #include "akv_common.h"
 #include "akv_params.h"
 
@@ -31,6 +36,7 @@ namespace akv {
 constexpr int kCWaves = 4;
 constexpr int kCThreads = 64 * kCWaves;
 constexpr int kRT = 2;                       // 16-row tiles per wave
+constexpr int kVT = 512 / kCThreads;         // staging slots (of 512 per block) per thread
 constexpr int kRowsPerWG = 16 * kRT * kCWaves;
 static_assert(kRowsPerWG == AKV_CHUNK_ROWS, "the split planner counts row groups of AKV_CHUNK_ROWS");
 
@@ -64,129 +70,357 @@ __device__ inline float fp32_pinned(float x) {
   return x;
 }
 
-// LDS layout of one staged block.  K rows (64 tokens x D 16-bit values, no
-// padding) hold 16-byte chunk c of token t at chunk position c ^ kswz(t): the
-// 16 tokens an MFMA operand read touches (t = 8u + v + const) and the 16 chunks
-// a staging write touches then fall in distinct banks.  V^T rows (D dims x 64
-// tokens) have a 144-byte pitch, so 16 consecutive dims start in distinct
-// banks.
+// LDS layout: two byte tables, then the block buffer (K hi rows, K lo rows,
+// V^T rows).  K rows (64 tokens x D 16-bit values, no padding) hold 16-byte
+// chunk c of token t at chunk position c ^ h(t) with the 3-bit
+// h(t) = (t & 3) | ((t ^ t >> 3) & 1) << 2: the 8 lanes of a 128-bit access
+// then touch 8 distinct bank groups both for the operand reads (tokens
+// 8u + v + const) and for the staging writes.  V^T rows (D dims x 64 tokens)
+// have a 144-byte pitch, so 8 consecutive dims start in distinct bank groups.
 template <int D>
 struct ChunkLds {
   static constexpr int CPR = D / 8;            // 16-byte chunks per K row
   static constexpr int KP = D * 2;
   static constexpr int VP = 64 * 2 + 16;
   static constexpr int K_BYTES = 64 * KP;
-  static constexpr int V_BYTES = D * VP;
-  static constexpr int KLO = K_BYTES;           // compressed tier: K lo parts
-  static constexpr int V0 = 2 * K_BYTES;
-  static constexpr int LEV = V0 + V_BYTES;      // 16 fp32 levels
-  static constexpr int BYTES = LEV + 64;
+  static constexpr int KLO = K_BYTES;          // compressed tier: K lo parts (buffer-relative)
+  static constexpr int V0 = 2 * K_BYTES;       // V^T rows (buffer-relative)
+  static constexpr int BUF = V0 + D * VP;
+  static constexpr int KLUT = 0;               // 256 x (level lo nibble, level hi nibble) fp32
+  static constexpr int VLUT = 256 * 8;         // 256 x the same in fp16
+  static constexpr int BUF0 = VLUT + 256 * 4;  // the block buffer
+  static constexpr int BYTES = BUF0 + BUF;
 };
 
 template <int D>
 __device__ inline int kchunk_off(int t, int c) {
-  const int h = ((t & 3) << 2) | ((t >> 3) & 3);
-  return t * ChunkLds<D>::KP + 16 * (c ^ (h & (ChunkLds<D>::CPR - 1)));
+  const int h = (t & 3) | (((t ^ (t >> 3)) & 1) << 2);
+  return t * ChunkLds<D>::KP + 16 * (c ^ h);
 }
 
-// ---- expand one compressed block (64 tokens, nvalid of them real) into LDS
+// ---------------------------------------------------------------- staging
+// Register copy of one block's share for this thread.
+// A block's staging work is cut into 512 slots; thread t takes slots
+// t + kCThreads * u (u < kVT).
 template <int D>
-__device__ inline void stage_quant_block(const AttnParams& p, int pb, int kv, int nvalid, unsigned char* smem) {
-  constexpr int M = D / 32, VP = ChunkLds<D>::VP;
-  const int tid = threadIdx.x;
-  const float* lev = reinterpret_cast<const float*>(smem + ChunkLds<D>::LEV);
+struct QRegs {
+  static constexpr int KDW = D / 64;  // K code dwords per slot
+  static constexpr int VDW = D / 64;  // V code dwords per slot
+  uint32_t kc[kVT][KDW];
+  uint32_t ks[kVT][KDW];  // fp16 K scale of each dword's group (low 16 bits)
+  uint32_t vc[kVT][VDW];
+  u32x4 vs[kVT];          // fp16 V scales of the slot's group, tokens tok0 .. tok0 + 7
+};
+template <int D>
+struct ERegs {
+  static constexpr int KCH = 64 * D / 8 / 512;  // 16-byte K chunks per slot
+  u32x4 k[kVT][KCH];
+  u32x4 v0[kVT], v1[kVT];  // tokens 2pp and 2pp + 1 of one 8-dim chunk (slots below 32 * D / 8)
+};
+
+// Slot v's K dwords: token v / 8, dword wi_k = 4 (p & 3) + (p >> 2) + 2k of
+// the row (p = v % 8; D = 128), which holds dims 32 (wi % M) + 8 (wi / M) + 0..7.
+template <int D>
+__device__ inline int qk_dword(int t, int k) {
+  if constexpr (D == 128) {
+    const int p = t & 7;
+    return 4 * (p & 3) + (p >> 2) + 2 * k;
+  } else {
+    return t & 7;
+  }
+}
+
+template <int D>
+__device__ inline void quant_fetch(QRegs<D>& r, const AttnParams& p, int pb, int kv) {
+  constexpr int M = D / 32;
+  const int t = threadIdx.x;
   const size_t slab = (size_t)pb * p.Hkv + kv;
-  const unsigned char* kcs = p.kc + slab * (32 * D);
-  const unsigned char* vcs = p.vc + slab * (32 * D);
+  const uint32_t* kcs = reinterpret_cast<const uint32_t*>(p.kc + slab * (32 * D));
+  const uint32_t* vcs = reinterpret_cast<const uint32_t*>(p.vc + slab * (32 * D));
   const uint16_t* kss = p.ks + slab * (2 * D);
   const uint16_t* vss = p.vs + slab * (2 * D);
-  // K: code dword w of a token row holds dims 32*(w % M) + 8*(w / M) + 0..7
-  constexpr int KQ = D / 32;  // 16-byte code loads per token row
-  for (int ci = tid; ci < 64 * KQ; ci += kCThreads) {
-    const int tok = ci / KQ, ch = ci - tok * KQ;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(kcs + tok * (D / 2) + 16 * ch);
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const int wi = 4 * ch + wd, m = wi % M, a = wi / M;
-      const float s = tok < nvalid ? half_bits(kss[m * 64 + tok]) : 0.0f;
-      half8 hi, lo;
+  for (int u = 0; u < kVT; ++u) {
+    const int v = t + kCThreads * u, tok = v >> 3;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = fp32_pinned(lev[(x[wd] >> (4 * e)) & 15] * s);
-        hi[e] = (_Float16)v;
-        lo[e] = (_Float16)(v - (float)hi[e]);
-      }
-      const int off = kchunk_off<D>(tok, 4 * m + a);
-      *reinterpret_cast<half8*>(smem + off) = hi;
-      *reinterpret_cast<half8*>(smem + ChunkLds<D>::KLO + off) = lo;
+    for (int k = 0; k < QRegs<D>::KDW; ++k) {
+      const int wi = qk_dword<D>(v, k);
+      r.kc[u][k] = kcs[tok * (D / 8) + wi];
+      r.ks[u][k] = kss[(wi % M) * 64 + tok];
     }
-  }
-  // V: code dword (row16 = (4c + a) * 16 + i, t) holds dim 16t + i of tokens
-  // 32c + 8a + 0..7; a thread takes 4 consecutive t, lanes run over i.  The
-  // slab is 8 (c, a) x 16 i rows of D/4 bytes: 2D loads of 16 bytes.
-  constexpr int T4 = D / 64;
-  for (int ci = tid; ci < 8 * 16 * T4; ci += kCThreads) {
-    const int i = ci & 15, t4 = (ci >> 4) % T4, ca = (ci >> 4) / T4;
-    const int row16 = ca * 16 + i, tok0 = 8 * ca;  // 32c + 8a == 8 * (4c + a)
-    const u32x4 w = *reinterpret_cast<const u32x4*>(vcs + row16 * (D / 4) + 16 * t4);
+    // V: slots run over i (dim within 16), then over 4 dword columns, then 8 token groups
+    const int i = v & 15, tq = (v >> 4) & 3, ca = v >> 6;
+    const int row16 = ca * 16 + i;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int dim = 16 * (4 * t4 + k) + i, g = dim >> 5;
-      const u32x4 sc = *reinterpret_cast<const u32x4*>(vss + g * 64 + tok0);
-      half8 out;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = tok0 + e < nvalid ? half_bits(sc[e >> 1] >> (16 * (e & 1))) : 0.0f;
-        out[e] = (_Float16)(lev[(w[k] >> (4 * e)) & 15] * s);
-      }
-      *reinterpret_cast<half8*>(smem + ChunkLds<D>::V0 + dim * VP + tok0 * 2) = out;
-    }
+    for (int k = 0; k < QRegs<D>::VDW; ++k) r.vc[u][k] = vcs[row16 * (D / 16) + tq * QRegs<D>::VDW + k];
+    const int g = (16 * tq * QRegs<D>::VDW + i) >> 5;
+    r.vs[u] = *reinterpret_cast<const u32x4*>(vss + g * 64 + 8 * ca);
   }
 }
 
-// ---- copy one exact block into LDS (K rows, V transposed)
 template <int D>
-__device__ inline void stage_exact_block(const AttnParams& p, int pb, int kv, int nvalid, unsigned char* smem) {
-  constexpr int CPR = ChunkLds<D>::CPR, VP = ChunkLds<D>::VP;
-  const int tid = threadIdx.x;
+__device__ inline void exact_fetch(ERegs<D>& r, const AttnParams& p, int pb, int kv) {
+  constexpr int CPR = ChunkLds<D>::CPR;
+  const int t = threadIdx.x;
   const uint16_t* ks = p.ek + ((size_t)pb * p.Hkv + kv) * kBlock * D;
   const uint16_t* vs = p.ev + ((size_t)pb * p.Hkv + kv) * kBlock * D;
-  for (int ci = tid; ci < 64 * CPR; ci += kCThreads) {
-    const int tok = ci / CPR, ch = ci - tok * CPR;
-    u32x4 kx = *reinterpret_cast<const u32x4*>(ks + tok * D + 8 * ch);
-    if (tok >= nvalid) kx = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(smem + kchunk_off<D>(tok, ch)) = kx;
-  }
-  // V: a thread takes tokens 2pp, 2pp+1 of one 8-dim chunk and writes 8 dwords
-  for (int ci = tid; ci < 32 * CPR; ci += kCThreads) {
-    const int pp = ci & 31, ch = ci >> 5;
-    u32x4 x0 = *reinterpret_cast<const u32x4*>(vs + (2 * pp) * D + 8 * ch);
-    u32x4 x1 = *reinterpret_cast<const u32x4*>(vs + (2 * pp + 1) * D + 8 * ch);
-    if (2 * pp >= nvalid) x0 = u32x4{0, 0, 0, 0};
-    if (2 * pp + 1 >= nvalid) x1 = u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t a = (x0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const uint32_t b = (x1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      *reinterpret_cast<uint32_t*>(smem + ChunkLds<D>::V0 + (8 * ch + e) * VP + 4 * pp) = a | (b << 16);
+  for (int u = 0; u < kVT; ++u) {
+    const int v = t + kCThreads * u;
+#pragma unroll
+    for (int k = 0; k < ERegs<D>::KCH; ++k) {
+      const int ci = v + 512 * k, tok = ci / CPR, ch = ci - tok * CPR;
+      r.k[u][k] = *reinterpret_cast<const u32x4*>(ks + tok * D + 8 * ch);
+    }
+    if (v < 32 * CPR) {
+      const int pp = v & 31, ch = v >> 5;
+      r.v0[u] = *reinterpret_cast<const u32x4*>(vs + (2 * pp) * D + 8 * ch);
+      r.v1[u] = *reinterpret_cast<const u32x4*>(vs + (2 * pp + 1) * D + 8 * ch);
     }
   }
 }
 
-// ---- one split of 128 rows
+// Compressed K -> LDS (fp16 hi + lo of the fp32 product level x scale).
+template <int D>
+__device__ inline void quant_stage_k(const QRegs<D>& r, unsigned char* smem, unsigned char* buf, int nvalid) {
+  constexpr int M = D / 32;
+  const float2* klut = reinterpret_cast<const float2*>(smem + ChunkLds<D>::KLUT);
+#pragma unroll
+  for (int u = 0; u < kVT; ++u)
+#pragma unroll
+  for (int k = 0; k < QRegs<D>::KDW; ++k) {
+    const int v = threadIdx.x + kCThreads * u, tok = v >> 3;
+    const int wi = qk_dword<D>(v, k), m = wi % M, a = wi / M;
+    const float s = tok < nvalid ? half_bits(r.ks[u][k] & 0xFFFFu) : 0.0f;
+    half8 hi, lo;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float2 lv = klut[(r.kc[u][k] >> (8 * b)) & 0xFFu];
+      const float v0 = fp32_pinned(lv.x * s), v1 = fp32_pinned(lv.y * s);
+      hi[2 * b] = (_Float16)v0;
+      hi[2 * b + 1] = (_Float16)v1;
+      lo[2 * b] = (_Float16)(v0 - (float)hi[2 * b]);
+      lo[2 * b + 1] = (_Float16)(v1 - (float)hi[2 * b + 1]);
+    }
+    const int off = kchunk_off<D>(tok, 4 * m + a);
+    *reinterpret_cast<half8*>(buf + off) = hi;
+    *reinterpret_cast<half8*>(buf + ChunkLds<D>::KLO + off) = lo;
+  }
+}
+
+// Compressed V -> LDS as V^T (fp16 level pair x fp16 scale pair).
+template <int D>
+__device__ inline void quant_stage_v(const QRegs<D>& r, unsigned char* smem, unsigned char* buf, int nvalid) {
+  constexpr int VP = ChunkLds<D>::VP;
+  const uint32_t* vlut = reinterpret_cast<const uint32_t*>(smem + ChunkLds<D>::VLUT);
+#pragma unroll
+  for (int u = 0; u < kVT; ++u) {
+    const int v = threadIdx.x + kCThreads * u, i = v & 15, tq = (v >> 4) & 3, ca = v >> 6, tok0 = 8 * ca;
+    u32x4 sc = r.vs[u];
+    if (tok0 + 8 > nvalid) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (tok0 + 2 * b >= nvalid) sc[b] = 0u;
+        else if (tok0 + 2 * b + 1 >= nvalid) sc[b] &= 0xFFFFu;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < QRegs<D>::VDW; ++k) {
+      const int dim = 16 * (tq * QRegs<D>::VDW + k) + i;
+      u32x4 out;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const half2v lv = __builtin_bit_cast(half2v, vlut[(r.vc[u][k] >> (8 * b)) & 0xFFu]);
+        // copy the element out first: a bit cast applied to a vector element
+        // expression reads element 0 whatever the index
+        const uint32_t sb = sc[b];
+        out[b] = __builtin_bit_cast(uint32_t, lv * __builtin_bit_cast(half2v, sb));
+      }
+      *reinterpret_cast<u32x4*>(buf + ChunkLds<D>::V0 + dim * VP + tok0 * 2) = out;
+    }
+  }
+}
+
+template <int D>
+__device__ inline void exact_stage_k(const ERegs<D>& r, unsigned char* buf, int nvalid) {
+  constexpr int CPR = ChunkLds<D>::CPR;
+#pragma unroll
+  for (int u = 0; u < kVT; ++u)
+#pragma unroll
+  for (int k = 0; k < ERegs<D>::KCH; ++k) {
+    const int ci = threadIdx.x + kCThreads * u + 512 * k, tok = ci / CPR, ch = ci - tok * CPR;
+    const u32x4 x = tok < nvalid ? r.k[u][k] : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(buf + kchunk_off<D>(tok, ch)) = x;
+  }
+}
+
+template <int D>
+__device__ inline void exact_stage_v(const ERegs<D>& r, unsigned char* buf, int nvalid) {
+  constexpr int CPR = ChunkLds<D>::CPR, VP = ChunkLds<D>::VP;
+#pragma unroll
+  for (int u = 0; u < kVT; ++u) {
+    const int v = threadIdx.x + kCThreads * u;
+    if (v < 32 * CPR) {
+      const int pp = v & 31, ch = v >> 5;
+      const u32x4 x0 = 2 * pp < nvalid ? r.v0[u] : u32x4{0, 0, 0, 0};
+      const u32x4 x1 = 2 * pp + 1 < nvalid ? r.v1[u] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = (x0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t b = (x1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        *reinterpret_cast<uint32_t*>(buf + ChunkLds<D>::V0 + (8 * ch + e) * VP + 4 * pp) = a | (b << 16);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- compute
+template <int D>
+struct RowState {
+  float m[kRT], l[kRT];
+  float4v O[D / 16][kRT];
+};
+
+// One 32-token half (c) of a staged block for this wave's 32 rows.
+// mask: apply the split end and the causal limits (last block / chunk blocks).
+template <int D, bool QUANT>
+__device__ inline void compute_half(const unsigned char* buf, int c, bool mask, int tb, int end, const int (&climit)[kRT],
+                                    const half8 (&Qh)[kRT][D / 32], const half8 (&Ql)[kRT][D / 32],
+                                    const bf16x8 (&Qe)[kRT][D / 32], float qs, RowState<D>& rs) {
+  constexpr int M = D / 32, NT = D / 16, VP = ChunkLds<D>::VP;
+  const int lane = threadIdx.x & 63, j = lane & 15, qq = lane >> 4;
+  // scores: row i of tile tp is token 32c + 8(i/4) + 4tp + i%4, so lane
+  // (j, qq) ends up with tokens 32c + 8qq + 0..7 of row j
+  float s[kRT][8];
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    const int krow = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
+    half8 kh[M], kl[M];
+    bf16x8 kb[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int off = kchunk_off<D>(krow, 4 * m + qq);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(buf + off);
+      if (QUANT) {
+        kh[m] = __builtin_bit_cast(half8, raw);
+        kl[m] = *reinterpret_cast<const half8*>(buf + ChunkLds<D>::KLO + off);
+      } else {
+        kb[m] = __builtin_bit_cast(bf16x8, raw);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      float4v acc = float4v{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        if (QUANT) {
+          acc = cmfma16(kh[m], Qh[rt][m], acc);
+          acc = cmfma16(kh[m], Ql[rt][m], acc);
+          acc = cmfma16(kl[m], Qh[rt][m], acc);
+        } else {
+          acc = cmfma16bf(kb[m], Qe[rt][m], acc);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[rt][4 * tp + r] = QUANT ? acc[r] : acc[r] * qs;
+    }
+  }
+  if (mask) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = tb + 32 * c + 8 * qq + e;
+        if (tok >= end || tok > climit[rt]) s[rt][e] = neg_inf();
+      }
+  }
+  // online softmax (base 2); lanes j, j+16, j+32, j+48 share a row
+  half8 ph[kRT];
+  bf16x8 pbf[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    float mx = s[rt][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[rt][e]);
+    mx = fmaxf(mx, cxor16(mx));
+    mx = fmaxf(mx, cxor32(mx));
+    const float mnew = fmaxf(rs.m[rt], mx);
+    const float muse = (mnew == neg_inf()) ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(rs.m[rt] - muse);
+    float sum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(s[rt][e] - muse);
+      sum += pe;
+      if (QUANT)
+        ph[rt][e] = (_Float16)pe;
+      else
+        pbf[rt][e] = (__bf16)pe;
+    }
+    rs.l[rt] = rs.l[rt] * alpha + sum;
+    rs.m[rt] = mnew;
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) rs.O[t][rt] *= alpha;
+    }
+  }
+  // values: lane (j, qq) supplies V^T[16t + j][32c + 8qq + 0..7]
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const u32x4 va = *reinterpret_cast<const u32x4*>(buf + ChunkLds<D>::V0 + (16 * t + j) * VP + (32 * c + 8 * qq) * 2);
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      if (QUANT)
+        rs.O[t][rt] = cmfma16(__builtin_bit_cast(half8, va), ph[rt], rs.O[t][rt]);
+      else
+        rs.O[t][rt] = cmfma16bf(__builtin_bit_cast(bf16x8, va), pbf[rt], rs.O[t][rt]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- one split
 template <int D, bool QUANT>
 __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int kv, int rg, int sx, int start,
                             int end, int el) {
-  constexpr int M = D / 32, NT = D / 16, VP = ChunkLds<D>::VP;
+  constexpr int M = D / 32, NT = D / 16;
+  using Regs = typename std::conditional<QUANT, QRegs<D>, ERegs<D>>::type;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, qq = lane >> 4;
   const int G = p.G, R = p.Tq * G;
-  if (QUANT && tid < 16)
-    reinterpret_cast<float*>(smem + ChunkLds<D>::LEV)[tid] = __builtin_bit_cast(float, kLevelBits[tid]);
+
+  // ---- blocks of this split (the exact tier stops at the last block any row sees)
+  int nb = ((end + 63) >> 6) - (start >> 6);
+  if (!QUANT) {
+    const int wg_limit = el - p.Tq + (min(rg * kRowsPerWG + kRowsPerWG, R) - 1) / G;
+    nb = min(nb, wg_limit < start ? 0 : ((wg_limit - start) >> 6) + 1);
+  }
+  const int* table = QUANT ? p.qtab + (size_t)b * p.qmax : p.etab + (size_t)b * p.emax;
+  const int nbpool = QUANT ? p.qnb : p.enb;
+  bool poison = false;
+  auto block_id = [&](int n) {
+    const int pb = table[(start >> 6) + n];
+    const bool ok = pb >= 0 && pb < nbpool;
+    poison |= !ok;
+    return ok ? pb : 0;
+  };
+  auto fetch = [&](Regs& r, int n) {
+    if constexpr (QUANT)
+      quant_fetch<D>(r, p, block_id(n), kv);
+    else
+      exact_fetch<D>(r, p, block_id(n), kv);
+  };
+
+  // ---- byte tables (compressed tier)
+  for (int e = tid; QUANT && e < 256; e += kCThreads) {
+    const float c0 = __builtin_bit_cast(float, kLevelBits[e & 15]);
+    const float c1 = __builtin_bit_cast(float, kLevelBits[e >> 4]);
+    reinterpret_cast<float2*>(smem + ChunkLds<D>::KLUT)[e] = float2{c0, c1};
+    reinterpret_cast<half2v*>(smem + ChunkLds<D>::VLUT)[e] = half2v{(_Float16)c0, (_Float16)c1};
+  }
 
   // ---- query operands: lane (row j of tile rt, qq) holds dims 32m + 8qq + e
   const int row0 = rg * kRowsPerWG + w * 16 * kRT;
-  int rowv[kRT];
+  int rowv[kRT], climit[kRT];
   half8 Qh[kRT][M], Ql[kRT][M];
   bf16x8 Qe[kRT][M];
 #pragma unroll
@@ -195,6 +429,7 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
     rowv[rt] = r;
     const int rr = r < R ? r : R - 1;
     const int tau = rr / G, g = rr - tau * G;
+    climit[rt] = QUANT ? 0x7FFFFFFF : el - p.Tq + tau;  // exact token p is visible iff p <= el - Tq + tau
     const uint16_t* qsrc = p.q + (((size_t)b * p.Tq + tau) * p.Hq + kv * G + g) * D + 8 * qq;
     u32x4 raw[M];
 #pragma unroll
@@ -256,128 +491,36 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
     }
   }
 
-  float mrun[kRT], lrun[kRT];
-  float4v O[NT][kRT];
-  int climit[kRT];  // exact token p is visible to a row iff p <= el - Tq + tau
+  RowState<D> rs;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    mrun[rt] = neg_inf();
-    lrun[rt] = 0.0f;
+    rs.m[rt] = neg_inf();
+    rs.l[rt] = 0.0f;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) O[t][rt] = float4v{0, 0, 0, 0};
-    climit[rt] = el - p.Tq + (rowv[rt] < R ? rowv[rt] : R - 1) / G;
+    for (int t = 0; t < NT; ++t) rs.O[t][rt] = float4v{0, 0, 0, 0};
   }
-  const int wg_limit = el - p.Tq + (min(rg * kRowsPerWG + kRowsPerWG, R) - 1) / G;
-  bool poison = false;
 
-  const int* table = QUANT ? p.qtab + (size_t)b * p.qmax : p.etab + (size_t)b * p.emax;
-  const int nbpool = QUANT ? p.qnb : p.enb;
-  for (int tb = start; tb < end; tb += 64) {
-    if (!QUANT && tb > wg_limit) break;  // the rest is in every row's future
-    const int pb = table[tb >> 6];
-    const int nvalid = min(64, end - tb);
-    __syncthreads();  // every wave is done with the previous block
-    if (pb < 0 || pb >= nbpool) {
-      poison = true;
-      continue;
+  unsigned char* buf = smem + ChunkLds<D>::BUF0;
+  auto nvalid_of = [&](int n) { return min(64, end - (start + 64 * n)); };
+  const int causal_from = el - p.Tq;  // blocks reaching past this token need the causal mask
+  Regs regs;
+  if (nb > 0) fetch(regs, 0);
+  __syncthreads();  // byte tables visible
+  for (int n = 0; n < nb; ++n) {
+    if (n) __syncthreads();  // every wave is done with the previous block
+    if constexpr (QUANT) {
+      quant_stage_k<D>(regs, smem, buf, nvalid_of(n));
+      quant_stage_v<D>(regs, smem, buf, nvalid_of(n));
+    } else {
+      exact_stage_k<D>(regs, buf, nvalid_of(n));
+      exact_stage_v<D>(regs, buf, nvalid_of(n));
     }
-    if (QUANT)
-      stage_quant_block<D>(p, pb, kv, nvalid, smem);
-    else
-      stage_exact_block<D>(p, pb, kv, nvalid, smem);
     __syncthreads();
-    const bool causal_block = !QUANT && tb + 63 > el - p.Tq;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (tb + 32 * c >= end) break;
-      // scores: row i of tile tp is token 32c + 8(i/4) + 4tp + i%4, so lane
-      // (j, qq) ends up with tokens 32c + 8qq + 0..7 of row j
-      float s[kRT][8];
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        const int krow = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
-        half8 kh[M], kl[M];
-        bf16x8 kb[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const int off = kchunk_off<D>(krow, 4 * m + qq);
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(smem + off);
-          if (QUANT) {
-            kh[m] = __builtin_bit_cast(half8, raw);
-            kl[m] = *reinterpret_cast<const half8*>(smem + ChunkLds<D>::KLO + off);
-          } else {
-            kb[m] = __builtin_bit_cast(bf16x8, raw);
-          }
-        }
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          float4v acc = float4v{0, 0, 0, 0};
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            if (QUANT) {
-              acc = cmfma16(kh[m], Qh[rt][m], acc);
-              acc = cmfma16(kh[m], Ql[rt][m], acc);
-              acc = cmfma16(kl[m], Qh[rt][m], acc);
-            } else {
-              acc = cmfma16bf(kb[m], Qe[rt][m], acc);
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s[rt][4 * tp + r] = QUANT ? acc[r] : acc[r] * p.qscale2;
-        }
-      }
-      // masks: tokens past the split end, and each row's causal future
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tok = tb + 32 * c + 8 * qq + e;
-          if (tok >= end || (causal_block && tok > climit[rt])) s[rt][e] = neg_inf();
-        }
-      // online softmax (base 2); lanes j, j+16, j+32, j+48 share a row
-      half8 ph[kRT];
-      bf16x8 pbf[kRT];
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        float mx = s[rt][0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[rt][e]);
-        mx = fmaxf(mx, cxor16(mx));
-        mx = fmaxf(mx, cxor32(mx));
-        const float mnew = fmaxf(mrun[rt], mx);
-        const float muse = (mnew == neg_inf()) ? 0.0f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(mrun[rt] - muse);
-        float sum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(s[rt][e] - muse);
-          sum += pe;
-          if (QUANT)
-            ph[rt][e] = (_Float16)pe;
-          else
-            pbf[rt][e] = (__bf16)pe;
-        }
-        lrun[rt] = lrun[rt] * alpha + sum;
-        mrun[rt] = mnew;
-        if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) O[t][rt] *= alpha;
-        }
-      }
-      // values: lane (j, qq) supplies V^T[16t + j][32c + 8qq + 0..7]
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 va =
-            *reinterpret_cast<const u32x4*>(smem + ChunkLds<D>::V0 + (16 * t + j) * VP + (32 * c + 8 * qq) * 2);
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          if (QUANT)
-            O[t][rt] = cmfma16(__builtin_bit_cast(half8, va), ph[rt], O[t][rt]);
-          else
-            O[t][rt] = cmfma16bf(__builtin_bit_cast(bf16x8, va), pbf[rt], O[t][rt]);
-        }
-      }
-    }
+    if (n + 1 < nb) fetch(regs, n + 1);  // in flight while this block is computed
+    const int tb = start + 64 * n;
+    const bool mask = (tb + 64 > end) || (!QUANT && tb + 63 > causal_from);
+    compute_half<D, QUANT>(buf, 0, mask, tb, end, climit, Qh, Ql, Qe, p.qscale2, rs);
+    if (tb + 32 < end) compute_half<D, QUANT>(buf, 1, mask, tb, end, climit, Qh, Ql, Qe, p.qscale2, rs);
   }
 
   // ---- partial rows straight from registers: lane holds O^T[16t + 4qq + r][row j]
@@ -385,22 +528,22 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     const int r = rowv[rt];
-    float l = lrun[rt];
+    float l = rs.l[rt];
     l += cxor16(l);
     l += cxor32(l);
     if (r >= R) continue;
     const size_t prow = ((size_t)(b * p.Hkv + kv) * S + sx) * R + r;
     float* dst = p.part_o + prow * D;
-    const bool empty = mrun[rt] == neg_inf();
+    const bool empty = rs.m[rt] == neg_inf();
     const float inv = empty ? 0.0f : 1.0f / l;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      float4v v = O[t][rt] * inv;
+      float4v v = rs.O[t][rt] * inv;
       if (poison) v = float4v{1, 1, 1, 1} * __builtin_nanf("");
       *reinterpret_cast<float4v*>(dst + 16 * t + 4 * qq) = v;
     }
     if (qq == 0)
-      p.part_lse[prow] = poison ? __builtin_nanf("") : (empty ? neg_inf() : (mrun[rt] + __builtin_log2f(l)) * kLn2);
+      p.part_lse[prow] = poison ? __builtin_nanf("") : (empty ? neg_inf() : (rs.m[rt] + __builtin_log2f(l)) * kLn2);
   }
 }
 

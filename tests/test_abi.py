@@ -81,7 +81,7 @@ def test_chunk_split_planner_c5_shape():
     assert akv.akv_decode_workspace_bytes(good_desc(exact=e, quant=q)) == (4 * (5 + 29) * 8) * 516
     # a small chunk still gets whole-block splits, never above the maximum
     d3 = good_desc(Tq=1, Hq=4, Hkv=1, exact=e, quant=q)
-    rows = 1 * 1 * (72 + 456) * 1 * 4      # 512 units wanted -> one block per split
+    rows = 1 * 1 * (72 + 456) * 1 * 4      # 512 runs wanted -> one block per split
     assert akv.akv_chunk_workspace_bytes(d3) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
 
 
