@@ -71,17 +71,17 @@ __device__ inline float fp32_pinned(float x) {
 }
 
 // LDS layout: two byte tables, then the block buffer (K hi rows, K lo rows,
-// V^T rows).  K rows (64 tokens x D 16-bit values, no padding) hold 16-byte
-// chunk c of token t at chunk position c ^ h(t) with the 3-bit
-// h(t) = (t & 3) | ((t ^ t >> 3) & 1) << 2: the 8 lanes of a 128-bit access
-// then touch 8 distinct bank groups both for the operand reads (tokens
-// 8u + v + const) and for the staging writes.  V^T rows (D dims x 64 tokens)
-// have a 144-byte pitch, so 8 consecutive dims start in distinct bank groups.
+// V^T rows), rows unpadded.  A 128-bit LDS access on gfx950 serves 16 lanes
+// per cycle over 64 banks, in lane groups that are not simply 16 consecutive
+// lanes, so the chunk permutations below were chosen by measuring the bank-
+// conflict counter for the operand reads and the staging writes (all zero):
+//   K row t:     16-byte chunk c at position c ^ ((t & 3) | ((t >> 3) & 3) << 2);
+//   V^T row dim: 16-byte chunk c (8 tokens) at position c ^ (dim & 7).
 template <int D>
 struct ChunkLds {
   static constexpr int CPR = D / 8;            // 16-byte chunks per K row
   static constexpr int KP = D * 2;
-  static constexpr int VP = 64 * 2 + 16;
+  static constexpr int VP = 64 * 2;
   static constexpr int K_BYTES = 64 * KP;
   static constexpr int KLO = K_BYTES;          // compressed tier: K lo parts (buffer-relative)
   static constexpr int V0 = 2 * K_BYTES;       // V^T rows (buffer-relative)
@@ -94,8 +94,13 @@ struct ChunkLds {
 
 template <int D>
 __device__ inline int kchunk_off(int t, int c) {
-  const int h = (t & 3) | (((t ^ (t >> 3)) & 1) << 2);
+  const int h = ((t & 3) | (((t >> 3) & 3) << 2)) & (ChunkLds<D>::CPR - 1);
   return t * ChunkLds<D>::KP + 16 * (c ^ h);
+}
+// byte offset of tokens 8c .. 8c + 7 of V^T row dim
+template <int D>
+__device__ inline int vchunk_off(int dim, int c) {
+  return ChunkLds<D>::V0 + dim * ChunkLds<D>::VP + 16 * (c ^ (dim & 7));
 }
 
 // ---------------------------------------------------------------- staging
@@ -236,7 +241,7 @@ __device__ inline void quant_stage_v(const QRegs<D>& r, unsigned char* smem, uns
         const uint32_t sb = sc[b];
         out[b] = __builtin_bit_cast(uint32_t, lv * __builtin_bit_cast(half2v, sb));
       }
-      *reinterpret_cast<u32x4*>(buf + ChunkLds<D>::V0 + dim * VP + tok0 * 2) = out;
+      *reinterpret_cast<u32x4*>(buf + vchunk_off<D>(dim, ca)) = out;
     }
   }
 }
@@ -268,7 +273,7 @@ __device__ inline void exact_stage_v(const ERegs<D>& r, unsigned char* buf, int 
       for (int e = 0; e < 8; ++e) {
         const uint32_t a = (x0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
         const uint32_t b = (x1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(buf + ChunkLds<D>::V0 + (8 * ch + e) * VP + 4 * pp) = a | (b << 16);
+        *reinterpret_cast<uint32_t*>(buf + vchunk_off<D>(8 * ch + e, pp >> 2) + 4 * (pp & 3)) = a | (b << 16);
       }
     }
   }
@@ -367,7 +372,7 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
   // values: lane (j, qq) supplies V^T[16t + j][32c + 8qq + 0..7]
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const u32x4 va = *reinterpret_cast<const u32x4*>(buf + ChunkLds<D>::V0 + (16 * t + j) * VP + (32 * c + 8 * qq) * 2);
+    const u32x4 va = *reinterpret_cast<const u32x4*>(buf + vchunk_off<D>(16 * t + j, 4 * c + qq));
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       if (QUANT)
