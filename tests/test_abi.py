@@ -200,3 +200,11 @@ def test_frozen_device_constants_match_oracle():
     assert np.array_equal(table("kLevelBits"), O.centroids_f32().view(np.uint32))
     assert np.array_equal(table("kThreshBits"), O.thresholds_f32().view(np.uint32))
     assert "0x3DB504F3u" in src and O.inv_sqrt_f32(128).view(np.uint32) == 0x3DB504F3
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    """No fallback: with the library missing the binding raises instead of computing anything."""
+    monkeypatch.setattr(akv, "LIB_PATH", str(tmp_path / "libakv.so"))
+    import pytest as _pytest
+    with _pytest.raises(ImportError):
+        akv._load()
