@@ -119,6 +119,7 @@ def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None, 
     n_rep = max(1, -(-min_bytes // kv_bytes))
     dw.add_replicas(n_rep)
     descs = [dw.desc(r, split_exact=split_exact, split_quant=split_quant) for r in range(n_rep)]
+    dw.plan = akv.akv_split_plan(descs[0])  # the split sizes the library picks for this shape
     dw.ensure_ws(descs[0])
     h = stream.cuda_stream
     ws, wsb = harness.ptr(dw.ws), dw.ws_bytes
@@ -261,8 +262,7 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16, 1% x8 outlier channels)",
         "config": {"workload": "hybrid128k", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "history_tokens": hist, "compressed_tokens": int(w.quant_len[0]),
-                   "exact_tokens": int(w.exact_len[0]), "split_tokens_quant": args.split_quant or 1024,
-                   "split_tokens_exact": args.split_exact or 1024,
+                   "exact_tokens": int(w.exact_len[0]), **dw.plan,
                    "input_replicas": n_rep, "replica_bytes": kv_bytes * n_rep},
         "kv_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,

@@ -45,8 +45,14 @@
  * Hkv = key/value heads, d = head dimension (64 or 128), G = Hq/Hkv <= 8;
  * query head h reads key/value head h / G.  A block holds 64 tokens.
  *
- * Exact tier pools K, V: bf16, element (block p, kv head k, token r, dim t) at
- *   ((p*Hkv + k)*64 + r)*d + t.
+ * Exact tier pools: bf16, element (block p, kv head k, token r, dim t) at
+ *   K: ((p*Hkv + k)*64 + r)*d + t                   (token-major)
+ *   V: (((p*Hkv + k)*2 + r/32)*d + t)*32 + r%32     (dim-major inside each
+ *                                                    32-token half block)
+ * so that a lane's matrix-core operand (8 dims of one token for K, 8 tokens
+ * of one dim for V) is one contiguous 16-byte load, and the 64 lanes of one
+ * load instruction read 1 KB of consecutive bytes.  Appending a token writes
+ * one row of K and one bf16 per dim of V.
  *
  * Compressed tier: one slab of 32*d code bytes and one slab of 2*d fp16
  * scales per (block p, kv head k), at byte offset (p*Hkv + k)*32*d and element
@@ -81,12 +87,24 @@ extern "C" {
 #define AKV_ABI_VERSION 1
 #define AKV_BLOCK_TOKENS 64
 #define AKV_GROUP 32
-/* Fixed split rule (a length-only rule, so repeated calls partition the
- * history identically): a tier of n tokens is cut into ceil(n / P) splits of
- * P tokens, the last one shorter.  P defaults below; a descriptor may pass
- * another multiple of 64. */
+/* Fixed split rule (the lengths never enter it, so repeated calls on one
+ * shape partition the history identically): a tier of n tokens is cut into
+ * ceil(n / P) splits of P tokens, the last one shorter.  A descriptor may pass
+ * P (a multiple of 64) per tier; 0 picks the default from the shape alone.
+ * akv_attend_decode's default aims at one round of workgroups: with
+ * budget = AKV_DECODE_TARGET_WORKGROUPS / (B * Hkv) splits per kv head and
+ * tier capacities Nq = 64 * quant.max_blocks, Ne = 64 * exact.max_blocks
+ * tokens, the compressed tier takes the smallest Pq in 256, 512, 768 with
+ * ceil(Nq / Pq) + ceil(Ne / AKV_SPLIT_TOKENS_EXACT_DEFAULT) <= budget (else
+ * AKV_SPLIT_TOKENS_QUANT_DEFAULT); with rem = budget - ceil(Nq / Pq) >= 1 the
+ * exact tier takes Pe = 64 * ceil(exact.max_blocks / rem) clamped to
+ * [AKV_MIN_SPLIT_TOKENS, AKV_SPLIT_TOKENS_EXACT_DEFAULT], else the default.
+ * E.g. 1 sequence, 4 kv heads, 123,904 + 4,096 tokens: Pq = 1024 (121
+ * splits), Pe = 640 (7 splits), 512 workgroups. */
 #define AKV_SPLIT_TOKENS_EXACT_DEFAULT 1024
 #define AKV_SPLIT_TOKENS_QUANT_DEFAULT 1024
+#define AKV_MIN_SPLIT_TOKENS 256
+#define AKV_DECODE_TARGET_WORKGROUPS 512   /* two per compute unit on 256 CUs */
 /* akv_attend_chunk's default instead: with Tq*G rows per kv head taken in
  * row groups of AKV_CHUNK_ROWS, a tier of max_blocks blocks is cut into
  * want = ceil(AKV_CHUNK_TARGET_WORKGROUPS / (B * Hkv * row groups)) runs of
@@ -110,8 +128,8 @@ typedef enum akv_status {
 /* Exact (bf16) tier of a batch.  Absent when max_blocks == 0 (then the
  * pointers may be NULL and every sequence has 0 exact tokens). */
 typedef struct akv_exact_tier {
-  const uint16_t* k;           /* bf16 pool, layout above */
-  const uint16_t* v;           /* bf16 pool */
+  const uint16_t* k;           /* bf16 pool, token-major (layout above) */
+  const uint16_t* v;           /* bf16 pool, dim-major inside each half block */
   const int32_t* block_table;  /* [B][max_blocks] */
   const int32_t* lengths;      /* [B], 0 <= len <= 64*max_blocks */
   int32_t max_blocks;          /* row stride of block_table */
@@ -142,8 +160,8 @@ typedef struct akv_attn_desc {
   const uint16_t* q;           /* bf16 [B][Tq][Hq][d], 4-byte aligned */
   akv_exact_tier exact;
   akv_quant_tier quant;
-  int32_t split_tokens_exact;  /* 0 => default (decode: AKV_SPLIT_TOKENS_EXACT_DEFAULT) */
-  int32_t split_tokens_quant;  /* 0 => default (decode: AKV_SPLIT_TOKENS_QUANT_DEFAULT) */
+  int32_t split_tokens_exact;  /* 0 => the shape-only default above */
+  int32_t split_tokens_quant;  /* 0 => the shape-only default above */
   float* o;                    /* fp32 [B][Tq][Hq][d] normalized output */
   float* lse;                  /* fp32 [B][Tq][Hq] natural-log sum of exp(scores) */
 } akv_attn_desc;
@@ -166,7 +184,7 @@ typedef akv_attn_desc akv_chunk_desc;
 typedef struct akv_compress_desc {
   uint32_t struct_size;        /* sizeof(akv_compress_desc) */
   int32_t Hkv, d;
-  const uint16_t* src_k;       /* bf16 exact-tier pools */
+  const uint16_t* src_k;       /* bf16 exact-tier pools (layouts above) */
   const uint16_t* src_v;
   const int32_t* src_block_table;  /* [src_max_blocks] one sequence's row */
   int32_t src_max_blocks, src_num_blocks;
@@ -190,6 +208,13 @@ const char* akv_last_error(void);
  * (per-split partial outputs and statistics).  Returns 0 if desc is invalid. */
 size_t akv_decode_workspace_bytes(const akv_attn_desc* desc);
 size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc);
+
+/* The split plan a call with `desc` would use (chunk != 0: akv_attend_chunk,
+ * else akv_attend_decode): out[0..3] = compressed-tier split tokens, exact-
+ * tier split tokens, compressed-tier splits, exact-tier splits per sequence
+ * and kv head.  Validates desc like the call itself and returns its status;
+ * out (host memory, 4 int32) is written only on AKV_OK. */
+akv_status akv_split_plan(const akv_attn_desc* desc, int32_t chunk, int32_t* out);
 
 /* Split-KV decode attention, one query token per sequence.
  * Enqueues two kernels: a split kernel in which every (split, kv head,

@@ -32,6 +32,8 @@ GROUP = 32
 SPLIT_TOKENS_EXACT_DEFAULT = 1024
 SPLIT_TOKENS_QUANT_DEFAULT = 1024
 MAX_SPLIT_TOKENS = 32768
+MIN_SPLIT_TOKENS = 256
+DECODE_TARGET_WORKGROUPS = 512
 MAX_SPLITS = 2048
 MAX_CHUNK = 512
 
@@ -101,6 +103,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P(AttnDesc), c_void_p, c_size_t, c_void_p]
+    lib.akv_split_plan.restype = ctypes.c_int
+    lib.akv_split_plan.argtypes = [P(AttnDesc), c_int32, P(c_int32)]
     lib.akv_lse_merge.restype = ctypes.c_int
     lib.akv_lse_merge.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.akv_compress_evicted.restype = ctypes.c_int
@@ -131,6 +135,14 @@ def akv_decode_workspace_bytes(desc: AttnDesc) -> int:
 
 def akv_chunk_workspace_bytes(desc: AttnDesc) -> int:
     return LIB.akv_chunk_workspace_bytes(ctypes.byref(desc))
+
+
+def akv_split_plan(desc: AttnDesc, chunk: bool = False) -> dict:
+    """Split sizes and counts the library picks for desc (raises AKVError if desc is invalid)."""
+    out = (c_int32 * 4)()
+    check(LIB.akv_split_plan(ctypes.byref(desc), int(bool(chunk)), out))
+    return {"split_tokens_quant": out[0], "split_tokens_exact": out[1], "splits_quant": out[2],
+            "splits_exact": out[3]}
 
 
 def akv_attend_decode(desc: AttnDesc, ws: int, ws_bytes: int, stream: int = 0) -> int:

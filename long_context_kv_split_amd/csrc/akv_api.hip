@@ -81,9 +81,34 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan) {
   if (chunk && d->Tq > AKV_MAX_CHUNK) return fail(AKV_ERR_UNSUPPORTED, "chunk Tq %d > %d", d->Tq, AKV_MAX_CHUNK);
   if (chunk && e.max_blocks == 0) return fail(AKV_ERR_UNSUPPORTED, "chunk needs the exact tier (it holds the chunk)");
   if (d->B > 65535 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
-  int Pe = split_tokens(d->split_tokens_exact, AKV_SPLIT_TOKENS_EXACT_DEFAULT);
-  int Pq = split_tokens(d->split_tokens_quant, AKV_SPLIT_TOKENS_QUANT_DEFAULT);
-  if (chunk) {
+  int Pe, Pq;
+  if (!chunk) {
+    // about AKV_DECODE_TARGET_WORKGROUPS / (B * Hkv) splits per kv head (one
+    // round of workgroups): the compressed tier in the smallest multiple of
+    // 256 tokens that leaves room for the exact tier at the default size, the
+    // exact tier in equal runs of whole blocks over the slots left (a
+    // shape-only rule, like the chunk one below)
+    const long long units = (long long)d->B * d->Hkv;
+    const long long budget = std::max(1LL, AKV_DECODE_TARGET_WORKGROUPS / units);
+    const long long nq = (long long)q.max_blocks * AKV_BLOCK_TOKENS;
+    const long long ne = (long long)e.max_blocks * AKV_BLOCK_TOKENS;
+    const long long se_max = (ne + AKV_SPLIT_TOKENS_EXACT_DEFAULT - 1) / AKV_SPLIT_TOKENS_EXACT_DEFAULT;
+    int pq = AKV_SPLIT_TOKENS_QUANT_DEFAULT;
+    for (int c = AKV_MIN_SPLIT_TOKENS; c < AKV_SPLIT_TOKENS_QUANT_DEFAULT; c += 4 * AKV_BLOCK_TOKENS)
+      if ((nq + c - 1) / c + se_max <= budget) {
+        pq = c;
+        break;
+      }
+    Pq = split_tokens(d->split_tokens_quant, pq);
+    const long long rem = budget - (nq + Pq - 1) / Pq;
+    int pe = AKV_SPLIT_TOKENS_EXACT_DEFAULT;
+    if (rem >= 1) {
+      const long long blocks = (e.max_blocks + rem - 1) / rem;
+      pe = (int)std::min<long long>(AKV_SPLIT_TOKENS_EXACT_DEFAULT,
+                                    std::max<long long>(AKV_MIN_SPLIT_TOKENS, blocks * AKV_BLOCK_TOKENS));
+    }
+    Pe = split_tokens(d->split_tokens_exact, pe);
+  } else {
     // each tier in about AKV_CHUNK_TARGET_WORKGROUPS / (B * Hkv * row groups)
     // equal runs of whole blocks (a shape-only rule, like the decode one)
     const long long nrg = ((long long)d->Tq * G + AKV_CHUNK_ROWS - 1) / AKV_CHUNK_ROWS;
@@ -192,6 +217,18 @@ size_t akv_decode_workspace_bytes(const akv_attn_desc* desc) {
 size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc) {
   Plan plan;
   return check_attn(desc, true, &plan) == AKV_OK ? plan.ws_bytes : 0;
+}
+
+akv_status akv_split_plan(const akv_attn_desc* desc, int32_t chunk, int32_t* out) {
+  Plan plan;
+  akv_status s = check_attn(desc, chunk != 0, &plan);
+  if (s != AKV_OK) return s;
+  if (!out) return fail(AKV_ERR_NULL, "out is NULL");
+  out[0] = plan.Pq;
+  out[1] = plan.Pe;
+  out[2] = plan.Sq;
+  out[3] = plan.Se;
+  return AKV_OK;
 }
 
 akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream) {

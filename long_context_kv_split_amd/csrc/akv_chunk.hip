@@ -120,7 +120,7 @@ template <int D>
 struct ERegs {
   static constexpr int KCH = 64 * D / 8 / 512;  // 16-byte K chunks per slot
   u32x4 k[kVT][KCH];
-  u32x4 v0[kVT], v1[kVT];  // tokens 2pp and 2pp + 1 of one 8-dim chunk (slots below 32 * D / 8)
+  u32x4 v[kVT][D / 64];    // 16-byte V chunks v + 512 h: dim (v + 512 h) / 8, tokens 8 ((v + 512 h) % 8) ..
 };
 
 // Slot v's K dwords: token v / 8, dword wi_k = 4 (p & 3) + (p >> 2) + 2k of
@@ -177,10 +177,12 @@ __device__ inline void exact_fetch(ERegs<D>& r, const AttnParams& p, int pb, int
       const int ci = v + 512 * k, tok = ci / CPR, ch = ci - tok * CPR;
       r.k[u][k] = *reinterpret_cast<const u32x4*>(ks + tok * D + 8 * ch);
     }
-    if (v < 32 * CPR) {
-      const int pp = v & 31, ch = v >> 5;
-      r.v0[u] = *reinterpret_cast<const u32x4*>(vs + (2 * pp) * D + 8 * ch);
-      r.v1[u] = *reinterpret_cast<const u32x4*>(vs + (2 * pp + 1) * D + 8 * ch);
+    // V is dim-major inside each half block: chunk c8 of dim t (tokens
+    // 8 c8 ..) sits in half c8 / 4, at ((c8 / 4) * D + t) * 32 + 8 (c8 % 4)
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {
+      const int ci = v + 512 * h, c8 = ci & 7;
+      r.v[u][h] = *reinterpret_cast<const u32x4*>(vs + ((c8 >> 2) * D + (ci >> 3)) * (kBlock / 2) + 8 * (c8 & 3));
     }
   }
 }
@@ -261,20 +263,21 @@ __device__ inline void exact_stage_k(const ERegs<D>& r, unsigned char* buf, int 
 
 template <int D>
 __device__ inline void exact_stage_v(const ERegs<D>& r, unsigned char* buf, int nvalid) {
-  constexpr int CPR = ChunkLds<D>::CPR, VP = ChunkLds<D>::VP;
 #pragma unroll
   for (int u = 0; u < kVT; ++u) {
     const int v = threadIdx.x + kCThreads * u;
-    if (v < 32 * CPR) {
-      const int pp = v & 31, ch = v >> 5;
-      const u32x4 x0 = 2 * pp < nvalid ? r.v0[u] : u32x4{0, 0, 0, 0};
-      const u32x4 x1 = 2 * pp + 1 < nvalid ? r.v1[u] : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (x0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t b = (x1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(buf + vchunk_off<D>(8 * ch + e, pp >> 2) + 4 * (pp & 3)) = a | (b << 16);
+    for (int h = 0; h < D / 64; ++h) {
+      const int ci = v + 512 * h, dim = ci >> 3, c = ci & 7;
+      u32x4 x = r.v[u][h];
+      if (nvalid < 64) {  // zero tokens 8c + 2i (low half), 8c + 2i + 1 (high half) past the length
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t0 = 8 * c + 2 * i;
+          x[i] &= t0 >= nvalid ? 0u : (t0 + 1 >= nvalid ? 0xFFFFu : ~0u);
+        }
       }
+      *reinterpret_cast<u32x4*>(buf + vchunk_off<D>(dim, c)) = x;
     }
   }
 }

@@ -57,17 +57,22 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressParams p) {
 #pragma unroll
   for (int tk = 0; tk < 2; ++tk) {
     float x[E];
+    // exact-tier K is token-major (a token's dims adjacent), V dim-major
+    // inside each 32-token half block (dim t of token r at
+    // ((r / 32) * d + t) * 32 + r % 32)
     const uint16_t* src = nullptr;
+    const int dstride = isv ? kBlock / 2 : 1;
     if (tk < ntok) {
       int s = p.src_start + first + tk;
       int blk = p.src_table[s >> 6];
       if (blk >= 0 && blk < p.src_num_blocks) {
-        src = (isv ? p.src_v : p.src_k) + ((size_t)(blk * p.Hkv + kv) * kBlock + (s & 63)) * D;
+        const size_t slab = (size_t)(blk * p.Hkv + kv) * kBlock * D;
+        src = isv ? p.src_v + slab + ((s & 63) >> 5) * (kBlock / 2) * D + (s & 31) : p.src_k + slab + (size_t)(s & 63) * D;
         ok[tk] = true;
       }
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = src ? bf16_bits_to_float(src[lane + 64 * e]) : 0.0f;  // E1
+    for (int e = 0; e < E; ++e) x[e] = src ? bf16_bits_to_float(src[(lane + 64 * e) * dstride]) : 0.0f;  // E1
     // E2: butterflies across lanes for h < 64, inside the lane for h = 64
 #pragma unroll
     for (int h = 1; h < 64 && h < D; h <<= 1) {

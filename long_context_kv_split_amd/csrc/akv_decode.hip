@@ -39,9 +39,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMainLds = 65536;               // LUT / V staging / merge scratch
 constexpr int kMaxWaveBlocks = 128;           // blocks per wave per split (P <= 32768)
-constexpr int kScaleStage = 1056;             // per wave: one unit's K and V scales (512 B used)
+constexpr int kScaleStage = 1056;             // per wave: two units' K and V scales (1024 B used)
 constexpr int kLdsBytes = kMainLds + kWaves * kScaleStage;
-constexpr int kVPitch = 260;  // bytes per staged exact-tier V row (bank spread)
 
 __device__ inline float4v mfma16(half8 a, half8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -115,11 +114,19 @@ __device__ inline float lane_butterfly(float x, int lane) {
   return (lane & H) ? (o - x) : (x + o);
 }
 
-// Online-softmax step on 8 scores of one head held by this lane; the running
+// Online-softmax step on N scores of one head held by this lane; the running
 // max is shared by the 4 lanes (rows 0..3 of 16) with the same column.
 // Returns the factor the running output must be scaled by.
-__device__ inline float softmax_step(SoftmaxState& st, float (&s)[8], float (&p)[8]) {
-  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+template <int N>
+__device__ inline float softmax_step(SoftmaxState& st, const float (&s)[N], float (&p)[N]) {
+  float t[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) t[e] = s[e];
+#pragma unroll
+  for (int h = N / 2; h >= 1; h >>= 1)  // pairwise tree
+#pragma unroll
+    for (int e = 0; e < h; ++e) t[e] = fmaxf(t[e], t[e + h]);
+  float mx = t[0];
   mx = fmaxf(mx, xor16(mx));
   mx = fmaxf(mx, xor32(mx));
   float mnew = fmaxf(st.m, mx);
@@ -127,7 +134,7 @@ __device__ inline float softmax_step(SoftmaxState& st, float (&s)[8], float (&p)
   float alpha = __builtin_amdgcn_exp2f(st.m - muse);
   float sum = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < N; ++e) {
     p[e] = __builtin_amdgcn_exp2f(s[e] - muse);
     sum += p[e];
   }
@@ -171,6 +178,29 @@ __device__ inline WaveBlocks load_wave_blocks(const int* table, int blk0, int nb
   wb.lo = lane < nblk_w ? table[blk0 + w + kWaves * lane] : -1;
   wb.hi = lane + 64 < nblk_w ? table[blk0 + w + kWaves * (lane + 64)] : -1;
   return wb;
+}
+
+// The block ids a wave may take in a split of P tokens starting at block
+// blk0, read before the tier length is known: the table row of tmax entries
+// bounds the read, so it can be in flight together with the length load.
+__device__ inline WaveBlocks load_split_blocks(const int* row, int tmax, int blk0, int P, int w, int lane) {
+  const int cap = min(P >> 6, tmax - blk0);
+  return load_wave_blocks(row, blk0, cap > w ? (cap - w + kWaves - 1) / kWaves : 0, w, lane);
+}
+
+// Keep the ids of the wave's first nblk_w blocks only.
+__device__ inline WaveBlocks trim_blocks(WaveBlocks wb, int nblk_w, int lane) {
+  wb.lo = lane < nblk_w ? wb.lo : -1;
+  wb.hi = lane + 64 < nblk_w ? wb.hi : -1;
+  return wb;
+}
+
+// Both tier lengths of sequence b; false if either lies outside its table
+// (the sequence's splits then write nothing and the merge reports NaN).
+__device__ inline bool tier_lengths(const AttnParams& p, int b, int& ql, int& el) {
+  ql = p.qmax ? p.qlen[b] : 0;
+  el = p.emax ? p.elen[b] : 0;
+  return ql >= 0 && ql <= p.qmax * 64 && el >= 0 && el <= p.emax * 64;
 }
 
 // Decode partials are laid out per query head: row ((b * Hkv + kv) * G + g)
@@ -280,38 +310,42 @@ __device__ inline void quant_load(QUnit<D>& u, const AttnParams& p, int pb, int 
   u.sc = *reinterpret_cast<const u32x4*>(sb);
 }
 
-template <int D, bool PARTIAL>
-__device__ inline void quant_compute(const QUnit<D>& u, int nvalid, const half8 (&Q)[D / 32],
-                                     const unsigned char* lut, unsigned char* stage, uint32_t loff, int qq,
-                                     int lane, SoftmaxState& st, float4v (&O)[D / 16]) {
-  constexpr int M = D / 32, NT = D / 16;
-  // scales: lanes < 8M hold the unit's 2M 64-byte segments; park them in LDS
-  // and read back this lane's 8 tokens per group (LDS ops of a wave run in order)
-  __builtin_amdgcn_wave_barrier();
+// This lane's group scales of one unit, parked in LDS and read back: lanes
+// < 8M hold the unit's 2M 64-byte segments (M K-groups, then M V-groups);
+// lane (col, qq) reads its 8 tokens 8qq.. of every group.
+template <int D>
+__device__ inline void quant_scales(const QUnit<D>& u, unsigned char* stage, int qq, int lane, u32x4 (&ksc)[D / 32],
+                                    u32x4 (&vsc)[D / 32]) {
+  constexpr int M = D / 32;
   if (lane < 8 * M) *reinterpret_cast<u32x4*>(stage + 16 * lane) = u.sc;
   __builtin_amdgcn_wave_barrier();
-  u32x4 ksc[M], vsc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     ksc[m] = *reinterpret_cast<const u32x4*>(stage + 64 * m + 16 * qq);
     vsc[m] = *reinterpret_cast<const u32x4*>(stage + 64 * (M + m) + 16 * qq);
   }
-  __builtin_amdgcn_wave_barrier();
-  if (PARTIAL) {
-    // zero the value scales of missing tokens so 0 * garbage cannot appear
+}
+
+// Zero the value scales of tokens >= nvalid, so 0 * garbage cannot appear.
+template <int D>
+__device__ inline void mask_value_scales(u32x4 (&vsc)[D / 32], int nvalid, int qq) {
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+  for (int m = 0; m < D / 32; ++m)
 #pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        int t0 = 8 * qq + 2 * q2;
-        uint32_t x = vsc[m][q2];
-        if (t0 >= nvalid) x = 0;
-        else if (t0 + 1 >= nvalid) x &= 0xFFFFu;
-        vsc[m][q2] = x;
-      }
-  }
-  // ---- scores
-  float s[8];
+    for (int q2 = 0; q2 < 4; ++q2) {
+      const int t0 = 8 * qq + 2 * q2;
+      uint32_t x = vsc[m][q2];
+      if (t0 >= nvalid) x = 0;
+      else if (t0 + 1 >= nvalid) x &= 0xFFFFu;
+      vsc[m][q2] = x;
+    }
+}
+
+// Scores (log2 units) of this lane's 8 tokens 8qq + e of one unit.
+template <int D>
+__device__ inline void quant_scores(const QUnit<D>& u, const u32x4 (&ksc)[D / 32], const half8 (&Q)[D / 32],
+                                    const unsigned char* lut, uint32_t loff, float (&s)[8]) {
+  constexpr int M = D / 32;
 #pragma unroll
   for (int tp = 0; tp < 2; ++tp) {
     float acc[4] = {0, 0, 0, 0};
@@ -326,7 +360,8 @@ __device__ inline void quant_compute(const QUnit<D>& u, int nvalid, const half8 
                                                   *reinterpret_cast<const uint32_t*>(r1),
                                                   *reinterpret_cast<const uint32_t*>(r2),
                                                   *reinterpret_cast<const uint32_t*>(r3)});
-      // keep the hi and lo reads as separate 32-bit reads (a paired read is slower here)
+      // keep the hi and lo reads apart: a paired read returns (hi, lo) in
+      // adjacent registers, which then need moves into the two operands
       asm volatile("" ::: "memory");
       half8 klo = __builtin_bit_cast(half8, u32x4{*reinterpret_cast<const uint32_t*>(r0 + 128),
                                                   *reinterpret_cast<const uint32_t*>(r1 + 128),
@@ -345,18 +380,15 @@ __device__ inline void quant_compute(const QUnit<D>& u, int nvalid, const half8 
     for (int r = 0; r < 4; ++r) s[4 * tp + r] = acc[r];
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    s[e] += row_swap8(s[e]);  // hi-column + lo-column partial scores
-    if (PARTIAL && 8 * qq + e >= nvalid) s[e] = neg_inf();
-  }
-  float pr[8];
-  rescale(O, softmax_step(st, s, pr));
-  half8 pb8;
+  for (int e = 0; e < 8; ++e) s[e] += row_swap8(s[e]);  // hi-column + lo-column partial scores
+}
+
+// O^T += V'^T P^T for one unit, V'^T[dim][token] = C16[code] * scale.
+template <int D>
+__device__ inline void quant_values(const QUnit<D>& u, const u32x4 (&vsc)[D / 32], half8 pb8, const unsigned char* lut,
+                                    uint32_t loff, float4v (&O)[D / 16]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pb8[e] = (_Float16)pr[e];
-  // ---- values: V'^T[dim][token] = C16[code] * scale
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int t = 0; t < D / 16; ++t) {
     const int g = t >> 1;
     const uint32_t w = u.vw[t];
     half2v l0 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<0>(w, loff)));
@@ -372,8 +404,50 @@ __device__ inline void quant_compute(const QUnit<D>& u, int nvalid, const half8 
   }
 }
 
+// One 64-token block = two 32-token units (a: tokens 0..31, b: 32..63) per
+// softmax step: the two units' table reads and matrix-core chains are
+// independent, so one wave keeps more of them in flight.  PARTIAL: only
+// the first nva / nvb tokens of a / b exist.
+template <int D, bool PARTIAL>
+__device__ inline void quant_block(const QUnit<D>& ua, const QUnit<D>& ub, int nva, int nvb, const half8 (&Q)[D / 32],
+                                   const unsigned char* lut, unsigned char* stage, uint32_t loff, int qq, int lane,
+                                   SoftmaxState& st, float4v (&O)[D / 16]) {
+  constexpr int M = D / 32;
+  // scales of both units (LDS ops of a wave run in order)
+  __builtin_amdgcn_wave_barrier();
+  u32x4 ksa[M], vsa[M], ksb[M], vsb[M];
+  quant_scales<D>(ua, stage, qq, lane, ksa, vsa);
+  quant_scales<D>(ub, stage + 512, qq, lane, ksb, vsb);
+  __builtin_amdgcn_wave_barrier();
+  if (PARTIAL) {
+    mask_value_scales<D>(vsa, nva, qq);
+    mask_value_scales<D>(vsb, nvb, qq);
+  }
+  float s[16];
+  {
+    float sa[8], sb[8];
+    quant_scores<D>(ua, ksa, Q, lut, loff, sa);
+    quant_scores<D>(ub, ksb, Q, lut, loff, sb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s[e] = (PARTIAL && 8 * qq + e >= nva) ? neg_inf() : sa[e];
+      s[8 + e] = (PARTIAL && 8 * qq + e >= nvb) ? neg_inf() : sb[e];
+    }
+  }
+  float pr[16];
+  rescale(O, softmax_step<16>(st, s, pr));
+  half8 pa8, pb8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pa8[e] = (_Float16)pr[e];
+    pb8[e] = (_Float16)pr[8 + e];
+  }
+  quant_values<D>(ua, vsa, pa8, lut, loff, O);
+  quant_values<D>(ub, vsb, pb8, lut, loff, O);
+}
+
 template <int D>
-__device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, int sx, int start, int end) {
+__device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, int sx, int s) {
   constexpr int M = D / 32;   // groups = score tiles per token tile
   constexpr int NT = D / 16;  // value tiles
   constexpr int QV = D / 32;  // query values per lane in the rotation
@@ -382,12 +456,11 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   const int G = p.G;
   unsigned char* smem = L.main;
 
-  // requests first: this wave's block ids and this lane's query values
+  // requests first, none waiting for another: this wave's block ids, this
+  // lane's query values and the tier lengths
+  const int start = s * p.Pq;
   const int blk0 = start >> 6;
-  const int nblk = ((end + 63) >> 6) - blk0;
-  const int nblk_w = (nblk - w + kWaves - 1) / kWaves;
-  const int nunits = 2 * nblk_w;  // unit u = half (u & 1) of this wave's block u >> 1
-  const WaveBlocks wb = load_wave_blocks(p.qtab + (size_t)b * p.qmax, blk0, nblk_w, w, lane);
+  const WaveBlocks wb_all = load_split_blocks(p.qtab + (size_t)b * p.qmax, p.qmax, blk0, p.Pq, w, lane);
   // rotation work split: wave w takes heads 2w, 2w+1; lane holds dims QV*(lane%32).. of head 2w + lane/32
   const int rh = 2 * w + (lane >> 5), rd0 = QV * (lane & 31);
   float qv[QV];
@@ -396,12 +469,19 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
 #pragma unroll
     for (int e = 0; e < QV; ++e) qv[e] = bf16_bits_to_float(qsrc[e]);
   }
+  // the level pair of code byte tid, for the level table below
+  const float c0 = __builtin_bit_cast(float, kLevelBits[tid & 15]);
+  const float c1 = __builtin_bit_cast(float, kLevelBits[tid >> 4]);
+  int ql, el;
+  if (!tier_lengths(p, b, ql, el) || start >= ql) return;  // bad lengths, or an idle split
+  const int end = min(start + p.Pq, ql);
+  const int nblk = ((end + 63) >> 6) - blk0;
+  const int nblk_w = (nblk - w + kWaves - 1) / kWaves;
+  const WaveBlocks wb = trim_blocks(wb_all, nblk_w, lane);
 
   // level table (needs nothing loaded): row e (code byte) = 256 B: 32 x hi pair | 32 x lo pair
   {
     const int e = tid;  // 256 threads, 256 rows
-    float c0 = __builtin_bit_cast(float, kLevelBits[e & 15]);
-    float c1 = __builtin_bit_cast(float, kLevelBits[e >> 4]);
     _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
     _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
     const uint32_t hip = h2_as_u32(half2v{h0, h1});
@@ -416,16 +496,21 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
     }
   }
 
-  // first two units' loads as soon as the block ids are in
-  auto block_of = [&](int u, bool& ok) {
-    int pb = wb.get(u >> 1);
+  // the first block's loads as soon as the block ids are in; every ring
+  // step loads a block, past the wave's last one too (that block again): with
+  // loads on every path the compiler's wait counts stay exact instead of
+  // draining all loads in flight where paths join
+  const int klast = max(nblk_w - 1, 0);
+  auto load_block = [&](QUnit<D>& u0, QUnit<D>& u1, bool& ok, int k) {
+    int pb = wb.get(min(k, klast));
     ok = pb >= 0 && pb < p.qnb;
-    return ok ? pb : 0;
+    pb = ok ? pb : 0;
+    quant_load<D>(u0, p, pb, kv, 0, j, qq, lane);
+    quant_load<D>(u1, p, pb, kv, 1, j, qq, lane);
   };
-  QUnit<D> u0, u1, u2;
-  bool ok0 = false, ok1 = false, ok2 = false;
-  if (nunits > 0) quant_load<D>(u0, p, block_of(0, ok0), kv, 0, j, qq, lane);
-  if (nunits > 1) quant_load<D>(u1, p, block_of(1, ok1), kv, 1, j, qq, lane);
+  QUnit<D> ra0, ra1, rb0, rb1;
+  bool oka, okb;
+  load_block(ra0, ra1, oka, 0);
 
   // rotated, pre-scaled query q' = H q * (RN(1/sqrt d) * scale * log2 e):
   // butterflies inside the lane for h < QV, across lanes (xor h/QV) above
@@ -489,28 +574,24 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   for (int t = 0; t < NT; ++t) O[t] = float4v{0, 0, 0, 0};
   bool poison = false;
   unsigned char* stage = L.stage + w * kScaleStage;
-  auto process = [&](const QUnit<D>& u, bool ok, int un) {
-    const int tb = (blk0 + w + kWaves * (un >> 1)) * 64 + 32 * (un & 1);
-    if (tb >= end) return;
-    if (!ok) {
-      poison = true;
-      return;
-    }
-    if (end - tb >= 32)
-      quant_compute<D, false>(u, 32, Q, smem, stage, loff, qq, lane, st, O);
+  // block k of this wave covers tokens tb .. tb + 63; a bad block id poisons
+  // the split (its partial becomes NaN), the loads then read block 0
+  auto process = [&](const QUnit<D>& u0, const QUnit<D>& u1, bool ok, int k) {
+    const int tb = (blk0 + w + kWaves * k) * 64;
+    poison |= !ok;
+    if (end - tb >= 64)
+      quant_block<D, false>(u0, u1, 32, 32, Q, smem, stage, loff, qq, lane, st, O);
     else
-      quant_compute<D, true>(u, end - tb, Q, smem, stage, loff, qq, lane, st, O);
+      quant_block<D, true>(u0, u1, min(end - tb, 32), max(end - tb - 32, 0), Q, smem, stage, loff, qq, lane, st,
+                           O);
   };
-  // three unit buffers in a ring: unit u + 2 is in flight while unit u is computed
-  for (int un = 0; un < nunits; un += 3) {
-    if (un + 2 < nunits) quant_load<D>(u2, p, block_of(un + 2, ok2), kv, (un + 2) & 1, j, qq, lane);
-    process(u0, ok0, un);
-    if (un + 1 >= nunits) break;
-    if (un + 3 < nunits) quant_load<D>(u0, p, block_of(un + 3, ok0), kv, (un + 3) & 1, j, qq, lane);
-    process(u1, ok1, un + 1);
-    if (un + 2 >= nunits) break;
-    if (un + 4 < nunits) quant_load<D>(u1, p, block_of(un + 4, ok1), kv, (un + 4) & 1, j, qq, lane);
-    process(u2, ok2, un + 2);
+  // two blocks in a ring: block k + 1 is in flight while block k is computed
+  for (int k = 0; k < nblk_w; k += 2) {
+    load_block(rb0, rb1, okb, k + 1);
+    process(ra0, ra1, oka, k);
+    if (k + 1 >= nblk_w) break;
+    load_block(ra0, ra1, oka, k + 2);
+    process(rb0, rb1, okb, k + 1);
   }
   split_epilogue<D>(p, L, b, kv, sx, st, O, poison);
 }
@@ -518,13 +599,18 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
 // ------------------------------------------------------------- exact tier
 template <int D>
 struct EUnit {
-  u32x4 kx[2][D / 32];     // K rows of both 16-token tiles
-  u32x4 vx[32 * D / 512];  // V rows (16-byte chunks) of the 32 tokens
+  u32x4 kx[2][D / 32];  // K rows of both 16-token tiles
+  u32x4 vx[D / 16];     // V^T operand of value tile t: 8 tokens of dim 16t + j
 };
 
+// Issue the loads of one 32-token unit (half c of pool block pb).  K is
+// token-major, so lane (row j, qq) reads 8 dims of one token per tile; V is
+// dim-major inside each half block, so the same lane reads tokens
+// 32c + 8qq .. + 7 of dim 16t + j: both operands straight from HBM, 1 KB of
+// consecutive bytes per load instruction, no transposition.
 template <int D>
 __device__ inline void exact_load(EUnit<D>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq, int lane) {
-  constexpr int MK = D / 32, PER = 32 * D / 512;
+  constexpr int MK = D / 32, NT = D / 16;
   const uint16_t* kslab = p.ek + ((size_t)pb * p.Hkv + kv) * kBlock * D;
   const uint16_t* vslab = p.ev + ((size_t)pb * p.Hkv + kv) * kBlock * D;
 #pragma unroll
@@ -534,26 +620,15 @@ __device__ inline void exact_load(EUnit<D>& u, const AttnParams& p, int pb, int 
 #pragma unroll
     for (int m = 0; m < MK; ++m) u.kx[tp][m] = src[m];
   }
-  const u32x4* vsrc = reinterpret_cast<const u32x4*>(vslab + 32 * c * D);
 #pragma unroll
-  for (int k = 0; k < PER; ++k) u.vx[k] = vsrc[lane + 64 * k];
+  for (int t = 0; t < NT; ++t)
+    u.vx[t] = *reinterpret_cast<const u32x4*>(vslab + (c * D + 16 * t + j) * (kBlock / 2) + 8 * qq);
 }
 
 template <int D, bool PARTIAL>
-__device__ inline void exact_compute(const EUnit<D>& u, int nvalid, const bf16x8 (&Q)[D / 32], unsigned char* vst,
-                                     float qscale2, int j, int qq, int lane, SoftmaxState& st,
-                                     float4v (&O)[D / 16]) {
-  constexpr int MK = D / 32, NT = D / 16, CH = D / 8, PER = 32 * D / 512;
-  // ---- stage V rows (zeros for missing tokens); LDS ops of one wave run in order
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    int ci = lane + 64 * k, row = ci / CH, col = ci - row * CH;
-    u32x4 x = (!PARTIAL || row < nvalid) ? u.vx[k] : u32x4{0, 0, 0, 0};
-    uint32_t* dst = reinterpret_cast<uint32_t*>(vst + row * kVPitch + col * 16);
-    dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
-  }
-  __builtin_amdgcn_wave_barrier();
+__device__ inline void exact_compute(const EUnit<D>& u, int nvalid, const bf16x8 (&Q)[D / 32], float qscale2,
+                                     int qq, SoftmaxState& st, float4v (&O)[D / 16]) {
+  constexpr int MK = D / 32, NT = D / 16;
   // ---- scores
   float s[8];
 #pragma unroll
@@ -564,36 +639,45 @@ __device__ inline void exact_compute(const EUnit<D>& u, int nvalid, const bf16x8
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[4 * tp + r] = dm[r] * qscale2;
   }
+  // missing tokens: score -inf and value 0 (the pool past the length may hold
+  // anything, and 0 * NaN would not vanish)
+  uint32_t vmask[4] = {~0u, ~0u, ~0u, ~0u};
   if (PARTIAL) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (8 * qq + e >= nvalid) s[e] = neg_inf();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t0 = 8 * qq + 2 * i;
+      vmask[i] = t0 >= nvalid ? 0u : (t0 + 1 >= nvalid ? 0xFFFFu : ~0u);
+    }
   }
   float pr[8];
   rescale(O, softmax_step(st, s, pr));
   bf16x8 pb8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) pb8[e] = (__bf16)pr[e];
-  // ---- values: V^T[dim 16t + j][token 8qq + e] from the staged rows
+  // ---- values: O^T[dim 16t + j] += V^T[dim][tokens 8qq..] x P^T
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    bf16x8 a;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      a[e] = *reinterpret_cast<const __bf16*>(vst + (8 * qq + e) * kVPitch + (16 * t + j) * 2);
-    O[t] = mfma16bf(a, pb8, O[t]);
+    u32x4 x = u.vx[t];
+    if (PARTIAL) x = u32x4{x[0] & vmask[0], x[1] & vmask[1], x[2] & vmask[2], x[3] & vmask[3]};
+    O[t] = mfma16bf(__builtin_bit_cast(bf16x8, x), pb8, O[t]);
   }
-  __builtin_amdgcn_wave_barrier();
 }
 
 template <int D>
-__device__ void exact_split(const AttnParams& p, const Lds& L, int b, int kv, int sx, int start, int end) {
+__device__ void exact_split(const AttnParams& p, const Lds& L, int b, int kv, int sx, int s) {
   constexpr int MK = D / 32;  // score tiles per token tile
   constexpr int NT = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, qq = lane >> 4;
   const int G = p.G;
 
+  // requests first, as in the compressed tier: block ids, query, lengths
+  const int start = s * p.Pe;
+  const int blk0 = start >> 6;
+  const WaveBlocks wb_all = load_split_blocks(p.etab + (size_t)b * p.emax, p.emax, blk0, p.Pe, w, lane);
   // query operand: lane (col j, qq) holds dims qq*D/4 + 8m + e of head j
   bf16x8 Q[MK];
   {
@@ -606,7 +690,9 @@ __device__ void exact_split(const AttnParams& p, const Lds& L, int b, int kv, in
       Q[m] = __builtin_bit_cast(bf16x8, x);
     }
   }
-  unsigned char* vst = L.main + w * (32 * kVPitch + 64);  // this wave's V staging rows
+  int ql, el;
+  if (!tier_lengths(p, b, ql, el) || start >= el) return;  // bad lengths, or an idle split
+  const int end = min(start + p.Pe, el);
 
   SoftmaxState st{neg_inf(), 0.0f};
   float4v O[NT];
@@ -614,28 +700,31 @@ __device__ void exact_split(const AttnParams& p, const Lds& L, int b, int kv, in
   for (int t = 0; t < NT; ++t) O[t] = float4v{0, 0, 0, 0};
   bool poison = false;
 
-  const int blk0 = start >> 6;
   const int nblk = ((end + 63) >> 6) - blk0;
   const int nblk_w = (nblk - w + kWaves - 1) / kWaves;
-  const WaveBlocks wb = load_wave_blocks(p.etab + (size_t)b * p.emax, blk0, nblk_w, w, lane);
+  const WaveBlocks wb = trim_blocks(wb_all, nblk_w, lane);
+  // every step loads, past the wave's last block too (that block again), so
+  // the wait counts stay exact; a bad block id poisons the split (its
+  // partial becomes NaN) and the loads then read block 0
+  const int ilast = max(nblk_w - 1, 0);
   auto block_of = [&](int i, bool& ok) {
-    int pb = wb.get(i);
+    int pb = wb.get(min(i, ilast));
     ok = pb >= 0 && pb < p.enb;
     return ok ? pb : 0;
   };
   EUnit<D> ua, ub;
-  bool oka = false, okb = false;
-  if (nblk_w > 0) exact_load<D>(ua, p, block_of(0, oka), kv, 0, j, qq, lane);
+  bool oka, okb;
+  exact_load<D>(ua, p, block_of(0, oka), kv, 0, j, qq, lane);
   for (int i = 0; i < nblk_w; ++i) {
-    int pb = block_of(i, okb);
+    const int pb = block_of(i, okb);
     exact_load<D>(ub, p, pb, kv, 1, j, qq, lane);
     const int tb = (blk0 + w + kWaves * i) * 64;
-    if (!oka) poison = true;
-    else if (end - tb >= 32) exact_compute<D, false>(ua, 32, Q, vst, p.qscale2, j, qq, lane, st, O);
-    else exact_compute<D, true>(ua, end - tb, Q, vst, p.qscale2, j, qq, lane, st, O);
-    if (i + 1 < nblk_w) exact_load<D>(ua, p, block_of(i + 1, oka), kv, 0, j, qq, lane);
-    if (okb && end - tb >= 64) exact_compute<D, false>(ub, 32, Q, vst, p.qscale2, j, qq, lane, st, O);
-    else if (okb && end - tb > 32) exact_compute<D, true>(ub, end - tb - 32, Q, vst, p.qscale2, j, qq, lane, st, O);
+    poison |= !oka;
+    if (end - tb >= 32) exact_compute<D, false>(ua, 32, Q, p.qscale2, qq, st, O);
+    else exact_compute<D, true>(ua, end - tb, Q, p.qscale2, qq, st, O);
+    exact_load<D>(ua, p, block_of(i + 1, oka), kv, 0, j, qq, lane);
+    if (end - tb >= 64) exact_compute<D, false>(ub, 32, Q, p.qscale2, qq, st, O);
+    else if (end - tb > 32) exact_compute<D, true>(ub, end - tb - 32, Q, p.qscale2, qq, st, O);
   }
   split_epilogue<D>(p, L, b, kv, sx, st, O, poison);
 }
@@ -664,20 +753,12 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(AttnParams p)
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   const Lds L = lds_layout(smem);
   const int sx = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int ql = p.qmax ? p.qlen[b] : 0;
-  const int el = p.emax ? p.elen[b] : 0;
-  if (ql < 0 || ql > p.qmax * 64 || el < 0 || el > p.emax * 64) return;  // merge reports NaN
-  const bool quant = sx < p.Sq;
-  const int s = quant ? sx : sx - p.Sq;
-  const int P = quant ? p.Pq : p.Pe;
-  const int len = quant ? ql : el;
-  const int start = s * P;
-  if (start >= len) return;  // idle split of a shorter sequence
-  const int end = min(start + P, len);
-  if (quant)
-    quant_split<D>(p, L, b, kv, sx, start, end);
+  // the split reads its tier's length itself, in the same round trip as its
+  // block ids and query
+  if (sx < p.Sq)
+    quant_split<D>(p, L, b, kv, sx, sx);
   else
-    exact_split<D>(p, L, b, kv, sx, start, end);
+    exact_split<D>(p, L, b, kv, sx, sx - p.Sq);
 }
 
 constexpr int kMergeThreads = 512;

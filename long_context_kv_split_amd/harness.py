@@ -34,15 +34,21 @@ def vcode_byte(d: int, tok: np.ndarray, dim: np.ndarray) -> np.ndarray:
     return ((c * 4 + a) * 16 + i) * (d >> 2) + 4 * t + b
 
 
-def pages_from_tokens(x: np.ndarray, n_blocks_pool: int, table_row: np.ndarray, out: np.ndarray) -> None:
-    """Scatter token-major x [n, Hkv, d] into a pool [blocks, Hkv, 64, d] by a table row."""
+def pages_from_tokens(x: np.ndarray, n_blocks_pool: int, table_row: np.ndarray, out: np.ndarray,
+                      dim_major: bool = False) -> None:
+    """Scatter token-major x [n, Hkv, d] into a pool by a table row: [blocks, Hkv, 64, d]
+    (exact-tier K), or [blocks, Hkv, 2, d, 32] with dim_major (exact-tier V: dim-major
+    inside each 32-token half block)."""
     n, hkv, d = x.shape
     nb = -(-n // BLOCK)
     if nb == 0:
         return
     pad = np.zeros((nb * BLOCK, hkv, d), dtype=x.dtype)
     pad[:n] = x
-    out[table_row[:nb]] = pad.reshape(nb, BLOCK, hkv, d).transpose(0, 2, 1, 3)
+    if dim_major:
+        out[table_row[:nb]] = pad.reshape(nb, 2, BLOCK // 2, hkv, d).transpose(0, 3, 1, 4, 2)
+    else:
+        out[table_row[:nb]] = pad.reshape(nb, BLOCK, hkv, d).transpose(0, 2, 1, 3)
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:
@@ -87,10 +93,10 @@ class DeviceWorkload:
         self.emax = w.exact_table.shape[1] if w.exact_len.max(initial=0) > 0 else 0
         self.qmax = w.quant_table.shape[1] if (w.quant_len.max(initial=0) > 0 or w.evict) else 0
         ek = np.zeros((max(1, w.exact_pool_blocks), hkv, BLOCK, d), dtype=np.uint16)
-        ev = np.zeros_like(ek)
+        ev = np.zeros((max(1, w.exact_pool_blocks), hkv, 2, d, BLOCK // 2), dtype=np.uint16)
         for b in range(w.B):
             pages_from_tokens(w.exact_k[b], w.exact_pool_blocks, w.exact_table[b], ek)
-            pages_from_tokens(w.exact_v[b], w.exact_pool_blocks, w.exact_table[b], ev)
+            pages_from_tokens(w.exact_v[b], w.exact_pool_blocks, w.exact_table[b], ev, dim_major=True)
         qnb = max(1, w.quant_pool_blocks)
         self.pools = [Pools(
             _dev(ek, device), _dev(ev, device),
@@ -118,10 +124,10 @@ class DeviceWorkload:
                 continue
             nb = -(-n // BLOCK)
             sk = np.zeros((nb, w.Hkv, BLOCK, w.d), dtype=np.uint16)
-            sv = np.zeros_like(sk)
+            sv = np.zeros((nb, w.Hkv, 2, w.d, BLOCK // 2), dtype=np.uint16)
             ident = np.arange(nb, dtype=np.int32)
             pages_from_tokens(w.quant_k_src[b], nb, ident, sk)
-            pages_from_tokens(w.quant_v_src[b], nb, ident, sv)
+            pages_from_tokens(w.quant_v_src[b], nb, ident, sv, dim_major=True)
             dk, dv, dt = _dev(sk, self.device), _dev(sv, self.device), _dev(ident, self.device)
             dst_t = self.quant_table[b]
             desc = akv.CompressDesc(

@@ -41,7 +41,7 @@ def test_abi_version_and_exports():
     names = akv.header_functions()
     assert set(names) == {"akv_abi_version", "akv_last_error", "akv_decode_workspace_bytes",
                           "akv_chunk_workspace_bytes", "akv_attend_decode", "akv_attend_chunk",
-                          "akv_lse_merge", "akv_compress_evicted"}
+                          "akv_split_plan", "akv_lse_merge", "akv_compress_evicted"}
     for n in names:
         assert hasattr(akv.LIB, n), n
 
@@ -55,8 +55,8 @@ def test_exports_via_nm():
 
 def test_workspace_bytes_hybrid128k_shape():
     d = good_desc()
-    # splits: exact 64*64/1024 = 4, quant ceil(1936*64/1024) = 121 -> 125 splits
-    rows = 1 * 4 * 125 * 1 * 8
+    # splits: quant ceil(1936*64/1024) = 121, exact 7 of 640 tokens -> 128 splits
+    rows = 1 * 4 * 128 * 1 * 8
     po = (rows * 128 * 4 + 255) // 256 * 256
     assert akv.akv_decode_workspace_bytes(d) == po + rows * 4
     assert akv.akv_decode_workspace_bytes(good_desc(d=96)) == 0
@@ -77,12 +77,50 @@ def test_chunk_split_planner_c5_shape():
     d2 = good_desc(Tq=512, exact=e, quant=q, split_tokens_exact=4608, split_tokens_quant=29184)
     rows = 1 * 4 * 2 * 512 * 8
     assert akv.akv_chunk_workspace_bytes(d2) == rows * 128 * 4 + rows * 4
-    # the decode rule is unchanged (1024-token splits)
-    assert akv.akv_decode_workspace_bytes(good_desc(exact=e, quant=q)) == (4 * (5 + 29) * 8) * 516
+    # the decode rule on the same shape: 114 compressed splits of 256 and 12
+    # exact splits of 384 tokens (one round of 504 workgroups)
+    assert akv.akv_decode_workspace_bytes(good_desc(exact=e, quant=q)) == (4 * (114 + 12) * 8) * 516
     # a small chunk still gets whole-block splits, never above the maximum
     d3 = good_desc(Tq=1, Hq=4, Hkv=1, exact=e, quant=q)
     rows = 1 * 1 * (72 + 456) * 1 * 4      # 512 runs wanted -> one block per split
     assert akv.akv_chunk_workspace_bytes(d3) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+
+
+def _plan(chunk=False, **over):
+    p = akv.akv_split_plan(good_desc(**over), chunk)
+    return p["split_tokens_quant"], p["split_tokens_exact"], p["splits_quant"], p["splits_exact"]
+
+
+def _tiers(qblocks, eblocks):
+    q = good_desc().quant
+    q.max_blocks = q.num_blocks = qblocks
+    e = good_desc().exact
+    e.max_blocks = e.num_blocks = eblocks
+    return dict(quant=q, exact=e)
+
+
+def test_decode_split_planner():
+    """One round of <= 512 workgroups when the shape allows it, else 1024-token splits."""
+    # 1 sequence x 4 kv heads, 123,904 + 4,096 tokens: 4 * (121 + 7) = 512 workgroups
+    assert _plan() == (1024, 640, 121, 7)
+    # exact tier only, 32,768 tokens: 128 splits of 256 tokens per kv head
+    assert _plan(**_tiers(0, 512)) == (256, 256, 0, 128)
+    # 32 sequences (ragged batch, tables of 1,024 + 32 blocks): no room, the defaults
+    assert _plan(B=32, **_tiers(1024, 32)) == (1024, 1024, 64, 2)
+    # 4 query heads on 1 kv head, 384 + 128 tokens: the smallest splits
+    assert _plan(Hq=4, Hkv=1, d=64, **_tiers(6, 2)) == (256, 256, 2, 1)
+    # a 28,672 + 4,608-token history: 256-token compressed splits leave 16 slots
+    assert _plan(**_tiers(448, 72)) == (256, 320, 112, 15)
+    # explicit sizes win, and the other tier fills what is left
+    assert _plan(split_tokens_quant=2048) == (2048, 256, 61, 16)
+    assert _plan(split_tokens_exact=2048) == (1024, 2048, 121, 2)
+    # the chunk keeps its own rule
+    assert _plan(True, Tq=512, **_tiers(456, 72)) == (7296, 1152, 4, 4)
+    for tq, tiers in ((1, _tiers(1936, 64)), (1, _tiers(0, 512))):
+        p = akv.akv_split_plan(good_desc(Tq=tq, **tiers))
+        assert 4 * (p["splits_quant"] + p["splits_exact"]) <= 512
+    with pytest.raises(akv.AKVError):
+        akv.akv_split_plan(good_desc(d=96))
 
 
 def test_null_checks_first():
