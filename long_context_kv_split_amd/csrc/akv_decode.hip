@@ -383,24 +383,32 @@ __device__ inline void quant_scores(const QUnit<D>& u, const u32x4 (&ksc)[D / 32
   for (int e = 0; e < 8; ++e) s[e] += row_swap8(s[e]);  // hi-column + lo-column partial scores
 }
 
-// O^T += V'^T P^T for one unit, V'^T[dim][token] = C16[code] * scale.
+// O^T += V'^T P^T for one unit, V'^T[dim][token] = C16[code] * scale.  The
+// scale belongs to (token, group), so it multiplies the probabilities
+// instead: value tile t (group t / 2) uses P_g = P * scale(., g), and the
+// table levels enter the matrix cores as they are (4 multiplies per group
+// instead of 4 per tile).
 template <int D>
 __device__ inline void quant_values(const QUnit<D>& u, const u32x4 (&vsc)[D / 32], half8 pb8, const unsigned char* lut,
                                     uint32_t loff, float4v (&O)[D / 16]) {
+  constexpr int M = D / 32;
+  const u32x4 pw = __builtin_bit_cast(u32x4, pb8);
+  half8 pg[M];
+#pragma unroll
+  for (int g = 0; g < M; ++g) {
+    u32x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = h2_as_u32(u32_as_h2(pw[i]) * u32_as_h2(vsc[g][i]));
+    pg[g] = __builtin_bit_cast(half8, x);
+  }
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    const int g = t >> 1;
     const uint32_t w = u.vw[t];
-    half2v l0 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<0>(w, loff)));
-    half2v l1 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<1>(w, loff)));
-    half2v l2 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<2>(w, loff)));
-    half2v l3 = u32_as_h2(*reinterpret_cast<const uint32_t*>(lut + lut_addr<3>(w, loff)));
-    half2v x0 = l0 * u32_as_h2(vsc[g][0]);
-    half2v x1 = l1 * u32_as_h2(vsc[g][1]);
-    half2v x2 = l2 * u32_as_h2(vsc[g][2]);
-    half2v x3 = l3 * u32_as_h2(vsc[g][3]);
-    half8 a = __builtin_bit_cast(half8, u32x4{h2_as_u32(x0), h2_as_u32(x1), h2_as_u32(x2), h2_as_u32(x3)});
-    O[t] = mfma16(a, pb8, O[t]);
+    const uint32_t l0 = *reinterpret_cast<const uint32_t*>(lut + lut_addr<0>(w, loff));
+    const uint32_t l1 = *reinterpret_cast<const uint32_t*>(lut + lut_addr<1>(w, loff));
+    const uint32_t l2 = *reinterpret_cast<const uint32_t*>(lut + lut_addr<2>(w, loff));
+    const uint32_t l3 = *reinterpret_cast<const uint32_t*>(lut + lut_addr<3>(w, loff));
+    O[t] = mfma16(__builtin_bit_cast(half8, u32x4{l0, l1, l2, l3}), pg[t >> 1], O[t]);
   }
 }
 
