@@ -19,6 +19,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -133,6 +135,44 @@ def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None, 
     return w, dw, kv_bytes, n_rep, ev_ms, wall_ms
 
 
+def bench_step(stream, steps=640, warmup=64):
+    """akv_append_evict on decode batches: every step appends each sequence's new
+    K/V to its exact window; every 64th step also moves the window's oldest block
+    into the compressed tier (rotate + encode), so a 64-step run holds one move
+    per sequence."""
+    import torch
+    from long_context_kv_split_amd import akv, harness, synth
+    out = {}
+    for label, B, W in (("B1", 1, 4096), ("B32", 32, 2048)):
+        Hkv, d = 4, 128
+        room = -(-(warmup + 2 * steps) // 64) + 2          # compressed blocks the moves need
+        w = synth.make_small(f"step_{label}", B=B, Hq=32, Hkv=Hkv, d=d, quant=[0] * B, exact=[W] * B,
+                             reserve_exact=[1] * B, reserve_quant=[room] * B)
+        dw = harness.DeviceWorkload(w)
+        nk, nv = synth.step_tokens(0, 8, B, Hkv, d)
+        dk = torch.from_numpy(nk.view(np.int16)).cuda()
+        dv = torch.from_numpy(nv.view(np.int16)).cuda()
+        descs = [dw.append_desc(W, dk[i], dv[i]) for i in range(8)]
+        h = stream.cuda_stream
+
+        def call(i):
+            st = akv.akv_append_evict(descs[i], h)
+            if st:
+                akv.check(st)
+
+        ev_ms, wall_ms = time_calls(call, 8, warmup, steps, stream)
+        lens = dw.exact_len.cpu().numpy()
+        assert ((lens >= W) & (lens < W + 64)).all(), f"step {label}: exact lengths {lens}"
+        # algorithmic bytes per step: new K/V read + written; amortized 1/64 of a
+        # block move (bf16 read, codes + scales written)
+        per_seq = Hkv * (2 * 2 * d * 2) + Hkv * 64 * (2 * 2 * d + 2 * (d // 2 + 2 * (d // 32))) / 64.0
+        out[label] = {"B": B, "window": W, "us_per_step": ev_ms * 1e3, "wall_us_per_step": wall_ms * 1e3,
+                      "steps": steps, "moves_per_64_steps": 1, "bytes_per_step": per_seq * B,
+                      "sequence_steps_per_s": B / (ev_ms * 1e-3)}
+        del dw
+    return out
+
+
 def chunk_flops(w) -> float:
     """QK^T + PV multiply-adds x 2 of one chunk call: every query sees the whole
     history before the chunk plus, causally, (Tq + 1) / 2 chunk tokens on average."""
@@ -222,6 +262,9 @@ def main():
                              "kv_gbps": b2 / (e2 * 1e-3) / 1e9, "replicas": r2,
                              "decode_tokens_per_s": w2.B / (e2 * 1e-3)}
                 log(f"bench: {name} {e2 * 1e3:.2f} us/call")
+        log("bench: per-step append / evict")
+        step = bench_step(stream)
+        log("bench: step " + ", ".join(f"{k} {v['us_per_step']:.2f} us" for k, v in step.items()))
         chunk = None
         if not args.no_chunk:
             log("bench: building chunk workload")
@@ -272,6 +315,8 @@ def main():
         "cpu_baseline": cpu,
         "kernel_source_hash": khash,
     }
+    out["step"] = {"workload": "akv_append_evict per decode step, Hkv 4, d 128 (B1: window 4096; "
+                           "B32: window 2048); one block move per sequence every 64 steps", **step}
     if chunk:
         out["chunk"] = chunk
     if aux:

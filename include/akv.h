@@ -258,6 +258,49 @@ akv_status akv_lse_merge(const float* o_parts, const float* lse_parts, int32_t P
  * akv_compress_desc).  Enqueues one encode kernel. */
 akv_status akv_compress_evicted(const akv_compress_desc* desc, void* stream);
 
+/* One decode step's history bookkeeping, fused on the GPU (ActiveKV,
+ * "Context beyond VRAM", "What I built": each step appends the new key/value
+ * to the recent exact window, and older history lives in the compact tier).
+ * For every sequence b, with n = exact_lengths[b] and m = quant_lengths[b]
+ * read on the device:
+ *   1. the new token's K and V (bf16 [B][Hkv][d]) are written at exact-tier
+ *      position n (block exact_table[b][n / 64], layouts above);
+ *   2. if n + 1 >= window + 64, m + 64 <= 64 * quant_max_blocks and m is even,
+ *      the 64 oldest exact tokens (the first block of the row) are rotated
+ *      and encoded into compressed positions [m, m + 64) exactly as
+ *      akv_compress_evicted encodes them, the ceil((n + 1) / 64) entries in
+ *      use of the exact table row rotate left by one (the freed block comes
+ *      right after the blocks still in use, where the appends continue),
+ *      exact_lengths[b] = n + 1 - 64 and quant_lengths[b] = m + 64;
+ *   3. otherwise exact_lengths[b] = n + 1.
+ * Lengths and the exact table are device memory, updated in place; the
+ * compressed table is only read.  A sequence whose exact table has no room
+ * for the new token (n / 64 >= exact_max_blocks), or whose length is out of
+ * range, gets exact_lengths[b] = -1, so its attention outputs are NaN until
+ * the caller resets it.  window: a positive multiple of 64 with
+ * window / 64 + 1 <= exact_max_blocks.  Enqueues two kernels (append +
+ * encode, then lengths and table).  Calls on one sequence must not overlap. */
+typedef struct akv_append_desc {
+  uint32_t struct_size;        /* sizeof(akv_append_desc) */
+  int32_t B, Hkv, d, window;
+  const uint16_t* new_k;       /* bf16 [B][Hkv][d], 16-byte aligned */
+  const uint16_t* new_v;
+  uint16_t* exact_k;           /* exact-tier pools (layouts above) */
+  uint16_t* exact_v;
+  int32_t* exact_table;        /* [B][exact_max_blocks], rotated in place */
+  int32_t* exact_lengths;      /* [B], updated in place */
+  int32_t exact_max_blocks, exact_num_blocks;
+  uint8_t* k_codes;            /* compressed-tier pools (layouts above) */
+  uint8_t* v_codes;
+  uint16_t* k_scales;
+  uint16_t* v_scales;
+  const int32_t* quant_table;  /* [B][quant_max_blocks] */
+  int32_t* quant_lengths;      /* [B], updated in place */
+  int32_t quant_max_blocks, quant_num_blocks;
+} akv_append_desc;
+
+akv_status akv_append_evict(const akv_append_desc* desc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,18 @@ class CompressDesc(ctypes.Structure):
         super().__init__(struct_size=ctypes.sizeof(CompressDesc), **kw)
 
 
+class AppendDesc(ctypes.Structure):
+    _fields_ = [("struct_size", c_uint32), ("B", c_int32), ("Hkv", c_int32), ("d", c_int32), ("window", c_int32),
+                ("new_k", c_void_p), ("new_v", c_void_p), ("exact_k", c_void_p), ("exact_v", c_void_p),
+                ("exact_table", c_void_p), ("exact_lengths", c_void_p), ("exact_max_blocks", c_int32),
+                ("exact_num_blocks", c_int32), ("k_codes", c_void_p), ("v_codes", c_void_p),
+                ("k_scales", c_void_p), ("v_scales", c_void_p), ("quant_table", c_void_p),
+                ("quant_lengths", c_void_p), ("quant_max_blocks", c_int32), ("quant_num_blocks", c_int32)]
+
+    def __init__(self, **kw):
+        super().__init__(struct_size=ctypes.sizeof(AppendDesc), **kw)
+
+
 class AKVError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -109,6 +121,8 @@ def _load() -> ctypes.CDLL:
     lib.akv_lse_merge.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.akv_compress_evicted.restype = ctypes.c_int
     lib.akv_compress_evicted.argtypes = [P(CompressDesc), c_void_p]
+    lib.akv_append_evict.restype = ctypes.c_int
+    lib.akv_append_evict.argtypes = [P(AppendDesc), c_void_p]
     return lib
 
 
@@ -166,3 +180,7 @@ def check(status: int) -> None:
     """Raise AKVError for a non-OK status (with the library's message)."""
     if status != AKV_OK:
         raise AKVError(status, akv_last_error())
+
+
+def akv_append_evict(desc: AppendDesc, stream: int = 0) -> int:
+    return LIB.akv_append_evict(ctypes.byref(desc), stream)

@@ -19,6 +19,7 @@ hipError_t launch_chunk(const AttnParams& p, int D, hipStream_t stream);
 hipError_t launch_lse_merge(const float* op, const float* lp, int P, int R, int d, float* o, float* lse,
                             hipStream_t stream);
 hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream);
+hipError_t launch_append_evict(const akv_append_desc* d, hipStream_t stream);
 }  // namespace akv
 
 
@@ -283,6 +284,30 @@ akv_status akv_compress_evicted(const akv_compress_desc* d, void* stream) {
     return fail(AKV_ERR_ALIGN, "compress buffers misaligned");
   if (d->n_tokens == 0) return AKV_OK;
   return hip_status(akv::launch_compress(d, static_cast<hipStream_t>(stream)), "akv_compress_evicted");
+}
+
+akv_status akv_append_evict(const akv_append_desc* d, void* stream) {
+  if (!d) return fail(AKV_ERR_NULL, "descriptor is NULL");
+  if (d->struct_size < sizeof(akv_append_desc))
+    return fail(AKV_ERR_SHAPE, "struct_size %u < %zu", d->struct_size, sizeof(akv_append_desc));
+  if (!d->new_k || !d->new_v || !d->exact_k || !d->exact_v || !d->exact_table || !d->exact_lengths ||
+      !d->k_codes || !d->v_codes || !d->k_scales || !d->v_scales || !d->quant_table || !d->quant_lengths)
+    return fail(AKV_ERR_NULL, "an append pointer is NULL");
+  if (d->B < 1 || d->Hkv < 1 || d->d < 1 || d->exact_max_blocks < 1 || d->exact_num_blocks < 1 ||
+      d->quant_max_blocks < 1 || d->quant_num_blocks < 1)
+    return fail(AKV_ERR_SHAPE, "append sizes out of range");
+  if (d->window < AKV_BLOCK_TOKENS || d->window % AKV_BLOCK_TOKENS)
+    return fail(AKV_ERR_SHAPE, "window %d must be a positive multiple of %d", d->window, AKV_BLOCK_TOKENS);
+  if (d->window / AKV_BLOCK_TOKENS + 1 > d->exact_max_blocks)
+    return fail(AKV_ERR_SHAPE, "window %d needs %d exact-table entries (have %d)", d->window,
+                d->window / AKV_BLOCK_TOKENS + 1, d->exact_max_blocks);
+  if (d->d != 64 && d->d != 128) return fail(AKV_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  if (d->B > 32767 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B must be <= 32767 and Hkv <= 65535");
+  if (!aligned(d->new_k, 2) || !aligned(d->new_v, 2) || !aligned(d->exact_k, 2) || !aligned(d->exact_v, 2) ||
+      !aligned(d->k_scales, 2) || !aligned(d->v_scales, 2) || !aligned(d->exact_table, 4) ||
+      !aligned(d->exact_lengths, 4) || !aligned(d->quant_table, 4) || !aligned(d->quant_lengths, 4))
+    return fail(AKV_ERR_ALIGN, "append buffers misaligned");
+  return hip_status(akv::launch_append_evict(d, static_cast<hipStream_t>(stream)), "akv_append_evict");
 }
 
 }  // extern "C"

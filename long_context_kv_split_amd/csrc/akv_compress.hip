@@ -41,11 +41,11 @@ struct CompressParams {
   int dst_num_blocks, dst_start;
 };
 
+// Encode token pair `pair` (tokens 2 pair, 2 pair + 1 of the range) of one
+// (kv head, K|V): one wavefront, lane l holding elements l + 64k.
 template <int D>
-__global__ __launch_bounds__(64) void compress_kernel(CompressParams p) {
+__device__ inline void encode_pair(const CompressParams& p, int pair, int kv, int isv, int lane) {
   constexpr int E = D / 64;  // elements per lane per token
-  const int pair = blockIdx.x, kv = blockIdx.y, isv = blockIdx.z;
-  const int lane = threadIdx.x;
   const int first = 2 * pair;
   const int ntok = min(2, p.n_tokens - first);
   const float rd = inv_sqrt_d(D);
@@ -150,6 +150,115 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressParams p) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(64) void compress_kernel(CompressParams p) {
+  encode_pair<D>(p, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
+}
+
+// ------------------------------------------------------------ per-step append / evict
+struct StepParams {
+  int B, Hkv, window;
+  const uint16_t* new_k;
+  const uint16_t* new_v;
+  uint16_t* ek;
+  uint16_t* ev;
+  int32_t* etab;
+  int32_t* elen;
+  int emax, enb;
+  uint8_t* kc;
+  uint8_t* vc;
+  uint16_t* ks;
+  uint16_t* vs;
+  const int32_t* qtab;
+  int32_t* qlen;
+  int qmax, qnb;
+};
+
+// What the step does to sequence b, decided from its lengths before the
+// step (both kernels of the step take the same decision).
+struct StepPlan {
+  int n, m;        // exact and compressed lengths before the step
+  bool append;     // the new token has a place in the exact table
+  bool evict;      // the exact tier's first block moves to the compressed tier
+};
+
+__device__ inline StepPlan step_plan(const StepParams& p, int b) {
+  StepPlan s;
+  s.n = p.elen[b];
+  s.m = p.qlen[b];
+  s.append = s.n >= 0 && (s.n >> 6) < p.emax;
+  s.evict = s.append && s.n + 1 >= p.window + kBlock && s.m >= 0 && s.m + kBlock <= p.qmax * kBlock && !(s.m & 1);
+  return s;
+}
+
+// grid (33, Hkv, 2B): x < 32 encodes token pair x of the evicted block (when
+// the sequence evicts), x == 32 writes the new token; z = 2 b + (K|V).  The
+// append writes block n / 64 >= 1 while the encode reads block 0, so the two
+// never touch the same bytes.
+template <int D>
+__global__ __launch_bounds__(64) void append_evict_kernel(StepParams p) {
+  const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z >> 1, isv = blockIdx.z & 1, lane = threadIdx.x;
+  const StepPlan s = step_plan(p, b);
+  if (x == kBlock / 2) {
+    if (!s.append) return;
+    const int pb = p.etab[(size_t)b * p.emax + (s.n >> 6)];
+    if (pb < 0 || pb >= p.enb) return;  // the attention reports the bad id as NaN
+    const int r = s.n & 63;
+    const uint16_t* src = (isv ? p.new_v : p.new_k) + ((size_t)b * p.Hkv + kv) * D;
+    const size_t slab = ((size_t)pb * p.Hkv + kv) * kBlock * D;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) {
+      const int t = lane + 64 * e;
+      if (!isv)
+        p.ek[slab + (size_t)r * D + t] = src[t];  // token-major
+      else
+        p.ev[slab + ((size_t)(r >> 5) * D + t) * (kBlock / 2) + (r & 31)] = src[t];  // dim-major per half block
+    }
+    return;
+  }
+  if (!s.evict) return;
+  CompressParams c;
+  c.Hkv = p.Hkv;
+  c.src_k = p.ek;
+  c.src_v = p.ev;
+  c.src_table = p.etab + (size_t)b * p.emax;
+  c.src_num_blocks = p.enb;
+  c.src_start = 0;
+  c.n_tokens = kBlock;
+  c.dst_kc = p.kc;
+  c.dst_vc = p.vc;
+  c.dst_ks = p.ks;
+  c.dst_vs = p.vs;
+  c.dst_table = p.qtab + (size_t)b * p.qmax;
+  c.dst_num_blocks = p.qnb;
+  c.dst_start = s.m;
+  encode_pair<D>(c, x, kv, isv, lane);
+}
+
+// After the encode has read the old first block: lengths, and the rotation
+// of the ceil((n + 1) / 64) blocks in use so the freed block comes right after
+// the ones still in use.
+__global__ __launch_bounds__(64) void step_commit_kernel(StepParams p) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b >= p.B) return;
+  const StepPlan s = step_plan(p, b);
+  if (!s.append) {
+    p.elen[b] = -1;
+    return;
+  }
+  if (!s.evict) {
+    p.elen[b] = s.n + 1;
+    return;
+  }
+  int32_t* row = p.etab + (size_t)b * p.emax;
+  const int used = (s.n + 1 + kBlock - 1) / kBlock;
+  const int first = row[0];
+  for (int i = 0; i + 1 < used; ++i) row[i] = row[i + 1];
+  row[used - 1] = first;
+  p.elen[b] = s.n + 1 - kBlock;
+  p.qlen[b] = s.m + kBlock;
+}
+
 hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream) {
   CompressParams p;
   p.Hkv = d->Hkv;
@@ -171,6 +280,38 @@ hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream) {
     hipLaunchKernelGGL(compress_kernel<64>, grid, dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_evict(const akv_append_desc* d, hipStream_t stream) {
+  StepParams p;
+  p.B = d->B;
+  p.Hkv = d->Hkv;
+  p.window = d->window;
+  p.new_k = d->new_k;
+  p.new_v = d->new_v;
+  p.ek = d->exact_k;
+  p.ev = d->exact_v;
+  p.etab = d->exact_table;
+  p.elen = d->exact_lengths;
+  p.emax = d->exact_max_blocks;
+  p.enb = d->exact_num_blocks;
+  p.kc = d->k_codes;
+  p.vc = d->v_codes;
+  p.ks = d->k_scales;
+  p.vs = d->v_scales;
+  p.qtab = d->quant_table;
+  p.qlen = d->quant_lengths;
+  p.qmax = d->quant_max_blocks;
+  p.qnb = d->quant_num_blocks;
+  dim3 grid(kBlock / 2 + 1, d->Hkv, 2 * d->B);
+  if (d->d == 64)
+    hipLaunchKernelGGL(append_evict_kernel<64>, grid, dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(append_evict_kernel<128>, grid, dim3(64), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(step_commit_kernel, dim3((d->B + 63) / 64), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

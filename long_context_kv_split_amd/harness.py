@@ -90,8 +90,9 @@ class DeviceWorkload:
         self.quant_len = _dev(w.quant_len, device)
         self.exact_table = _dev(w.exact_table, device)
         self.quant_table = _dev(w.quant_table, device)
-        self.emax = w.exact_table.shape[1] if w.exact_len.max(initial=0) > 0 else 0
-        self.qmax = w.quant_table.shape[1] if (w.quant_len.max(initial=0) > 0 or w.evict) else 0
+        # a tier is present when its table holds any block (tokens or room)
+        self.emax = w.exact_table.shape[1] if (w.exact_table >= 0).any() else 0
+        self.qmax = w.quant_table.shape[1] if (w.quant_table >= 0).any() else 0
         ek = np.zeros((max(1, w.exact_pool_blocks), hkv, BLOCK, d), dtype=np.uint16)
         ev = np.zeros((max(1, w.exact_pool_blocks), hkv, 2, d, BLOCK // 2), dtype=np.uint16)
         for b in range(w.B):
@@ -140,6 +141,30 @@ class DeviceWorkload:
             akv.check(akv.akv_compress_evicted(desc, stream or stream_handle()))
             torch.cuda.synchronize()
             del dk, dv, dt
+
+    def append_desc(self, window: int, new_k: torch.Tensor, new_v: torch.Tensor, replica: int = 0) -> akv.AppendDesc:
+        """Descriptor of one fused append / evict step on this workload's device state."""
+        w, P = self.w, self.pools[replica]
+        return akv.AppendDesc(
+            B=w.B, Hkv=w.Hkv, d=w.d, window=window, new_k=ptr(new_k), new_v=ptr(new_v),
+            exact_k=ptr(P.ek), exact_v=ptr(P.ev), exact_table=ptr(self.exact_table),
+            exact_lengths=ptr(self.exact_len), exact_max_blocks=w.exact_table.shape[1],
+            exact_num_blocks=max(1, w.exact_pool_blocks), k_codes=ptr(P.kc), v_codes=ptr(P.vc),
+            k_scales=ptr(P.ks), v_scales=ptr(P.vs), quant_table=ptr(self.quant_table),
+            quant_lengths=ptr(self.quant_len), quant_max_blocks=w.quant_table.shape[1],
+            quant_num_blocks=max(1, w.quant_pool_blocks))
+
+    def read_exact(self, b: int, replica: int = 0):
+        """Logical exact tier (K, V), bf16 bits [n, Hkv, d] each, of sequence b as the
+        device holds it now (its current length and block-table row)."""
+        n = int(self.exact_len[b].item())
+        table = self.exact_table[b].cpu().numpy()
+        P = self.pools[replica]
+        ek = P.ek.cpu().numpy().view(np.uint16)   # [blocks, Hkv, 64, d]
+        ev = P.ev.cpu().numpy().view(np.uint16)   # [blocks, Hkv, 2, d, 32]
+        tok = np.arange(n)
+        blk, r = table[tok // BLOCK], tok % BLOCK
+        return ek[blk, :, r, :], ev[blk, :, r // (BLOCK // 2), :, r % (BLOCK // 2)]
 
     def compress_desc(self, b: int, src_start: int, n: int, dst_start: int, replica: int = 0) -> akv.CompressDesc:
         """Descriptor moving exact tokens [src_start, +n) of sequence b to compressed [dst_start, +n)."""

@@ -36,7 +36,7 @@ BLOCK = 64  # tokens per paged block
 
 _STREAMS = (
     "q", "k_exact", "v_exact", "k_quant", "v_quant", "k_chunk", "v_chunk",
-    "outliers", "table_exact", "table_quant", "lengths",
+    "outliers", "table_exact", "table_quant", "lengths", "k_step", "v_step",
 )
 
 
@@ -165,11 +165,13 @@ def make_small(name: str, seed: int = 0, **kw) -> Workload:
     return _decode(name, seed, B=B, Hq=kw.get("Hq", 32), Hkv=kw.get("Hkv", 4), d=kw.get("d", 128),
                    quant=quant, exact=exact, outlier_frac=kw.get("outlier_frac", 0.0),
                    split_exact=kw.get("split_exact", 0), split_quant=kw.get("split_quant", 0),
-                   Tq=kw.get("Tq", 1), causal_tail=kw.get("causal_tail", 0))
+                   Tq=kw.get("Tq", 1), causal_tail=kw.get("causal_tail", 0),
+                   reserve_exact=kw.get("reserve_exact"), reserve_quant=kw.get("reserve_quant"))
 
 
 def _decode(name, seed, B, Hq, Hkv, d, quant, exact, outlier_frac=0.0,
-            split_exact=0, split_quant=0, Tq=1, causal_tail=0) -> Workload:
+            split_exact=0, split_quant=0, Tq=1, causal_tail=0, reserve_exact=None,
+            reserve_quant=None) -> Workload:
     out_k = out_v = None
     if outlier_frac > 0:
         orng = stream(seed, "outliers")
@@ -183,8 +185,10 @@ def _decode(name, seed, B, Hq, Hkv, d, quant, exact, outlier_frac=0.0,
     qv = [_normal_bf16(rv, n, Hkv, d, out_v) for n in quant]
     xk = [_normal_bf16(ek, n, Hkv, d, out_k) for n in exact]
     xv = [_normal_bf16(ev, n, Hkv, d, out_v) for n in exact]
-    et, ep = _deal_tables(stream(seed, "table_exact"), exact, [0] * B)
-    qt, qp = _deal_tables(stream(seed, "table_quant"), quant, [0] * B)
+    # reserve_*[b]: extra blocks at the end of sequence b's table row (room for
+    # tokens appended or moved there later)
+    et, ep = _deal_tables(stream(seed, "table_exact"), exact, reserve_exact or [0] * B)
+    qt, qp = _deal_tables(stream(seed, "table_quant"), quant, reserve_quant or [0] * B)
     notes = {}
     if out_k is not None:
         notes["outliers_k"] = out_k.tolist()
@@ -229,6 +233,13 @@ def contiguous(w: Workload) -> Workload:
     c.exact_table = ident(w.exact_table)
     c.quant_table = ident(w.quant_table)
     return c
+
+
+def step_tokens(seed: int, steps: int, B: int, Hkv: int, d: int):
+    """New keys and values of `steps` decode steps: bf16 [steps, B, Hkv, d] each."""
+    k = _normal_bf16(stream(seed, "k_step"), steps * B, Hkv, d).reshape(steps, B, Hkv, d)
+    v = _normal_bf16(stream(seed, "v_step"), steps * B, Hkv, d).reshape(steps, B, Hkv, d)
+    return k, v
 
 
 WORKLOADS = ("tiny", "exact32k", "hybrid128k", "ragged", "chunk")

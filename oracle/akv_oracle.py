@@ -416,3 +416,37 @@ def reference_outputs(w, encoded_k=None, encoded_v=None, heads=None, seqs=None):
                                  causal_tail=w.causal_tail, heads=heads)
         o[b], lse[b] = ob, lb
     return o, lse
+
+
+# ------------------------------------------------------------ per-step bookkeeping
+
+def append_evict_step(exact_k: np.ndarray, exact_v: np.ndarray, quant_k: np.ndarray, quant_v: np.ndarray,
+                      new_k: np.ndarray, new_v: np.ndarray, window: int, exact_capacity: int,
+                      quant_capacity: int):
+    """One decode step of a sequence's two-tier history, on logical token lists.
+
+    ActiveKV ("Context beyond VRAM", "What I built") appends each step's new
+    key/value to the recent exact window and keeps the older history in the
+    compact tier.  Tiers are token-ordered bf16 arrays [n, Hkv, d]; the
+    compressed tier is held as its values before encoding (encoding is per
+    token, so the codes of a moved token are ``encode`` of its bf16 values).
+
+    The new token goes to the end of the exact tier.  When the exact tier then
+    holds window + 64 tokens, the compressed tier has room for 64 more and its
+    length is even (two tokens share a value-code byte), the 64 oldest exact
+    tokens move, in order, to the end of the compressed tier.  Capacities are
+    in tokens.  Returns the four new arrays, or None when the exact tier has no
+    room for the new token.
+    """
+    n = exact_k.shape[0]
+    if n + 1 > exact_capacity:
+        return None
+    ek = np.concatenate([exact_k, new_k[None]], axis=0)
+    ev = np.concatenate([exact_v, new_v[None]], axis=0)
+    qk, qv = quant_k, quant_v
+    m = qk.shape[0]
+    if n + 1 >= window + 64 and m + 64 <= quant_capacity and m % 2 == 0:
+        qk = np.concatenate([qk, ek[:64]], axis=0)
+        qv = np.concatenate([qv, ev[:64]], axis=0)
+        ek, ev = ek[64:], ev[64:]
+    return ek, ev, qk, qv

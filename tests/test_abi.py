@@ -41,7 +41,7 @@ def test_abi_version_and_exports():
     names = akv.header_functions()
     assert set(names) == {"akv_abi_version", "akv_last_error", "akv_decode_workspace_bytes",
                           "akv_chunk_workspace_bytes", "akv_attend_decode", "akv_attend_chunk",
-                          "akv_split_plan", "akv_lse_merge", "akv_compress_evicted"}
+                          "akv_split_plan", "akv_lse_merge", "akv_compress_evicted", "akv_append_evict"}
     for n in names:
         assert hasattr(akv.LIB, n), n
 
@@ -246,3 +246,31 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     import pytest as _pytest
     with _pytest.raises(ImportError):
         akv._load()
+
+
+def append_desc(**over):
+    kw = dict(B=2, Hkv=4, d=128, window=128, new_k=FAKE + 0x100, new_v=FAKE + 0x200, exact_k=FAKE,
+              exact_v=FAKE + 0x1000000, exact_table=FAKE + 0x2000000, exact_lengths=FAKE + 0x2100000,
+              exact_max_blocks=3, exact_num_blocks=6, k_codes=FAKE + 0x3000000, v_codes=FAKE + 0x4000000,
+              k_scales=FAKE + 0x5000000, v_scales=FAKE + 0x5800000, quant_table=FAKE + 0x6000000,
+              quant_lengths=FAKE + 0x6100000, quant_max_blocks=4, quant_num_blocks=8)
+    kw.update(over)
+    return akv.AppendDesc(**kw)
+
+
+def test_append_evict_validation_order():
+    """Refusals happen on the host before anything is enqueued (no GPU needed)."""
+    assert akv.LIB.akv_append_evict(None, None) == akv.AKV_ERR_NULL
+    assert akv.akv_append_evict(append_desc(new_k=0)) == akv.AKV_ERR_NULL
+    assert akv.akv_append_evict(append_desc(quant_lengths=0, window=100)) == akv.AKV_ERR_NULL  # NULL first
+    assert akv.akv_append_evict(append_desc(window=100)) == akv.AKV_ERR_SHAPE
+    assert akv.akv_append_evict(append_desc(window=0)) == akv.AKV_ERR_SHAPE
+    assert akv.akv_append_evict(append_desc(window=192)) == akv.AKV_ERR_SHAPE  # needs 4 exact-table entries
+    assert akv.akv_append_evict(append_desc(B=0)) == akv.AKV_ERR_SHAPE
+    assert akv.akv_append_evict(append_desc(d=96)) == akv.AKV_ERR_UNSUPPORTED
+    assert akv.akv_append_evict(append_desc(d=96, window=100)) == akv.AKV_ERR_SHAPE  # SHAPE before UNSUPPORTED
+    assert akv.akv_append_evict(append_desc(B=40000)) == akv.AKV_ERR_UNSUPPORTED
+    assert akv.akv_append_evict(append_desc(exact_lengths=FAKE + 2)) == akv.AKV_ERR_ALIGN
+    d = append_desc()
+    d.struct_size = 8
+    assert akv.akv_append_evict(d) == akv.AKV_ERR_SHAPE

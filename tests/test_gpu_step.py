@@ -1,0 +1,129 @@
+"""GPU parity of the fused per-step append / evict (akv_append_evict).
+
+Decode steps are run on the device; the oracle replays the same steps on
+logical token lists (oracle.append_evict_step).  Afterwards the device's
+lengths must equal the oracle's, the exact tier read back through the
+device's (rotated) block table must equal the oracle's exact tokens bit for
+bit, the compressed codes and scales must equal the oracle's encoding of the
+moved tokens bit for bit, and attention over the new state must meet the
+decode tolerance against the oracle's attention over the oracle's history.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import akv_oracle as O
+from long_context_kv_split_amd import synth
+
+from test_gpu_parity import _mods, _say, assert_attention
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    _mods()
+
+
+def _replay(w, nk, nv, window, b, steps):
+    """Oracle: the steps on sequence b's logical tiers; None once a step is refused."""
+    ek, ev = w.exact_k[b], w.exact_v[b]
+    qk, qv = w.quant_k_src[b], w.quant_v_src[b]
+    ecap = int(w.exact_table.shape[1]) * synth.BLOCK
+    qcap = int((w.quant_table[b] >= 0).sum()) * synth.BLOCK
+    for t in range(steps):
+        r = O.append_evict_step(ek, ev, qk, qv, nk[t, b], nv[t, b], window, ecap, qcap)
+        if r is None:
+            return None
+        ek, ev, qk, qv = r
+    return ek, ev, qk, qv
+
+
+def _run_steps(dw, nk, nv, window, steps):
+    akv, harness = _mods()
+    dk = torch.from_numpy(nk.view(np.int16)).cuda()
+    dv = torch.from_numpy(nv.view(np.int16)).cuda()
+    for t in range(steps):
+        akv.check(akv.akv_append_evict(dw.append_desc(window, dk[t], dv[t]), harness.stream_handle()))
+    torch.cuda.synchronize()
+
+
+def _check_state(dw, w, nk, nv, window, steps, label):
+    """Compare the device tiers with the oracle replay; returns the oracle tiers per sequence."""
+    ref = []
+    for b in range(w.B):
+        r = _replay(w, nk, nv, window, b, steps)
+        n_dev, m_dev = int(dw.exact_len[b].item()), int(dw.quant_len[b].item())
+        if r is None:
+            assert n_dev == -1, f"{label} seq {b}: a refused step must leave length -1, got {n_dev}"
+            ref.append(None)
+            continue
+        ek, ev, qk, qv = r
+        assert (n_dev, m_dev) == (ek.shape[0], qk.shape[0]), f"{label} seq {b}: lengths"
+        gk, gv = dw.read_exact(b)
+        assert np.array_equal(gk, ek) and np.array_equal(gv, ev), f"{label} seq {b}: exact tier bytes"
+        kc, ks = O.encode(qk)
+        vc, vs = O.encode(qv)
+        if qk.shape[0]:
+            ck, cks, cv, cvs = dw.read_codes(b, 0, qk.shape[0])
+            assert np.array_equal(ck, kc) and np.array_equal(cks, ks), f"{label} seq {b}: K codes / scales"
+            assert np.array_equal(cv, vc) and np.array_equal(cvs, vs), f"{label} seq {b}: V codes / scales"
+        ref.append((ek, ev, kc, ks, vc, vs))
+        _say(f"{label} seq {b}: exact {n_dev} compressed {m_dev} tokens bit-exact")
+    return ref
+
+
+def _check_attention(dw, w, ref, label):
+    akv, _ = _mods()
+    dw.o.fill_(float("nan"))
+    akv.check(dw.attend())
+    torch.cuda.synchronize()
+    o, lse = dw.o.cpu().numpy(), dw.lse.cpu().numpy()
+    for b, r in enumerate(ref):
+        if r is None:
+            assert np.all(np.isnan(o[b])) and np.all(np.isnan(lse[b])), f"{label} seq {b}: expected NaN"
+            continue
+        ek, ev, kc, ks, vc, vs = r
+        o_ref, lse_ref = O.decode_sequence(w.q[b], ek, ev, kc, ks, vc, vs)
+        assert_attention(o[b], lse[b], o_ref, lse_ref, f"{label} seq {b}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_append_evict_steps_match_oracle(d):
+    """70 steps, window 128: sequences start 60, 10 and 63 tokens into the
+    block above the window, so they move blocks at different steps (one of
+    them twice, one into an empty compressed tier)."""
+    W, S = 128, 70
+    w = synth.make_small("step", B=3, Hq=8, Hkv=2, d=d, quant=[100, 0, 64], exact=[W + 60, W + 10, W + 63],
+                         reserve_quant=[2, 2, 2])
+    akv, harness = _mods()
+    _say(f"append/evict d={d}: B=3 exact {list(w.exact_len)} compressed {list(w.quant_len)} window {W}")
+    dw = harness.DeviceWorkload(w)
+    nk, nv = synth.step_tokens(0, S, w.B, w.Hkv, w.d)
+    _run_steps(dw, nk, nv, W, 30)
+    _check_state(dw, w, nk, nv, W, 30, f"d={d} after 30 steps")
+    _run_steps_from(dw, nk, nv, W, 30, S)
+    ref = _check_state(dw, w, nk, nv, W, S, f"d={d} after {S} steps")
+    _check_attention(dw, w, ref, f"d={d} attention after {S} steps")
+
+
+def _run_steps_from(dw, nk, nv, window, t0, t1):
+    _run_steps(dw, nk[t0:t1], nv[t0:t1], window, t1 - t0)
+
+
+def test_append_evict_full_tiers():
+    """Sequence 0: the compressed tier is full, so the window grows until the
+    exact table is full, then the step is refused (length -1, NaN outputs).
+    Sequence 1 is unaffected."""
+    W, S = 128, 4
+    w = synth.make_small("step_full", B=2, Hq=8, Hkv=2, d=128, quant=[128, 50], exact=[W + 62, W + 20],
+                         reserve_quant=[0, 1])
+    akv, harness = _mods()
+    dw = harness.DeviceWorkload(w)
+    nk, nv = synth.step_tokens(1, S, w.B, w.Hkv, w.d)
+    _run_steps(dw, nk, nv, W, S)
+    ref = _check_state(dw, w, nk, nv, W, S, "full tiers")
+    assert ref[0] is None and ref[1] is not None
+    _check_attention(dw, w, ref, "full tiers attention")

@@ -445,3 +445,81 @@ def test_generator_is_deterministic_and_shaped():
     assert list(a.quant_len) == [384] and list(a.exact_len) == [128]
     assert a.kv_bytes() == 60416
     assert sorted(a.exact_table[0][a.exact_table[0] >= 0].tolist()) == [0, 1]
+
+
+# ------------------------------------------------------------ per-step append / evict
+
+def _tokens(rng, n, hkv=2, d=64):
+    return O_bits(rng.standard_normal((n, hkv, d)))
+
+
+def O_bits(x):
+    from long_context_kv_split_amd.synth import f64_to_bf16_bits
+    return f64_to_bf16_bits(x)
+
+
+def _run_steps(ek, ev, qk, qv, new_k, new_v, window, ecap, qcap):
+    lens = []
+    for t in range(new_k.shape[0]):
+        r = O.append_evict_step(ek, ev, qk, qv, new_k[t], new_v[t], window, ecap, qcap)
+        if r is None:
+            lens.append(None)
+            break
+        ek, ev, qk, qv = r
+        lens.append((ek.shape[0], qk.shape[0]))
+    return ek, ev, qk, qv, lens
+
+
+@pytest.mark.parametrize("e0", [128, 150, 191])
+def test_append_evict_lengths_closed_form(e0):
+    """With room everywhere the exact tier cycles through [W, W + 63] and every
+    64th append moves one block: after t steps it holds W + (e0 - W + t) mod 64
+    tokens and the compressed tier q0 + 64 * floor((e0 - W + t) / 64)."""
+    rng = np.random.default_rng(1)
+    W, q0, T = 128, 40, 150
+    ek, ev = _tokens(rng, e0), _tokens(rng, e0)
+    qk, qv = _tokens(rng, q0), _tokens(rng, q0)
+    nk, nv = _tokens(rng, T), _tokens(rng, T)
+    *_, lens = _run_steps(ek, ev, qk, qv, nk, nv, W, 10 ** 6, 10 ** 6)
+    for t, (ne, nq) in enumerate(lens, start=1):
+        assert ne == W + (e0 - W + t) % 64
+        assert nq == q0 + 64 * ((e0 - W + t) // 64)
+
+
+def test_append_evict_conserves_the_history_order():
+    """Compressed tier then exact tier, concatenated, is the initial history
+    followed by every appended token, in order."""
+    rng = np.random.default_rng(2)
+    ek, ev, qk, qv = _tokens(rng, 190), _tokens(rng, 190), _tokens(rng, 64), _tokens(rng, 64)
+    nk, nv = _tokens(rng, 100), _tokens(rng, 100)
+    fk, fv, gk, gv, _ = _run_steps(ek, ev, qk, qv, nk, nv, 128, 10 ** 6, 10 ** 6)
+    assert np.array_equal(np.concatenate([gk, fk]), np.concatenate([qk, ek, nk]))
+    assert np.array_equal(np.concatenate([gv, fv]), np.concatenate([qv, ev, nv]))
+    assert gk.shape[0] > qk.shape[0]
+
+
+def test_append_evict_full_or_odd_compressed_tier_keeps_growing_the_window():
+    rng = np.random.default_rng(3)
+    ek, ev = _tokens(rng, 191), _tokens(rng, 191)
+    nk, nv = _tokens(rng, 5), _tokens(rng, 5)
+    # compressed tier at capacity: nothing moves, the exact tier grows by one per step
+    qk, qv = _tokens(rng, 100), _tokens(rng, 100)
+    fk, _, gk, _, lens = _run_steps(ek, ev, qk, qv, nk, nv, 128, 10 ** 6, 120)
+    assert [l[0] for l in lens] == [192, 193, 194, 195, 196] and gk.shape[0] == 100
+    # odd compressed length: two tokens would share a value byte across calls
+    qk, qv = _tokens(rng, 99), _tokens(rng, 99)
+    *_, lens = _run_steps(ek, ev, qk, qv, nk, nv, 128, 10 ** 6, 10 ** 6)
+    assert [l[1] for l in lens] == [99] * 5
+    # exact tier at capacity: the step is refused
+    assert O.append_evict_step(ek, ev, qk, qv, nk[0], nv[0], 128, 191, 10 ** 6) is None
+
+
+def test_encoding_is_per_token():
+    """The codes of tokens moved between tiers are encode() of their own values:
+    encoding a concatenation equals concatenating the encodings."""
+    rng = np.random.default_rng(4)
+    a, b = _tokens(rng, 7, 2, 128), _tokens(rng, 9, 2, 128)
+    ca, sa = O.encode(a)
+    cb, sb = O.encode(b)
+    cab, sab = O.encode(np.concatenate([a, b]))
+    assert np.array_equal(cab, np.concatenate([ca, cb])) and np.array_equal(sab, np.concatenate([sa, sb]))
