@@ -173,6 +173,37 @@ def bench_step(stream, steps=640, warmup=64):
     return out
 
 
+def bench_checkpoint(dw, n_rep, stream, steps=60, warmup=5):
+    """akv_checkpoint_save / _restore of the hybrid128k context (one image per
+    input replica, so neither side is served from the 256 MB cache)."""
+    import torch
+    from long_context_kv_split_amd import akv
+    descs = [dw.context_desc(r) for r in range(n_rep)]
+    nbytes = akv.akv_checkpoint_bytes(descs[0])
+    imgs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n_rep)]
+    h = stream.cuda_stream
+
+    def save(r):
+        st = akv.akv_checkpoint_save(descs[r], imgs[r].data_ptr(), h)
+        if st:
+            akv.check(st)
+
+    def restore(r):
+        st = akv.akv_checkpoint_restore(descs[r], imgs[r].data_ptr(), h)
+        if st:
+            akv.check(st)
+
+    sv, _ = time_calls(save, n_rep, warmup, steps, stream)
+    rs, _ = time_calls(restore, n_rep, warmup, steps, stream)
+    moved = 2 * nbytes  # each side reads and writes about one image
+    return {"workload": "hybrid128k context (123,904 compressed + 4,096 exact tokens, Hq 32 / Hkv 4, d 128)",
+            "image_bytes": nbytes, "save_us": sv * 1e3, "restore_us": rs * 1e3,
+            "save_gbps": moved / (sv * 1e-3) / 1e9, "restore_gbps": moved / (rs * 1e-3) / 1e9,
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac_save": moved / (sv * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "frac_restore": moved / (rs * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
+
+
 def chunk_flops(w) -> float:
     """QK^T + PV multiply-adds x 2 of one chunk call: every query sees the whole
     history before the chunk plus, causally, (Tq + 1) / 2 chunk tokens on average."""
@@ -262,6 +293,9 @@ def main():
                              "kv_gbps": b2 / (e2 * 1e-3) / 1e9, "replicas": r2,
                              "decode_tokens_per_s": w2.B / (e2 * 1e-3)}
                 log(f"bench: {name} {e2 * 1e3:.2f} us/call")
+        ckpt = bench_checkpoint(dw, n_rep, stream)
+        log(f"bench: checkpoint save {ckpt['save_us']:.1f} us, restore {ckpt['restore_us']:.1f} us "
+            f"({ckpt['image_bytes']} B image)")
         log("bench: per-step append / evict")
         step = bench_step(stream)
         log("bench: step " + ", ".join(f"{k} {v['us_per_step']:.2f} us" for k, v in step.items()))
@@ -315,6 +349,7 @@ def main():
         "cpu_baseline": cpu,
         "kernel_source_hash": khash,
     }
+    out["checkpoint"] = ckpt
     out["step"] = {"workload": "akv_append_evict per decode step, Hkv 4, d 128 (B1: window 4096; "
                            "B32: window 2048); one block move per sequence every 64 steps", **step}
     if chunk:

@@ -301,6 +301,57 @@ typedef struct akv_append_desc {
 
 akv_status akv_append_evict(const akv_append_desc* desc, void* stream);
 
+/* Context checkpoint (ActiveKV, "Context beyond VRAM", "What I built": a long
+ * context is suspended and resumed without recomputing it).  The image of a
+ * batch is a fixed-size byte string, every field little-endian:
+ *   [0, 256)   header: "AKVCTX01" (8 bytes), then int32 B, Hkv, d,
+ *              exact_max_blocks, quant_max_blocks, zeros up to 256;
+ *   [256, 256 + 8B) int32 exact_lengths[b], quant_lengths[b] for b = 0..B-1,
+ *              zeros up to the next multiple of 256 (offset E);
+ *   at E:      for b, then slot j < exact_max_blocks: the exact block of
+ *              tokens [64j, 64j + 64) as Hkv K slabs then Hkv V slabs
+ *              (256*Hkv*d bytes, pool layouts above);
+ *   then:      for b, then slot j < quant_max_blocks: K codes, V codes
+ *              (32*d*Hkv bytes each), K scales, V scales (4*d*Hkv bytes each).
+ * Slots at or past ceil(length / 64) are zeros, as are the bytes of a slot
+ * whose table entry is outside [0, num_blocks).  The image depends only on
+ * the tokens (not on which pool blocks hold them), so a context restored into
+ * another block placement attends bit-identically. */
+typedef struct akv_context_desc {
+  uint32_t struct_size;        /* sizeof(akv_context_desc) */
+  int32_t B, Hkv, d;
+  uint16_t* exact_k;           /* exact-tier pools (layouts above) */
+  uint16_t* exact_v;
+  const int32_t* exact_table;  /* [B][exact_max_blocks] */
+  int32_t* exact_lengths;      /* [B] */
+  int32_t exact_max_blocks, exact_num_blocks;
+  uint8_t* k_codes;            /* compressed-tier pools (layouts above) */
+  uint8_t* v_codes;
+  uint16_t* k_scales;
+  uint16_t* v_scales;
+  const int32_t* quant_table;  /* [B][quant_max_blocks] */
+  int32_t* quant_lengths;      /* [B] */
+  int32_t quant_max_blocks, quant_num_blocks;
+} akv_context_desc;
+
+/* Bytes of the image for desc's shape; 0 if desc is invalid. */
+size_t akv_checkpoint_bytes(const akv_context_desc* desc);
+
+/* Write the image of the batch into `image` (any memory the device can write:
+ * HBM, or mapped pinned host memory; 256-byte aligned, at least
+ * akv_checkpoint_bytes(desc) bytes).  Reads the pools, tables and lengths;
+ * writes nothing else.  One gather kernel. */
+akv_status akv_checkpoint_save(const akv_context_desc* desc, void* image, void* stream);
+
+/* Restore an image into the pool blocks that desc's tables name (which may
+ * differ from the saved placement): the slots below each saved length are
+ * copied to their blocks, then the lengths are set.  An image whose header
+ * does not match desc's shape, or a table entry outside [0, num_blocks),
+ * sets that batch's (or sequence's) exact length to -1, so its attention is
+ * NaN.  One scatter kernel; desc's pools, tables and lengths must not be in
+ * use by other work while it runs. */
+akv_status akv_checkpoint_restore(const akv_context_desc* desc, const void* image, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

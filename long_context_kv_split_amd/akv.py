@@ -83,6 +83,17 @@ class AppendDesc(ctypes.Structure):
         super().__init__(struct_size=ctypes.sizeof(AppendDesc), **kw)
 
 
+class ContextDesc(ctypes.Structure):
+    _fields_ = [("struct_size", c_uint32), ("B", c_int32), ("Hkv", c_int32), ("d", c_int32),
+                ("exact_k", c_void_p), ("exact_v", c_void_p), ("exact_table", c_void_p), ("exact_lengths", c_void_p),
+                ("exact_max_blocks", c_int32), ("exact_num_blocks", c_int32), ("k_codes", c_void_p),
+                ("v_codes", c_void_p), ("k_scales", c_void_p), ("v_scales", c_void_p), ("quant_table", c_void_p),
+                ("quant_lengths", c_void_p), ("quant_max_blocks", c_int32), ("quant_num_blocks", c_int32)]
+
+    def __init__(self, **kw):
+        super().__init__(struct_size=ctypes.sizeof(ContextDesc), **kw)
+
+
 class AKVError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -123,6 +134,12 @@ def _load() -> ctypes.CDLL:
     lib.akv_compress_evicted.argtypes = [P(CompressDesc), c_void_p]
     lib.akv_append_evict.restype = ctypes.c_int
     lib.akv_append_evict.argtypes = [P(AppendDesc), c_void_p]
+    lib.akv_checkpoint_bytes.restype = c_size_t
+    lib.akv_checkpoint_bytes.argtypes = [P(ContextDesc)]
+    for name in ("akv_checkpoint_save", "akv_checkpoint_restore"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P(ContextDesc), c_void_p, c_void_p]
     return lib
 
 
@@ -184,3 +201,15 @@ def check(status: int) -> None:
 
 def akv_append_evict(desc: AppendDesc, stream: int = 0) -> int:
     return LIB.akv_append_evict(ctypes.byref(desc), stream)
+
+
+def akv_checkpoint_bytes(desc: ContextDesc) -> int:
+    return LIB.akv_checkpoint_bytes(ctypes.byref(desc))
+
+
+def akv_checkpoint_save(desc: ContextDesc, image: int, stream: int = 0) -> int:
+    return LIB.akv_checkpoint_save(ctypes.byref(desc), image, stream)
+
+
+def akv_checkpoint_restore(desc: ContextDesc, image: int, stream: int = 0) -> int:
+    return LIB.akv_checkpoint_restore(ctypes.byref(desc), image, stream)

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libakv.so")
-SOURCES = ["akv_api.hip", "akv_decode.hip", "akv_chunk.hip", "akv_compress.hip"]
+SOURCES = ["akv_api.hip", "akv_decode.hip", "akv_chunk.hip", "akv_compress.hip", "akv_context.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -20,6 +20,10 @@ hipError_t launch_lse_merge(const float* op, const float* lp, int P, int R, int 
                             hipStream_t stream);
 hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream);
 hipError_t launch_append_evict(const akv_append_desc* d, hipStream_t stream);
+hipError_t launch_ctx_save(const akv_context_desc* d, void* image, hipStream_t stream);
+hipError_t launch_ctx_restore(const akv_context_desc* d, const void* image, hipStream_t stream);
+void ctx_layout(const akv_context_desc* d, size_t* lens_off, size_t* exact_off, size_t* quant_off, size_t* eslot,
+                size_t* qslot, size_t* total);
 }  // namespace akv
 
 
@@ -308,6 +312,53 @@ akv_status akv_append_evict(const akv_append_desc* d, void* stream) {
       !aligned(d->exact_lengths, 4) || !aligned(d->quant_table, 4) || !aligned(d->quant_lengths, 4))
     return fail(AKV_ERR_ALIGN, "append buffers misaligned");
   return hip_status(akv::launch_append_evict(d, static_cast<hipStream_t>(stream)), "akv_append_evict");
+}
+
+// ---------------------------------------------------------- context checkpoint
+static akv_status check_context(const akv_context_desc* d, const void* image, bool need_image, size_t* bytes) {
+  if (!d) return fail(AKV_ERR_NULL, "descriptor is NULL");
+  if (d->struct_size < sizeof(akv_context_desc))
+    return fail(AKV_ERR_SHAPE, "struct_size %u < %zu", d->struct_size, sizeof(akv_context_desc));
+  if (!d->exact_lengths || !d->quant_lengths) return fail(AKV_ERR_NULL, "a lengths pointer is NULL");
+  if (d->exact_max_blocks > 0 && (!d->exact_k || !d->exact_v || !d->exact_table))
+    return fail(AKV_ERR_NULL, "exact tier present but a pointer is NULL");
+  if (d->quant_max_blocks > 0 && (!d->k_codes || !d->v_codes || !d->k_scales || !d->v_scales || !d->quant_table))
+    return fail(AKV_ERR_NULL, "compressed tier present but a pointer is NULL");
+  if (need_image && !image) return fail(AKV_ERR_NULL, "image is NULL");
+  if (d->B < 1 || d->Hkv < 1 || d->d < 1 || d->exact_max_blocks < 0 || d->quant_max_blocks < 0)
+    return fail(AKV_ERR_SHAPE, "context sizes out of range");
+  if ((d->exact_max_blocks > 0 && d->exact_num_blocks < 1) || (d->quant_max_blocks > 0 && d->quant_num_blocks < 1))
+    return fail(AKV_ERR_SHAPE, "a present tier needs num_blocks >= 1");
+  if (d->d != 64 && d->d != 128) return fail(AKV_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  if (d->B > 65535 || d->exact_max_blocks > (1 << 30) || d->quant_max_blocks > (1 << 30))
+    return fail(AKV_ERR_UNSUPPORTED, "B must be <= 65535");
+  if (!aligned(d->exact_k, 16) || !aligned(d->exact_v, 16) || !aligned(d->k_codes, 16) || !aligned(d->v_codes, 16) ||
+      !aligned(d->k_scales, 16) || !aligned(d->v_scales, 16) || !aligned(d->exact_table, 4) ||
+      !aligned(d->quant_table, 4) || !aligned(d->exact_lengths, 4) || !aligned(d->quant_lengths, 4))
+    return fail(AKV_ERR_ALIGN, "pools must be 16-byte aligned, tables and lengths 4-byte");
+  if (need_image && !aligned(image, 256)) return fail(AKV_ERR_ALIGN, "image must be 256-byte aligned");
+  size_t lo, eo, qo, es, qs;
+  akv::ctx_layout(d, &lo, &eo, &qo, &es, &qs, bytes);
+  return AKV_OK;
+}
+
+size_t akv_checkpoint_bytes(const akv_context_desc* desc) {
+  size_t n = 0;
+  return check_context(desc, nullptr, false, &n) == AKV_OK ? n : 0;
+}
+
+akv_status akv_checkpoint_save(const akv_context_desc* desc, void* image, void* stream) {
+  size_t n = 0;
+  akv_status s = check_context(desc, image, true, &n);
+  if (s != AKV_OK) return s;
+  return hip_status(akv::launch_ctx_save(desc, image, static_cast<hipStream_t>(stream)), "akv_checkpoint_save");
+}
+
+akv_status akv_checkpoint_restore(const akv_context_desc* desc, const void* image, void* stream) {
+  size_t n = 0;
+  akv_status s = check_context(desc, image, true, &n);
+  if (s != AKV_OK) return s;
+  return hip_status(akv::launch_ctx_restore(desc, image, static_cast<hipStream_t>(stream)), "akv_checkpoint_restore");
 }
 
 }  // extern "C"

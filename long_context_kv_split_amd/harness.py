@@ -154,6 +154,17 @@ class DeviceWorkload:
             quant_lengths=ptr(self.quant_len), quant_max_blocks=w.quant_table.shape[1],
             quant_num_blocks=max(1, w.quant_pool_blocks))
 
+    def context_desc(self, replica: int = 0) -> akv.ContextDesc:
+        """Descriptor of this workload's device state for checkpoint save / restore."""
+        w, P = self.w, self.pools[replica]
+        return akv.ContextDesc(
+            B=w.B, Hkv=w.Hkv, d=w.d, exact_k=ptr(P.ek), exact_v=ptr(P.ev), exact_table=ptr(self.exact_table),
+            exact_lengths=ptr(self.exact_len), exact_max_blocks=self.emax,
+            exact_num_blocks=max(1, w.exact_pool_blocks), k_codes=ptr(P.kc), v_codes=ptr(P.vc),
+            k_scales=ptr(P.ks), v_scales=ptr(P.vs), quant_table=ptr(self.quant_table),
+            quant_lengths=ptr(self.quant_len), quant_max_blocks=self.qmax,
+            quant_num_blocks=max(1, w.quant_pool_blocks))
+
     def read_exact(self, b: int, replica: int = 0):
         """Logical exact tier (K, V), bf16 bits [n, Hkv, d] each, of sequence b as the
         device holds it now (its current length and block-table row)."""

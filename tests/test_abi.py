@@ -41,7 +41,8 @@ def test_abi_version_and_exports():
     names = akv.header_functions()
     assert set(names) == {"akv_abi_version", "akv_last_error", "akv_decode_workspace_bytes",
                           "akv_chunk_workspace_bytes", "akv_attend_decode", "akv_attend_chunk",
-                          "akv_split_plan", "akv_lse_merge", "akv_compress_evicted", "akv_append_evict"}
+                          "akv_split_plan", "akv_lse_merge", "akv_compress_evicted", "akv_append_evict",
+                          "akv_checkpoint_bytes", "akv_checkpoint_save", "akv_checkpoint_restore"}
     for n in names:
         assert hasattr(akv.LIB, n), n
 
@@ -274,3 +275,32 @@ def test_append_evict_validation_order():
     d = append_desc()
     d.struct_size = 8
     assert akv.akv_append_evict(d) == akv.AKV_ERR_SHAPE
+
+
+def context_desc(**over):
+    kw = dict(B=3, Hkv=4, d=128, exact_k=FAKE, exact_v=FAKE + 0x1000000, exact_table=FAKE + 0x2000000,
+              exact_lengths=FAKE + 0x2100000, exact_max_blocks=65, exact_num_blocks=200,
+              k_codes=FAKE + 0x3000000, v_codes=FAKE + 0x4000000, k_scales=FAKE + 0x5000000,
+              v_scales=FAKE + 0x5800000, quant_table=FAKE + 0x6000000, quant_lengths=FAKE + 0x6100000,
+              quant_max_blocks=1936, quant_num_blocks=6000)
+    kw.update(over)
+    return akv.ContextDesc(**kw)
+
+
+def test_checkpoint_image_size_and_validation():
+    """The image size is the documented layout: 256-byte header, lengths padded to
+    256, 256*Hkv*d bytes per exact slot and 72*Hkv*d per compressed slot."""
+    d = context_desc()
+    lens_end = 256 + 256                              # 8 * B = 24 bytes, padded
+    expect = lens_end + 3 * 65 * 256 * 4 * 128 + 3 * 1936 * 72 * 4 * 128
+    assert akv.akv_checkpoint_bytes(d) == expect
+    assert akv.akv_checkpoint_bytes(context_desc(quant_max_blocks=0, k_codes=0, v_codes=0, k_scales=0,
+                                                 v_scales=0, quant_table=0)) == lens_end + 3 * 65 * 256 * 512
+    assert akv.akv_checkpoint_bytes(context_desc(d=96)) == 0
+    img = FAKE + 0xB000000
+    assert akv.akv_checkpoint_save(context_desc(exact_lengths=0), img) == akv.AKV_ERR_NULL
+    assert akv.akv_checkpoint_save(context_desc(), 0) == akv.AKV_ERR_NULL
+    assert akv.akv_checkpoint_restore(context_desc(B=0), img) == akv.AKV_ERR_SHAPE
+    assert akv.akv_checkpoint_restore(context_desc(d=96), img) == akv.AKV_ERR_UNSUPPORTED
+    assert akv.akv_checkpoint_restore(context_desc(), img + 16) == akv.AKV_ERR_ALIGN
+    assert akv.akv_checkpoint_save(context_desc(exact_k=FAKE + 8), img) == akv.AKV_ERR_ALIGN
