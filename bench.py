@@ -204,6 +204,48 @@ def bench_checkpoint(dw, n_rep, stream, steps=60, warmup=5):
                          "frac_restore": moved / (rs * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
 
 
+def bench_staged(w, dw, ev_resident_ms, stream, slots=2, slot_mb=32, steps=20, warmup=10):
+    """akv_attend_decode_staged on hybrid128k: the compressed tier (71 MB) in pinned
+    host memory, streamed through a ring of `slots` x `slot_mb` MB on a copy stream."""
+    import torch
+    from long_context_kv_split_amd import akv, harness
+    keep, tiers = dw.host_tiers()
+    ring = torch.empty(slots * (slot_mb << 20), dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    sd, hold = dw.staging(tiers, ring, slots, cs)
+    desc = dw.desc()
+    h = stream.cuda_stream
+    ws, wsb = harness.ptr(dw.ws), dw.ws_bytes
+
+    def call(_):
+        st = akv.akv_attend_decode_staged(desc, sd, ws, wsb, h)
+        if st:
+            akv.check(st)
+
+    ev_ms, wall_ms = time_calls(call, 1, warmup, steps, stream)
+    pcie = sum(int(t.numel()) for t in keep)
+    # the same bytes in one copy: the link's own rate on this host
+    src = torch.cat([t.view(-1) for t in keep]).pin_memory()
+    dst = torch.empty_like(src, device="cuda")
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    copy_ms = (time.perf_counter() - t0) * 1e3 / 5
+    bf16 = int(w.quant_len.sum()) * w.Hkv * 4 * w.d
+    return {"workload": "hybrid128k decode, compressed tier (123,904 tokens) in pinned host memory",
+            "ring": f"{slots} slots x {slot_mb} MiB", "us_per_call": ev_ms * 1e3, "wall_us_per_call": wall_ms * 1e3,
+            "resident_us_per_call": ev_resident_ms * 1e3, "host_to_device_bytes_per_call": pcie,
+            "host_to_device_gbps": pcie / (ev_ms * 1e-3) / 1e9,
+            "plain_copy_gbps": pcie / (copy_ms * 1e-3) / 1e9,
+            "bf16_bytes_same_tokens": bf16, "bytes_saved_vs_bf16": 1.0 - pcie / bf16,
+            "roofline": {"bound": "pcie", "achieved": pcie / (ev_ms * 1e-3) / 1e9,
+                         "peak_measured": pcie / (copy_ms * 1e-3) / 1e9, "unit": "GB/s"}}
+
+
 def chunk_flops(w) -> float:
     """QK^T + PV multiply-adds x 2 of one chunk call: every query sees the whole
     history before the chunk plus, causally, (Tq + 1) / 2 chunk tokens on average."""
@@ -265,6 +307,8 @@ def main():
     ap.add_argument("--aux", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-chunk", action="store_true", help="skip the prefill-chunk line")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the host-staged, checkpoint and per-step legs (decode and chunk only)")
     ap.add_argument("--split-quant", type=int, default=0, help="compressed-tier split tokens (0 = library default)")
     ap.add_argument("--split-exact", type=int, default=0, help="exact-tier split tokens (0 = library default)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -293,12 +337,18 @@ def main():
                              "kv_gbps": b2 / (e2 * 1e-3) / 1e9, "replicas": r2,
                              "decode_tokens_per_s": w2.B / (e2 * 1e-3)}
                 log(f"bench: {name} {e2 * 1e3:.2f} us/call")
-        ckpt = bench_checkpoint(dw, n_rep, stream)
-        log(f"bench: checkpoint save {ckpt['save_us']:.1f} us, restore {ckpt['restore_us']:.1f} us "
-            f"({ckpt['image_bytes']} B image)")
-        log("bench: per-step append / evict")
-        step = bench_step(stream)
-        log("bench: step " + ", ".join(f"{k} {v['us_per_step']:.2f} us" for k, v in step.items()))
+        staged = ckpt = step = None
+        if not args.no_extra:
+            log("bench: host-staged decode")
+            staged = bench_staged(w, dw, ev_ms, stream)
+            log(f"bench: staged {staged['us_per_call']:.0f} us/call, {staged['host_to_device_gbps']:.1f} GB/s "
+                f"(plain copy {staged['plain_copy_gbps']:.1f} GB/s)")
+            ckpt = bench_checkpoint(dw, n_rep, stream)
+            log(f"bench: checkpoint save {ckpt['save_us']:.1f} us, restore {ckpt['restore_us']:.1f} us "
+                f"({ckpt['image_bytes']} B image)")
+            log("bench: per-step append / evict")
+            step = bench_step(stream)
+            log("bench: step " + ", ".join(f"{k} {v['us_per_step']:.2f} us" for k, v in step.items()))
         chunk = None
         if not args.no_chunk:
             log("bench: building chunk workload")
@@ -349,9 +399,11 @@ def main():
         "cpu_baseline": cpu,
         "kernel_source_hash": khash,
     }
-    out["checkpoint"] = ckpt
-    out["step"] = {"workload": "akv_append_evict per decode step, Hkv 4, d 128 (B1: window 4096; "
-                           "B32: window 2048); one block move per sequence every 64 steps", **step}
+    if staged:
+        out["staged"] = staged
+        out["checkpoint"] = ckpt
+        out["step"] = {"workload": "akv_append_evict per decode step, Hkv 4, d 128 (B1: window 4096; "
+                               "B32: window 2048); one block move per sequence every 64 steps", **step}
     if chunk:
         out["chunk"] = chunk
     if aux:

@@ -216,6 +216,33 @@ size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc);
  * out (host memory, 4 int32) is written only on AKV_OK. */
 akv_status akv_split_plan(const akv_attn_desc* desc, int32_t chunk, int32_t* out);
 
+/* One sequence's compressed tier held in pinned host memory (hipHostMalloc):
+ * ceil(length / 64) block records in token order (record i holds tokens
+ * [64i, 64i + 64)), each 72*Hkv*d bytes: Hkv K-code slabs (32*d bytes each),
+ * Hkv V-code slabs, Hkv K-scale slabs (2*d fp16 each), Hkv V-scale slabs,
+ * with the per-slab layouts above.  This is the record layout of a
+ * checkpoint image's compressed slots, so a sequence's slots of an image in
+ * pinned memory serve directly. */
+typedef struct akv_host_tier {
+  const void* blocks;          /* 16-byte aligned */
+  int32_t length;              /* tokens; must equal quant.lengths[b] on the device */
+} akv_host_tier;
+
+/* Staging for akv_attend_decode_staged.  The ring (device memory) is cut
+ * into `slots` equal slots; each holds the blocks of one chunk of whole
+ * compressed splits.  copy_stream and the 2*slots + 1 events are the
+ * caller's (created with hipStreamCreate / hipEventCreate, default priority);
+ * the library only enqueues on them. */
+typedef struct akv_staging_desc {
+  uint32_t struct_size;        /* sizeof(akv_staging_desc) */
+  const akv_host_tier* seqs;   /* host array [B] */
+  void* ring;                  /* device, 256-byte aligned */
+  size_t ring_bytes;
+  int32_t slots;               /* >= 2 */
+  void* copy_stream;           /* hipStream_t of the host-to-device copies */
+  void* const* events;         /* host array of 2*slots + 1 hipEvent_t */
+} akv_staging_desc;
+
 /* Split-KV decode attention, one query token per sequence.
  * Enqueues two kernels: a split kernel in which every (split, kv head,
  * sequence) workgroup attends its split (the compressed tier with the
@@ -228,6 +255,24 @@ akv_status akv_split_plan(const akv_attn_desc* desc, int32_t chunk, int32_t* out
  * akv_decode_workspace_bytes(desc) bytes; calls that overlap in time on one
  * workspace race. */
 akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/* akv_attend_decode with the compressed tier streamed from pinned host memory
+ * (ActiveKV, "Context beyond VRAM", "What I built": the authoritative history
+ * stays in host memory, the GPU keeps a budgeted staging region, and a
+ * staging buffer is reused only after every kernel that read it has
+ * finished).  The exact tier and the query are on the device as in
+ * akv_attend_decode; desc->quant supplies lengths (device, for the merge) and
+ * max_blocks (the split plan), and its pools and table may be NULL.  Per
+ * sequence, runs of whole compressed splits (their records, one
+ * hipMemcpyAsync each) are copied on copy_stream into the next ring slot
+ * while earlier slots are attended on
+ * `stream`; events order each copy after the kernel that last read its slot
+ * and each kernel after its copy.  Same splits, same arithmetic and same
+ * merge as akv_attend_decode, so the outputs are bit-identical to it.  A
+ * ring too small for one split of every tier block size returns
+ * AKV_ERR_WORKSPACE. */
+akv_status akv_attend_decode_staged(const akv_attn_desc* desc, const akv_staging_desc* staging, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Prefill-chunk attention: Tq causal queries per sequence over the two-tier
  * history (the prefill side of ActiveKV's two-tier cache; causal rule in the

@@ -94,6 +94,18 @@ class ContextDesc(ctypes.Structure):
         super().__init__(struct_size=ctypes.sizeof(ContextDesc), **kw)
 
 
+class HostTier(ctypes.Structure):
+    _fields_ = [("blocks", c_void_p), ("length", c_int32)]
+
+
+class StagingDesc(ctypes.Structure):
+    _fields_ = [("struct_size", c_uint32), ("seqs", c_void_p), ("ring", c_void_p), ("ring_bytes", c_size_t),
+                ("slots", c_int32), ("copy_stream", c_void_p), ("events", c_void_p)]
+
+    def __init__(self, **kw):
+        super().__init__(struct_size=ctypes.sizeof(StagingDesc), **kw)
+
+
 class AKVError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -128,6 +140,8 @@ def _load() -> ctypes.CDLL:
         fn.argtypes = [P(AttnDesc), c_void_p, c_size_t, c_void_p]
     lib.akv_split_plan.restype = ctypes.c_int
     lib.akv_split_plan.argtypes = [P(AttnDesc), c_int32, P(c_int32)]
+    lib.akv_attend_decode_staged.restype = ctypes.c_int
+    lib.akv_attend_decode_staged.argtypes = [P(AttnDesc), P(StagingDesc), c_void_p, c_size_t, c_void_p]
     lib.akv_lse_merge.restype = ctypes.c_int
     lib.akv_lse_merge.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.akv_compress_evicted.restype = ctypes.c_int
@@ -213,3 +227,7 @@ def akv_checkpoint_save(desc: ContextDesc, image: int, stream: int = 0) -> int:
 
 def akv_checkpoint_restore(desc: ContextDesc, image: int, stream: int = 0) -> int:
     return LIB.akv_checkpoint_restore(ctypes.byref(desc), image, stream)
+
+
+def akv_attend_decode_staged(desc: AttnDesc, staging: StagingDesc, ws: int, ws_bytes: int, stream: int = 0) -> int:
+    return LIB.akv_attend_decode_staged(ctypes.byref(desc), ctypes.byref(staging), ws, ws_bytes, stream)

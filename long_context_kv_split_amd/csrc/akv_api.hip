@@ -15,6 +15,8 @@
 
 namespace akv {
 hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream);
+hipError_t launch_decode_splits(const AttnParams& p, int D, int splits, int seqs, hipStream_t stream);
+hipError_t launch_decode_merge(const AttnParams& p, int D, hipStream_t stream);
 hipError_t launch_chunk(const AttnParams& p, int D, hipStream_t stream);
 hipError_t launch_lse_merge(const float* op, const float* lp, int P, int R, int d, float* o, float* lse,
                             hipStream_t stream);
@@ -52,8 +54,10 @@ struct Plan {
   size_t ws_bytes;
 };
 
-// Validate an attention descriptor; on success fill the plan.
-akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan) {
+// Validate an attention descriptor; on success fill the plan.  staged: the
+// compressed tier's pools and table live elsewhere (only its lengths and
+// max_blocks are used).
+akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool staged = false) {
   // ---- NULL
   if (!d) return fail(AKV_ERR_NULL, "descriptor is NULL");
   if (d->struct_size < sizeof(akv_attn_desc))
@@ -63,14 +67,15 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan) {
   const akv_quant_tier& q = d->quant;
   if (e.max_blocks > 0 && (!e.k || !e.v || !e.block_table || !e.lengths))
     return fail(AKV_ERR_NULL, "exact tier present but a pointer is NULL");
-  if (q.max_blocks > 0 && (!q.k_codes || !q.v_codes || !q.k_scales || !q.v_scales || !q.block_table || !q.lengths))
+  if (q.max_blocks > 0 && !q.lengths) return fail(AKV_ERR_NULL, "compressed tier present but lengths is NULL");
+  if (!staged && q.max_blocks > 0 && (!q.k_codes || !q.v_codes || !q.k_scales || !q.v_scales || !q.block_table))
     return fail(AKV_ERR_NULL, "compressed tier present but a pointer is NULL");
   // ---- SHAPE
   if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->d < 1 || d->Tq < 1)
     return fail(AKV_ERR_SHAPE, "B, Hq, Hkv, d and Tq must be >= 1");
   if (d->Hq % d->Hkv) return fail(AKV_ERR_SHAPE, "Hq (%d) is not a multiple of Hkv (%d)", d->Hq, d->Hkv);
   if (e.max_blocks < 0 || q.max_blocks < 0) return fail(AKV_ERR_SHAPE, "max_blocks < 0");
-  if ((e.max_blocks > 0 && e.num_blocks < 1) || (q.max_blocks > 0 && q.num_blocks < 1))
+  if ((e.max_blocks > 0 && e.num_blocks < 1) || (!staged && q.max_blocks > 0 && q.num_blocks < 1))
     return fail(AKV_ERR_SHAPE, "a present tier needs num_blocks >= 1");
   if (e.max_blocks == 0 && q.max_blocks == 0) return fail(AKV_ERR_SHAPE, "both tiers are absent");
   if (!(d->softmax_scale >= 0.0f) || !std::isfinite(d->softmax_scale))
@@ -198,6 +203,12 @@ akv::AttnParams make_params(const akv_attn_desc* d, const Plan& plan, void* ws) 
   p.part_lse = reinterpret_cast<float*>(base + po);
   p.o = d->o;
   p.lse = d->lse;
+  p.b0 = 0;
+  p.part_base = 0;
+  p.part_stride = plan.Sq + plan.Se;
+  p.qlen_fixed = -1;
+  p.q_code_stride = (size_t)d->Hkv * 32 * d->d;
+  p.q_scale_stride = (size_t)d->Hkv * 2 * d->d;
   return p;
 }
 
@@ -243,6 +254,149 @@ akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_byte
   if ((s = check_ws(plan, ws, ws_bytes)) != AKV_OK) return s;
   akv::AttnParams p = make_params(desc, plan, ws);
   return hip_status(akv::launch_decode(p, desc->d, static_cast<hipStream_t>(stream)), "akv_attend_decode");
+}
+
+// Validation of the staging descriptor, one category at a time (the caller
+// interleaves the categories with the attention descriptor's).
+akv_status check_staging(const akv_attn_desc* desc, const akv_staging_desc* st, akv_status category) {
+  if (category == AKV_ERR_NULL) {
+    if (!st) return fail(AKV_ERR_NULL, "staging descriptor is NULL");
+    if (st->struct_size >= sizeof(akv_staging_desc)) {
+      if (!st->seqs || !st->ring || !st->copy_stream || !st->events)
+        return fail(AKV_ERR_NULL, "a staging pointer is NULL");
+      for (int i = 0; i < 2 * st->slots + 1 && st->slots >= 2; ++i)
+        if (!st->events[i]) return fail(AKV_ERR_NULL, "staging event %d is NULL", i);
+      const int nb = (desc && desc->struct_size >= sizeof(akv_attn_desc) && desc->B <= 65535) ? desc->B : 0;
+      for (int b = 0; b < nb; ++b) {
+        const akv_host_tier& h = st->seqs[b];
+        if (h.length > 0 && !h.blocks) return fail(AKV_ERR_NULL, "host tier %d: blocks is NULL", b);
+      }
+    }
+  } else if (category == AKV_ERR_SHAPE) {
+    if (st->struct_size < sizeof(akv_staging_desc))
+      return fail(AKV_ERR_SHAPE, "staging struct_size %u < %zu", st->struct_size, sizeof(akv_staging_desc));
+    if (st->slots < 2) return fail(AKV_ERR_SHAPE, "staging needs >= 2 slots");
+    const long long cap = (long long)desc->quant.max_blocks * AKV_BLOCK_TOKENS;
+    for (int b = 0; b < desc->B; ++b)
+      if (st->seqs[b].length < 0 || st->seqs[b].length > cap)
+        return fail(AKV_ERR_SHAPE, "host tier %d: length %d outside [0, %lld]", b, st->seqs[b].length, cap);
+  } else if (category == AKV_ERR_ALIGN) {
+    if (!aligned(st->ring, 256)) return fail(AKV_ERR_ALIGN, "staging ring must be 256-byte aligned");
+    for (int b = 0; b < desc->B; ++b) {
+      const akv_host_tier& h = st->seqs[b];
+      if (h.length > 0 && !aligned(h.blocks, 16))
+        return fail(AKV_ERR_ALIGN, "host tier %d: blocks must be 16-byte aligned", b);
+    }
+  }
+  return AKV_OK;
+}
+
+// Position of a status in the validation order NULL -> SHAPE -> UNSUPPORTED -> ALIGN -> WORKSPACE.
+int status_rank(akv_status s) {
+  switch (s) {
+    case AKV_ERR_NULL: return 0;
+    case AKV_ERR_SHAPE: return 1;
+    case AKV_ERR_UNSUPPORTED: return 2;
+    case AKV_ERR_ALIGN: return 3;
+    case AKV_ERR_WORKSPACE: return 4;
+    default: return 5;
+  }
+}
+
+akv_status akv_attend_decode_staged(const akv_attn_desc* desc, const akv_staging_desc* st, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  Plan plan;
+  // NULL of both descriptors first, then the remaining categories in order
+  akv_status s = check_staging(desc, st, AKV_ERR_NULL);
+  if (s != AKV_OK) {
+    if (!desc) return fail(AKV_ERR_NULL, "descriptor is NULL");
+    return s;
+  }
+  akv_status sa = check_attn(desc, false, &plan, true);
+  if (sa == AKV_ERR_NULL) return sa;
+  const std::string attn_msg = g_err;
+  for (akv_status c : {AKV_ERR_SHAPE, AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN}) {
+    if (sa != AKV_OK && status_rank(sa) <= status_rank(c)) {
+      g_err = attn_msg;
+      return sa;
+    }
+    if ((s = check_staging(desc, st, c)) != AKV_OK) return s;
+  }
+  if (sa != AKV_OK) {
+    g_err = attn_msg;
+    return sa;
+  }
+  if ((s = check_ws(plan, ws, ws_bytes)) != AKV_OK) return s;
+  const akv_quant_tier& q = desc->quant;
+  // ring slots of whole compressed splits; a block is one record of
+  // Hkv*32*d K-code, Hkv*32*d V-code, Hkv*2*d K-scale and Hkv*2*d V-scale bytes / halves
+  const int D = desc->d, H = desc->Hkv;
+  const size_t code_bytes = (size_t)H * 32 * D, scale_bytes = (size_t)H * 4 * D;
+  const size_t block_bytes = 2 * code_bytes + 2 * scale_bytes;
+  const size_t slot_bytes = (st->ring_bytes / st->slots) & ~(size_t)255;
+  const int slot_blocks = (int)std::min<size_t>(slot_bytes / block_bytes, 1 << 30);
+  const int split_blocks = plan.Pq / AKV_BLOCK_TOKENS;
+  const int chunk_splits = slot_blocks / split_blocks;
+  if (q.max_blocks > 0 && chunk_splits < 1)
+    return fail(AKV_ERR_WORKSPACE, "staging slots of %zu bytes hold %d blocks; one split needs %d", slot_bytes,
+                slot_blocks, split_blocks);
+  hipStream_t cs = static_cast<hipStream_t>(stream), xs = static_cast<hipStream_t>(st->copy_stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(st->events));
+  const akv::AttnParams base = make_params(desc, plan, ws);
+  hipError_t e;
+#define AKV_HIP(call)                                          \
+  do {                                                         \
+    if ((e = (call)) != hipSuccess) return hip_status(e, #call); \
+  } while (0)
+  // slots may still be read by work already on `stream` (an earlier call)
+  AKV_HIP(hipEventRecord(ev[2 * st->slots], cs));
+  AKV_HIP(hipStreamWaitEvent(xs, ev[2 * st->slots], 0));
+  // exact-tier splits of every sequence (they overlap the first copies)
+  if (plan.Se > 0) {
+    akv::AttnParams p = base;
+    p.Sq = 0;
+    p.part_base = plan.Sq;
+    AKV_HIP(akv::launch_decode_splits(p, D, plan.Se, desc->B, cs));
+  }
+  // compressed chunks through the ring, one copy each
+  long long k = 0;
+  for (int b = 0; b < desc->B; ++b) {
+    const akv_host_tier& h = st->seqs[b];
+    const int ns = (h.length + plan.Pq - 1) / plan.Pq;
+    for (int s0 = 0; s0 < ns; s0 += chunk_splits) {
+      const int n = std::min(chunk_splits, ns - s0);
+      const int tok0 = s0 * plan.Pq, ntok = std::min(h.length - tok0, n * plan.Pq);
+      const int blk0 = tok0 / AKV_BLOCK_TOKENS, nblk = (ntok + AKV_BLOCK_TOKENS - 1) / AKV_BLOCK_TOKENS;
+      const int slot = (int)(k % st->slots);
+      unsigned char* sb = static_cast<unsigned char*>(st->ring) + (size_t)slot * slot_bytes;
+      if (k >= st->slots) AKV_HIP(hipStreamWaitEvent(xs, ev[st->slots + slot], 0));  // slot free
+      AKV_HIP(hipMemcpyAsync(sb, static_cast<const unsigned char*>(h.blocks) + (size_t)blk0 * block_bytes,
+                             (size_t)nblk * block_bytes, hipMemcpyHostToDevice, xs));
+      AKV_HIP(hipEventRecord(ev[slot], xs));  // slot ready
+      AKV_HIP(hipStreamWaitEvent(cs, ev[slot], 0));
+      akv::AttnParams p = base;
+      p.b0 = b;
+      p.Sq = n;
+      p.Se = 0;
+      p.part_base = s0;
+      p.kc = sb;
+      p.vc = sb + code_bytes;
+      p.ks = reinterpret_cast<const uint16_t*>(sb + 2 * code_bytes);
+      p.vs = reinterpret_cast<const uint16_t*>(sb + 2 * code_bytes + scale_bytes);
+      p.q_code_stride = block_bytes;
+      p.q_scale_stride = block_bytes / 2;
+      p.qtab = nullptr;
+      p.qlen_fixed = ntok;
+      p.qmax = slot_blocks;
+      p.qnb = slot_blocks;
+      AKV_HIP(akv::launch_decode_splits(p, D, n, 1, cs));
+      AKV_HIP(hipEventRecord(ev[st->slots + slot], cs));  // slot free once this kernel is done
+      ++k;
+    }
+  }
+  AKV_HIP(akv::launch_decode_merge(base, D, cs));
+#undef AKV_HIP
+  return AKV_OK;
 }
 
 akv_status akv_attend_chunk(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream) {

@@ -173,10 +173,12 @@ struct WaveBlocks {
   }
 };
 
+// table == nullptr: the identity table (block k of the tier is pool block k).
 __device__ inline WaveBlocks load_wave_blocks(const int* table, int blk0, int nblk_w, int w, int lane) {
   WaveBlocks wb;
-  wb.lo = lane < nblk_w ? table[blk0 + w + kWaves * lane] : -1;
-  wb.hi = lane + 64 < nblk_w ? table[blk0 + w + kWaves * (lane + 64)] : -1;
+  const int k0 = blk0 + w + kWaves * lane, k1 = k0 + kWaves * 64;
+  wb.lo = lane < nblk_w ? (table ? table[k0] : k0) : -1;
+  wb.hi = lane + 64 < nblk_w ? (table ? table[k1] : k1) : -1;
   return wb;
 }
 
@@ -198,7 +200,7 @@ __device__ inline WaveBlocks trim_blocks(WaveBlocks wb, int nblk_w, int lane) {
 // Both tier lengths of sequence b; false if either lies outside its table
 // (the sequence's splits then write nothing and the merge reports NaN).
 __device__ inline bool tier_lengths(const AttnParams& p, int b, int& ql, int& el) {
-  ql = p.qmax ? p.qlen[b] : 0;
+  ql = p.qlen_fixed >= 0 ? p.qlen_fixed : (p.qmax ? p.qlen[b] : 0);
   el = p.emax ? p.elen[b] : 0;
   return ql >= 0 && ql <= p.qmax * 64 && el >= 0 && el <= p.emax * 64;
 }
@@ -206,7 +208,7 @@ __device__ inline bool tier_lengths(const AttnParams& p, int b, int& ql, int& el
 // Decode partials are laid out per query head: row ((b * Hkv + kv) * G + g)
 // * (Sq + Se) + split, so one head's splits are contiguous for the merge.
 __device__ inline size_t part_row(const AttnParams& p, int b, int kv, int g, int sx) {
-  return ((size_t)(b * p.Hkv + kv) * p.G + g) * (p.Sq + p.Se) + sx;
+  return ((size_t)(b * p.Hkv + kv) * p.G + g) * p.part_stride + sx;
 }
 
 // ------------------------------------------------------------------ epilogue
@@ -282,9 +284,8 @@ struct QUnit {
 template <int D>
 __device__ inline void quant_load(QUnit<D>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq, int lane) {
   constexpr int M = D / 32, NT = D / 16;
-  const size_t slab = (size_t)pb * p.Hkv + kv;
-  const unsigned char* kcs = p.kc + slab * (32 * D);
-  const unsigned char* vcs = p.vc + slab * (32 * D);
+  const unsigned char* kcs = p.kc + (size_t)pb * p.q_code_stride + (size_t)kv * (32 * D);
+  const unsigned char* vcs = p.vc + (size_t)pb * p.q_code_stride + (size_t)kv * (32 * D);
 #pragma unroll
   for (int tp = 0; tp < 2; ++tp) {
     int row = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
@@ -306,7 +307,8 @@ __device__ inline void quant_load(QUnit<D>& u, const AttnParams& p, int pb, int 
   // scales of the unit: M K-groups then M V-groups, 64 bytes (32 tokens) each;
   // lane (seg, part) carries bytes [16 part, 16 part + 16) of segment seg
   const int lm = lane & (8 * M - 1), seg = lm >> 2, g = seg % M;
-  const uint16_t* sb = (seg < M ? p.ks : p.vs) + slab * (2 * D) + g * 64 + 32 * c + 8 * (lane & 3);
+  const uint16_t* sb = (seg < M ? p.ks : p.vs) + (size_t)pb * p.q_scale_stride + (size_t)kv * (2 * D) + g * 64 +
+                       32 * c + 8 * (lane & 3);
   u.sc = *reinterpret_cast<const u32x4*>(sb);
 }
 
@@ -468,7 +470,8 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   // lane's query values and the tier lengths
   const int start = s * p.Pq;
   const int blk0 = start >> 6;
-  const WaveBlocks wb_all = load_split_blocks(p.qtab + (size_t)b * p.qmax, p.qmax, blk0, p.Pq, w, lane);
+  const WaveBlocks wb_all =
+      load_split_blocks(p.qtab ? p.qtab + (size_t)b * p.qmax : nullptr, p.qmax, blk0, p.Pq, w, lane);
   // rotation work split: wave w takes heads 2w, 2w+1; lane holds dims QV*(lane%32).. of head 2w + lane/32
   const int rh = 2 * w + (lane >> 5), rd0 = QV * (lane & 31);
   float qv[QV];
@@ -760,13 +763,13 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   const Lds L = lds_layout(smem);
-  const int sx = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int sx = blockIdx.x, kv = blockIdx.y, b = p.b0 + blockIdx.z;
   // the split reads its tier's length itself, in the same round trip as its
   // block ids and query
   if (sx < p.Sq)
-    quant_split<D>(p, L, b, kv, sx, sx);
+    quant_split<D>(p, L, b, kv, p.part_base + sx, sx);
   else
-    exact_split<D>(p, L, b, kv, sx, sx - p.Sq);
+    exact_split<D>(p, L, b, kv, p.part_base + sx, sx - p.Sq);
 }
 
 constexpr int kMergeThreads = 512;
@@ -972,6 +975,26 @@ hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream) {
     hipLaunchKernelGGL(split_decode_kernel<128>, grid, dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
   }
+  return hipGetLastError();
+}
+
+// The split kernel alone on a grid of (splits, Hkv, sequences), and the merge
+// alone (a staged decode launches the split kernel per staged chunk).
+hipError_t launch_decode_splits(const AttnParams& p, int D, int splits, int seqs, hipStream_t stream) {
+  dim3 grid(splits, p.Hkv, seqs);
+  if (D == 64)
+    hipLaunchKernelGGL(split_decode_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(split_decode_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const AttnParams& p, int D, hipStream_t stream) {
+  dim3 mgrid(p.Hq, p.B);
+  if (D == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

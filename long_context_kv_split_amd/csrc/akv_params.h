@@ -26,6 +26,17 @@ struct AttnParams {
   float* part_lse;          // [B][Hkv][Sq+Se][Tq][G]
   float* o;                 // [B][Tq][Hq][d]
   float* lse;               // [B][Tq][Hq]
+  // Decode split kernel only.  Workgroup (x, y, z) attends split x of
+  // sequence b0 + z and writes partial row part_base + x of part_stride per
+  // head.  qlen_fixed >= 0 replaces every compressed length, and qtab ==
+  // nullptr means block i of a sequence's compressed tier is pool block i
+  // (both for a compressed chunk streamed into a staging buffer).
+  int b0, part_base, part_stride, qlen_fixed;
+  // Distance between consecutive compressed-tier pool blocks: code bytes
+  // (both code pools) and scale elements (both scale pools).  Separate pools
+  // use Hkv*32*d and Hkv*2*d; per-block records (codes, codes, scales,
+  // scales of one block together) use the record size for all four.
+  size_t q_code_stride, q_scale_stride;
 };
 
 }  // namespace akv

@@ -12,6 +12,8 @@ from __future__ import annotations
 from dataclasses import dataclass
 from typing import List, Optional
 
+import ctypes
+
 import numpy as np
 import torch
 
@@ -164,6 +166,37 @@ class DeviceWorkload:
             k_scales=ptr(P.ks), v_scales=ptr(P.vs), quant_table=ptr(self.quant_table),
             quant_lengths=ptr(self.quant_len), quant_max_blocks=self.qmax,
             quant_num_blocks=max(1, w.quant_pool_blocks))
+
+    def host_tiers(self, replica: int = 0):
+        """Each sequence's compressed tier copied to pinned host memory as block records
+        in token order (record i = tokens 64i..: K codes, V codes, K scales, V scales of
+        every kv head), as akv_attend_decode_staged reads it.  Returns the tensors (kept
+        alive by the caller) and the ctypes array of akv_host_tier."""
+        w, P = self.w, self.pools[replica]
+        keep, tiers = [], (akv.HostTier * w.B)()
+        for b in range(w.B):
+            n = int(w.quant_len[b])
+            nb = -(-n // BLOCK)
+            rec = torch.empty(0, dtype=torch.uint8)
+            if nb:
+                blocks = torch.from_numpy(w.quant_table[b][:nb].astype(np.int64)).to(self.device)
+                parts = [x.index_select(0, blocks).reshape(nb, -1).view(torch.uint8) for x in (P.kc, P.vc, P.ks, P.vs)]
+                rec = torch.cat(parts, dim=1).cpu().pin_memory()
+            keep.append(rec)
+            tiers[b] = akv.HostTier(rec.data_ptr() if nb else 0, n)
+        return keep, tiers
+
+    def staging(self, tiers, ring: torch.Tensor, slots: int, copy_stream: torch.cuda.Stream):
+        """A StagingDesc over `tiers` (from host_tiers) with a device ring of `slots`
+        slots.  Creates its 2 * slots + 1 events; returns (desc, keep-alive objects)."""
+        events = [torch.cuda.Event() for _ in range(2 * slots + 1)]
+        for e in events:
+            e.record(copy_stream)  # materialize the handle
+        handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        desc = akv.StagingDesc(seqs=ctypes.addressof(tiers), ring=ring.data_ptr(), ring_bytes=ring.numel(),
+                               slots=slots, copy_stream=copy_stream.cuda_stream,
+                               events=ctypes.addressof(handles))
+        return desc, (events, handles, tiers)
 
     def read_exact(self, b: int, replica: int = 0):
         """Logical exact tier (K, V), bf16 bits [n, Hkv, d] each, of sequence b as the

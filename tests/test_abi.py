@@ -42,7 +42,8 @@ def test_abi_version_and_exports():
     assert set(names) == {"akv_abi_version", "akv_last_error", "akv_decode_workspace_bytes",
                           "akv_chunk_workspace_bytes", "akv_attend_decode", "akv_attend_chunk",
                           "akv_split_plan", "akv_lse_merge", "akv_compress_evicted", "akv_append_evict",
-                          "akv_checkpoint_bytes", "akv_checkpoint_save", "akv_checkpoint_restore"}
+                          "akv_checkpoint_bytes", "akv_checkpoint_save", "akv_checkpoint_restore",
+                          "akv_attend_decode_staged"}
     for n in names:
         assert hasattr(akv.LIB, n), n
 
@@ -304,3 +305,32 @@ def test_checkpoint_image_size_and_validation():
     assert akv.akv_checkpoint_restore(context_desc(d=96), img) == akv.AKV_ERR_UNSUPPORTED
     assert akv.akv_checkpoint_restore(context_desc(), img + 16) == akv.AKV_ERR_ALIGN
     assert akv.akv_checkpoint_save(context_desc(exact_k=FAKE + 8), img) == akv.AKV_ERR_ALIGN
+
+
+def test_staged_decode_validation_order():
+    """Staging and attention descriptors are checked together, category by category."""
+    tiers = (akv.HostTier * 1)(akv.HostTier(FAKE + 0x100000, 1000))
+    events = (ctypes.c_void_p * 5)(*([FAKE + 0x10] * 5))
+
+    def sd(**over):
+        kw = dict(seqs=ctypes.addressof(tiers), ring=FAKE + 0xC000000, ring_bytes=1 << 24, slots=2,
+                  copy_stream=FAKE + 0x20, events=ctypes.addressof(events))
+        kw.update(over)
+        return akv.StagingDesc(**kw)
+
+    def call(desc=None, st=None, ws=FAKE + 0xA000000):
+        return akv.LIB.akv_attend_decode_staged(ctypes.byref(desc or good_desc()), ctypes.byref(st or sd()), ws,
+                                                1 << 40, None)
+
+    q = good_desc().quant
+    q.k_codes = q.v_codes = q.k_scales = q.v_scales = q.block_table = 0   # pools are on the host here
+    staged_desc = good_desc(quant=q)
+    assert akv.LIB.akv_attend_decode_staged(ctypes.byref(staged_desc), None, 0, 0, None) == akv.AKV_ERR_NULL
+    assert call(staged_desc, sd(ring=0)) == akv.AKV_ERR_NULL
+    assert call(good_desc(q=0), sd(slots=1)) == akv.AKV_ERR_NULL            # NULL before SHAPE
+    assert call(staged_desc, sd(slots=1)) == akv.AKV_ERR_SHAPE
+    assert call(good_desc(quant=q, d=96), sd(slots=1)) == akv.AKV_ERR_SHAPE  # staging SHAPE before UNSUPPORTED
+    assert call(good_desc(quant=q, d=96)) == akv.AKV_ERR_UNSUPPORTED
+    assert call(staged_desc, sd(ring=FAKE + 0xC000010)) == akv.AKV_ERR_ALIGN
+    assert call(staged_desc, ws=0) == akv.AKV_ERR_WORKSPACE
+    assert call(staged_desc, sd(ring_bytes=1 << 16)) == akv.AKV_ERR_WORKSPACE  # a slot below one split
