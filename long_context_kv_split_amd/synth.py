@@ -36,7 +36,7 @@ BLOCK = 64  # tokens per paged block
 
 _STREAMS = (
     "q", "k_exact", "v_exact", "k_quant", "v_quant", "k_chunk", "v_chunk",
-    "outliers", "table_exact", "table_quant", "lengths", "k_step", "v_step",
+    "outliers", "table_exact", "table_quant", "lengths", "k_step", "v_step", "rotation",
 )
 
 
@@ -233,6 +233,16 @@ def contiguous(w: Workload) -> Workload:
     c.exact_table = ident(w.exact_table)
     c.quant_table = ident(w.quant_table)
     return c
+
+
+def qr_rotation(d: int, seed: int = 0) -> np.ndarray:
+    """A seeded random orthogonal matrix, float32 [d, d]: the Q factor of a
+    QR factorization of an N(0,1) matrix, columns signed so that R's diagonal
+    is positive (the Haar-distributed choice).  Rounded to float32 once."""
+    a = stream(seed, "rotation").standard_normal((d, d))
+    q, r = np.linalg.qr(a)
+    q = q * np.sign(np.diag(r))[None, :]
+    return q.astype(np.float32)
 
 
 def step_tokens(seed: int, steps: int, B: int, Hkv: int, d: int):

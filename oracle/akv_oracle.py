@@ -191,6 +191,23 @@ def fwht_f32(x: np.ndarray) -> np.ndarray:
     return x
 
 
+def dense_rotate_f32(x: np.ndarray, rotation: np.ndarray) -> np.ndarray:
+    """E2 with a caller-given rotation R (float32 [d, d]): y = R x on the last axis.
+
+    The QuantForge walkthrough (section 5, "README Polish") sets a Hadamard
+    rotation against a QR (random orthogonal) one; with R orthogonal no
+    further normalization follows (there is no E3).  Each y_i is summed in
+    ascending k from 0: y_i = (((0 + R_i0 x_0) + R_i1 x_1) + ...), every
+    product and every sum one float32 operation, nothing fused.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    r = np.asarray(rotation, dtype=np.float32)
+    acc = np.zeros(x.shape, dtype=np.float32)
+    for k in range(x.shape[-1]):
+        acc = acc + x[..., k:k + 1] * r[:, k]
+    return acc
+
+
 def group_rms_f32(y: np.ndarray) -> np.ndarray:
     """E4: per 32-group sqrt(mean(y^2)) in float32 with the fixed pairwise tree.
 
@@ -213,17 +230,23 @@ def f32_to_f16_sat(s: np.ndarray) -> np.ndarray:
     return s.astype(np.float16)
 
 
-def encode(bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+def encode(bits: np.ndarray, rotation: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """E1-E8 for vectors of bf16 bit patterns shaped [..., d].
 
     Returns (codes uint8 [..., d] in 0..15, scales as uint16 fp16 bit patterns
     [..., d/32]).  Nibble packing (E9) is a storage detail: see pack_nibbles.
+    With ``rotation`` (float32 [d, d], orthogonal) E2 is dense_rotate_f32 and
+    E3 is skipped; otherwise E2 is the Hadamard butterflies and E3 the
+    1/sqrt(d) normalization.
     """
     bits = np.asarray(bits, dtype=np.uint16)
     d = bits.shape[-1]
     x = bf16_to_f32(bits)                                 # E1
-    x = fwht_f32(x)                                       # E2
-    y = x * inv_sqrt_f32(d)                               # E3
+    if rotation is not None:
+        y = dense_rotate_f32(x, rotation)                 # E2 (dense; no E3)
+    else:
+        x = fwht_f32(x)                                   # E2
+        y = x * inv_sqrt_f32(d)                           # E3
     s32 = group_rms_f32(y)                                # E4
     s16 = f32_to_f16_sat(s32)                             # E5
     s = s16.astype(np.float32)                            # E6
@@ -268,10 +291,13 @@ def dequant_rotated(codes: np.ndarray, scales16: np.ndarray) -> np.ndarray:
     return (vals * s[..., None]).reshape(codes.shape)
 
 
-def dequant(codes: np.ndarray, scales16: np.ndarray) -> np.ndarray:
-    """Unrotated reconstruction (H/sqrt(d)) @ rotated, with the explicit matrix."""
+def dequant(codes: np.ndarray, scales16: np.ndarray, rotation: Optional[np.ndarray] = None) -> np.ndarray:
+    """Unrotated reconstruction: (H/sqrt(d)) @ rotated with the explicit matrix, or
+    R^T @ rotated for a given rotation R (orthogonal, so R^T undoes it)."""
     r = dequant_rotated(codes, scales16)
     d = r.shape[-1]
+    if rotation is not None:
+        return r @ np.asarray(rotation, dtype=np.float64)   # row-vector form of R^T @ r
     return r @ normalized_hadamard(d)   # H is symmetric: row-vector form of H @ r
 
 
@@ -301,12 +327,12 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 def history_f64(k_exact_bits: np.ndarray, v_exact_bits: np.ndarray,
                 kq_codes: Optional[np.ndarray], kq_scales: Optional[np.ndarray],
                 vq_codes: Optional[np.ndarray], vq_scales: Optional[np.ndarray],
-                head: int) -> Tuple[np.ndarray, np.ndarray]:
+                head: int, rotation: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attended history of one kv head: compressed tier first, then exact tier."""
     ks, vs = [], []
     if kq_codes is not None and kq_codes.shape[0]:
-        ks.append(dequant(kq_codes[:, head], kq_scales[:, head]))
-        vs.append(dequant(vq_codes[:, head], vq_scales[:, head]))
+        ks.append(dequant(kq_codes[:, head], kq_scales[:, head], rotation))
+        vs.append(dequant(vq_codes[:, head], vq_scales[:, head], rotation))
     if k_exact_bits.shape[0]:
         ks.append(bf16_to_f64(k_exact_bits[:, head]))
         vs.append(bf16_to_f64(v_exact_bits[:, head]))
@@ -319,7 +345,7 @@ def history_f64(k_exact_bits: np.ndarray, v_exact_bits: np.ndarray,
 def decode_sequence(q_bits: np.ndarray, k_exact_bits, v_exact_bits,
                     kq_codes, kq_scales, vq_codes, vq_scales,
                     scale: Optional[float] = None, causal_tail: int = 0,
-                    heads: Optional[Sequence[int]] = None):
+                    heads: Optional[Sequence[int]] = None, rotation: Optional[np.ndarray] = None):
     """Attention of one sequence's queries over its whole two-tier history.
 
     q_bits [Tq, Hq, d] bf16; exact tier [Ne, Hkv, d] bf16; compressed tier as
@@ -341,7 +367,7 @@ def decode_sequence(q_bits: np.ndarray, k_exact_bits, v_exact_bits,
         hs = [h for h in range(kv * G, (kv + 1) * G) if h in want]
         if not hs:
             continue
-        k, v = history_f64(k_exact_bits, v_exact_bits, kq_codes, kq_scales, vq_codes, vq_scales, kv)
+        k, v = history_f64(k_exact_bits, v_exact_bits, kq_codes, kq_scales, vq_codes, vq_scales, kv, rotation)
         mask = None
         if causal_tail:
             n = k.shape[0]
@@ -395,7 +421,7 @@ def encode_tier(src_bits: List[np.ndarray]):
     return [encode(x) for x in src_bits]
 
 
-def reference_outputs(w, encoded_k=None, encoded_v=None, heads=None, seqs=None):
+def reference_outputs(w, encoded_k=None, encoded_v=None, heads=None, seqs=None, rotation=None):
     """o [B, Tq, Hq, d] and lse [B, Tq, Hq] (float64) for a synth.Workload-like object.
 
     ``w`` needs: q, exact_k, exact_v, quant_k_src, quant_v_src, causal_tail.
@@ -407,13 +433,13 @@ def reference_outputs(w, encoded_k=None, encoded_v=None, heads=None, seqs=None):
     lse = np.full((B, Tq, Hq), np.nan)
     for b in (range(B) if seqs is None else seqs):
         if encoded_k is None:
-            kc, ks = encode(w.quant_k_src[b])
-            vc, vs = encode(w.quant_v_src[b])
+            kc, ks = encode(w.quant_k_src[b], rotation)
+            vc, vs = encode(w.quant_v_src[b], rotation)
         else:
             kc, ks = encoded_k[b]
             vc, vs = encoded_v[b]
         ob, lb = decode_sequence(w.q[b], w.exact_k[b], w.exact_v[b], kc, ks, vc, vs,
-                                 causal_tail=w.causal_tail, heads=heads)
+                                 causal_tail=w.causal_tail, heads=heads, rotation=rotation)
         o[b], lse[b] = ob, lb
     return o, lse
 

@@ -523,3 +523,67 @@ def test_encoding_is_per_token():
     cb, sb = O.encode(b)
     cab, sab = O.encode(np.concatenate([a, b]))
     assert np.array_equal(cab, np.concatenate([ca, cb])) and np.array_equal(sab, np.concatenate([sa, sb]))
+
+
+# ------------------------------------------------------------ dense (QR) rotation
+
+def test_dense_rotation_matches_python_float32_loop():
+    """E2 with a given rotation, checked against scalar float32 operations."""
+    rng = np.random.default_rng(5)
+    d = 8
+    r = rng.standard_normal((d, d)).astype(np.float32)
+    x = rng.standard_normal((3, d)).astype(np.float32)
+    got = O.dense_rotate_f32(x, r)
+    for n in range(3):
+        for i in range(d):
+            acc = np.float32(0.0)
+            for k in range(d):
+                acc = np.float32(acc + np.float32(r[i, k] * x[n, k]))
+            assert got[n, i] == acc
+
+
+def test_qr_rotation_is_orthogonal_and_seeded():
+    from long_context_kv_split_amd.synth import qr_rotation
+    for d in (64, 128):
+        r = qr_rotation(d, 0).astype(np.float64)
+        assert np.max(np.abs(r @ r.T - np.eye(d))) < 2e-6
+        assert np.all(np.diag(np.linalg.qr(qr_rotation(d, 0).astype(np.float64))[1]) != 0)
+        assert np.array_equal(qr_rotation(d, 0), qr_rotation(d, 0))
+        assert not np.array_equal(qr_rotation(d, 0), qr_rotation(d, 1))
+
+
+def test_dense_encoder_with_hadamard_matrix_differs_only_near_midpoints():
+    """With R = H/sqrt(d) as a dense float32 matrix the dense encoder computes the
+    same rotation in another summation order: codes differ by at most one level,
+    and only where u sits within a few ulps of a threshold."""
+    from long_context_kv_split_amd.synth import f64_to_bf16_bits
+    rng = np.random.default_rng(6)
+    d = 128
+    x = f64_to_bf16_bits(rng.standard_normal((400, d)))
+    h = O.normalized_hadamard(d).astype(np.float32)
+    c0, s0 = O.encode(x)
+    c1, s1 = O.encode(x, h)
+    diff = c0.astype(int) - c1.astype(int)
+    assert np.max(np.abs(diff)) <= 1
+    assert np.mean(diff != 0) < 1e-3
+    # scales: the same group RMS up to a few float32 ulps, so fp16 equal almost always
+    assert np.mean(s0 != s1) < 5e-3
+
+
+def test_qr_round_trip_and_attention_are_lloyd_max_sized():
+    """Encoding under a QR rotation and undoing it with R^T gives the Lloyd-Max error,
+    and attention over the reconstruction stays close to exact attention."""
+    from long_context_kv_split_amd.synth import f64_to_bf16_bits, qr_rotation
+    rng = np.random.default_rng(7)
+    d = 128
+    r = qr_rotation(d, 3)
+    xb = f64_to_bf16_bits(rng.standard_normal((2000, 1, d)))
+    c, s = O.encode(xb, r)
+    xh = O.dequant(c[:, 0], s[:, 0], r)
+    x = O.bf16_to_f64(xb[:, 0])
+    rel = np.mean((xh - x) ** 2) / np.mean(x ** 2)
+    assert 0.005 < rel < 0.02
+    q = rng.standard_normal((4, d))
+    oe, le = O.attention(q, x, x, 1 / np.sqrt(d))
+    oq, lq = O.attention(q, xh, xh, 1 / np.sqrt(d))
+    assert np.max(np.abs(le - lq)) < 0.5 and np.max(np.abs(oe - oq)) < 0.2
