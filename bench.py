@@ -112,11 +112,12 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "seconds_per_call": per_call}
 
 
-def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None, split_quant=None, split_exact=None):
+def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None, split_quant=None, split_exact=None,
+                 rotation=None):
     import torch
     from long_context_kv_split_amd import akv, harness, synth
     w = synth.make(name) if w is None else w
-    dw = harness.DeviceWorkload(w)
+    dw = harness.DeviceWorkload(w, rotation=rotation)
     kv_bytes = w.kv_bytes()
     n_rep = max(1, -(-min_bytes // kv_bytes))
     dw.add_replicas(n_rep)
@@ -246,6 +247,40 @@ def bench_staged(w, dw, ev_resident_ms, stream, slots=2, slot_mb=32, steps=20, w
                          "peak_measured": pcie / (copy_ms * 1e-3) / 1e9, "unit": "GB/s"}}
 
 
+def bench_rotation(w, ev_hadamard_ms, stream, steps=500, warmup=20):
+    """The compressed tier under a QR (random orthogonal) rotation instead of the
+    Walsh-Hadamard one: hybrid128k decode (the query rotated by R once per call,
+    the compressed-tier output by R^T once per head), and the encoder moving the
+    4,096 exact tokens of hybrid128k into the compressed tier under each rotation."""
+    from long_context_kv_split_amd import akv, harness, synth
+    R = synth.qr_rotation(w.d, seed=0)
+    _, dwr, kv_bytes, n_rep, ev_ms, wall_ms = bench_decode("hybrid128k", steps, warmup, stream, w=w, rotation=R)
+    h = stream.cuda_stream
+    n = int(w.exact_len[0])
+    enc = {}
+    for label, rot in (("hadamard", 0), ("qr", harness.ptr(dwr.rotation))):
+        cds = []
+        for r in range(n_rep):
+            c = dwr.compress_desc(0, 0, n, 0, replica=r)
+            c.rotation = rot
+            cds.append(c)
+
+        def encode(r):
+            st = akv.akv_compress_evicted(cds[r], h)
+            if st:
+                akv.check(st)
+
+        e_ms, _ = time_calls(encode, n_rep, 5, 100, stream)
+        enc[label] = e_ms * 1e3
+    enc_bytes = w.Hkv * n * (2 * 2 * w.d + 2 * (w.d // 2 + 2 * (w.d // 32)))
+    return {"workload": "hybrid128k decode and a 4,096-token encode (Hkv 4, d 128) with a QR rotation",
+            "decode_us_per_call": ev_ms * 1e3, "decode_us_per_call_hadamard": ev_hadamard_ms * 1e3,
+            "decode_kv_gbps": kv_bytes / (ev_ms * 1e-3) / 1e9,
+            "encode_us": enc["qr"], "encode_us_hadamard": enc["hadamard"],
+            "encode_gbps": enc_bytes / (enc["qr"] * 1e-6) / 1e9,
+            "encode_gbps_hadamard": enc_bytes / (enc["hadamard"] * 1e-6) / 1e9}
+
+
 def chunk_flops(w) -> float:
     """QK^T + PV multiply-adds x 2 of one chunk call: every query sees the whole
     history before the chunk plus, causally, (Tq + 1) / 2 chunk tokens on average."""
@@ -337,7 +372,7 @@ def main():
                              "kv_gbps": b2 / (e2 * 1e-3) / 1e9, "replicas": r2,
                              "decode_tokens_per_s": w2.B / (e2 * 1e-3)}
                 log(f"bench: {name} {e2 * 1e3:.2f} us/call")
-        staged = ckpt = step = None
+        staged = ckpt = step = rot = None
         if not args.no_extra:
             log("bench: host-staged decode")
             staged = bench_staged(w, dw, ev_ms, stream)
@@ -349,6 +384,10 @@ def main():
             log("bench: per-step append / evict")
             step = bench_step(stream)
             log("bench: step " + ", ".join(f"{k} {v['us_per_step']:.2f} us" for k, v in step.items()))
+            log("bench: QR rotation")
+            rot = bench_rotation(w, ev_ms, stream)
+            log(f"bench: QR decode {rot['decode_us_per_call']:.2f} us (Hadamard {rot['decode_us_per_call_hadamard']:.2f}), "
+                f"encode {rot['encode_us']:.1f} us (Hadamard {rot['encode_us_hadamard']:.1f})")
         chunk = None
         if not args.no_chunk:
             log("bench: building chunk workload")
@@ -402,6 +441,7 @@ def main():
     if staged:
         out["staged"] = staged
         out["checkpoint"] = ckpt
+        out["rotation"] = rot
         out["step"] = {"workload": "akv_append_evict per decode step, Hkv 4, d 128 (B1: window 4096; "
                                "B32: window 2048); one block move per sequence every 64 steps", **step}
     if chunk:

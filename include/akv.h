@@ -69,6 +69,18 @@
  * Dequantized (rotated-space) value of dim t of a token: C[code] * scale(t/32),
  * with C the Lloyd-Max table; the unrotated vector is (H_d/sqrt(d)) times it.
  *
+ * Rotation (the QuantForge walkthrough, section 5, sets the Hadamard rotation
+ * against a QR, i.e. random orthogonal, one): every descriptor that encodes
+ * or reads the compressed tier has a `rotation` field.  NULL selects the
+ * normalized Walsh-Hadamard rotation above.  Otherwise it is a device
+ * pointer to a float32 [d][d] row-major orthogonal matrix R, 16-byte
+ * aligned: the encoder stores codes of y = R x (y_i summed in ascending k,
+ * one float32 multiply and add per term, no 1/sqrt(d) step), decode rotates
+ * each query by R once per call (workspace grows by 4*B*Hq*d bytes) and the
+ * compressed-tier output by R^T once per head, and the unrotated vector is
+ * R^T times the rotated one.  The same R must be used to encode and to
+ * attend.  akv_attend_chunk takes NULL only (AKV_ERR_UNSUPPORTED otherwise).
+ *
  * Block tables: int32 [B][max_blocks]; entry j of row b is the pool block of
  * tier-local tokens [64j, 64j+64) of sequence b.  Tier lengths: int32 [B].
  * In the attended history of a sequence the compressed tier comes first
@@ -164,6 +176,7 @@ typedef struct akv_attn_desc {
   int32_t split_tokens_quant;  /* 0 => the shape-only default above */
   float* o;                    /* fp32 [B][Tq][Hq][d] normalized output */
   float* lse;                  /* fp32 [B][Tq][Hq] natural-log sum of exp(scores) */
+  const float* rotation;       /* NULL, or the compressed tier's rotation R (see "Rotation") */
 } akv_attn_desc;
 
 typedef akv_attn_desc akv_decode_desc;
@@ -196,6 +209,7 @@ typedef struct akv_compress_desc {
   const int32_t* dst_block_table;  /* [dst_max_blocks] */
   int32_t dst_max_blocks, dst_num_blocks;
   int32_t dst_start;
+  const float* rotation;       /* NULL, or the rotation R (see "Rotation") */
 } akv_compress_desc;
 
 /* ABI version of the loaded library (AKV_ABI_VERSION at build time). */
@@ -342,6 +356,7 @@ typedef struct akv_append_desc {
   const int32_t* quant_table;  /* [B][quant_max_blocks] */
   int32_t* quant_lengths;      /* [B], updated in place */
   int32_t quant_max_blocks, quant_num_blocks;
+  const float* rotation;       /* NULL, or the rotation R (see "Rotation") */
 } akv_append_desc;
 
 akv_status akv_append_evict(const akv_append_desc* desc, void* stream);

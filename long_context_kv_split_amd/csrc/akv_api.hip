@@ -17,6 +17,7 @@ namespace akv {
 hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream);
 hipError_t launch_decode_splits(const AttnParams& p, int D, int splits, int seqs, hipStream_t stream);
 hipError_t launch_decode_merge(const AttnParams& p, int D, hipStream_t stream);
+hipError_t launch_decode_qrot(const AttnParams& p, int D, hipStream_t stream);
 hipError_t launch_chunk(const AttnParams& p, int D, hipStream_t stream);
 hipError_t launch_lse_merge(const float* op, const float* lp, int P, int R, int d, float* o, float* lse,
                             hipStream_t stream);
@@ -51,6 +52,7 @@ int split_tokens(int v, int dflt) { return v ? v : dflt; }
 struct Plan {
   int G, Pe, Pq, Se, Sq;
   size_t part_rows;  // partial rows = B * Hkv * (Sq+Se) * Tq * G
+  size_t qrot_off;   // rotated queries (given rotation only), after the partials
   size_t ws_bytes;
 };
 
@@ -90,6 +92,7 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   if (!chunk && d->Tq != 1) return fail(AKV_ERR_UNSUPPORTED, "decode takes Tq = 1 (got %d)", d->Tq);
   if (chunk && d->Tq > AKV_MAX_CHUNK) return fail(AKV_ERR_UNSUPPORTED, "chunk Tq %d > %d", d->Tq, AKV_MAX_CHUNK);
   if (chunk && e.max_blocks == 0) return fail(AKV_ERR_UNSUPPORTED, "chunk needs the exact tier (it holds the chunk)");
+  if (chunk && d->rotation) return fail(AKV_ERR_UNSUPPORTED, "the chunk takes the Walsh-Hadamard rotation only");
   if (d->B > 65535 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
   int Pe, Pq;
   if (!chunk) {
@@ -141,6 +144,7 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   if ((long long)d->Tq * d->Hq > (1LL << 30)) return fail(AKV_ERR_UNSUPPORTED, "Tq * Hq too large");
   // ---- ALIGN
   if (!aligned(d->q, 16)) return fail(AKV_ERR_ALIGN, "q must be 16-byte aligned");
+  if (!aligned(d->rotation, 16)) return fail(AKV_ERR_ALIGN, "rotation must be 16-byte aligned");
   if (!aligned(d->o, 4) || !aligned(d->lse, 4)) return fail(AKV_ERR_ALIGN, "o and lse must be 4-byte aligned");
   if (e.max_blocks > 0 && (!aligned(e.k, 16) || !aligned(e.v, 16) || !aligned(e.block_table, 4) ||
                            !aligned(e.lengths, 4)))
@@ -157,6 +161,8 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   size_t po = plan->part_rows * d->d * sizeof(float);
   po = (po + 255) & ~(size_t)255;
   plan->ws_bytes = po + plan->part_rows * sizeof(float);
+  plan->qrot_off = (plan->ws_bytes + 255) & ~(size_t)255;
+  if (d->rotation) plan->ws_bytes = plan->qrot_off + (size_t)d->B * d->Hq * d->d * sizeof(float);
   return AKV_OK;
 }
 
@@ -209,6 +215,8 @@ akv::AttnParams make_params(const akv_attn_desc* d, const Plan& plan, void* ws) 
   p.qlen_fixed = -1;
   p.q_code_stride = (size_t)d->Hkv * 32 * d->d;
   p.q_scale_stride = (size_t)d->Hkv * 2 * d->d;
+  p.rot = d->rotation;
+  p.qrot = d->rotation ? reinterpret_cast<float*>(base + plan.qrot_off) : nullptr;
   return p;
 }
 
@@ -351,7 +359,9 @@ akv_status akv_attend_decode_staged(const akv_attn_desc* desc, const akv_staging
   // slots may still be read by work already on `stream` (an earlier call)
   AKV_HIP(hipEventRecord(ev[2 * st->slots], cs));
   AKV_HIP(hipStreamWaitEvent(xs, ev[2 * st->slots], 0));
-  // exact-tier splits of every sequence (they overlap the first copies)
+  // queries rotated by a given rotation, then the exact-tier splits of every
+  // sequence (they overlap the first copies)
+  AKV_HIP(akv::launch_decode_qrot(base, D, cs));
   if (plan.Se > 0) {
     akv::AttnParams p = base;
     p.Sq = 0;
@@ -440,6 +450,7 @@ akv_status akv_compress_evicted(const akv_compress_desc* d, void* stream) {
   if (!aligned(d->src_k, 2) || !aligned(d->src_v, 2) || !aligned(d->dst_k_scales, 2) ||
       !aligned(d->dst_v_scales, 2) || !aligned(d->src_block_table, 4) || !aligned(d->dst_block_table, 4))
     return fail(AKV_ERR_ALIGN, "compress buffers misaligned");
+  if (!aligned(d->rotation, 16)) return fail(AKV_ERR_ALIGN, "rotation must be 16-byte aligned");
   if (d->n_tokens == 0) return AKV_OK;
   return hip_status(akv::launch_compress(d, static_cast<hipStream_t>(stream)), "akv_compress_evicted");
 }
@@ -463,7 +474,8 @@ akv_status akv_append_evict(const akv_append_desc* d, void* stream) {
   if (d->B > 32767 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B must be <= 32767 and Hkv <= 65535");
   if (!aligned(d->new_k, 2) || !aligned(d->new_v, 2) || !aligned(d->exact_k, 2) || !aligned(d->exact_v, 2) ||
       !aligned(d->k_scales, 2) || !aligned(d->v_scales, 2) || !aligned(d->exact_table, 4) ||
-      !aligned(d->exact_lengths, 4) || !aligned(d->quant_table, 4) || !aligned(d->quant_lengths, 4))
+      !aligned(d->exact_lengths, 4) || !aligned(d->quant_table, 4) || !aligned(d->quant_lengths, 4) ||
+      !aligned(d->rotation, 16))
     return fail(AKV_ERR_ALIGN, "append buffers misaligned");
   return hip_status(akv::launch_append_evict(d, static_cast<hipStream_t>(stream)), "akv_append_evict");
 }

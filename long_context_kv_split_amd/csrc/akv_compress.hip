@@ -19,8 +19,13 @@
 // nothing is contracted into a fused multiply-add, so codes and scales are
 // bit-exact functions of the input.
 //
-// One wavefront per (token pair, kv head, K|V): lane l holds elements
-// l + 64k of both tokens; butterflies with h < 64 exchange across lanes.
+// With a given orthogonal rotation R (the QuantForge walkthrough, section 5,
+// compares a QR rotation with the Hadamard one), E2 is y = R x summed in
+// ascending k and E3 is dropped.
+//
+// One wavefront per (token pair, kv head, K|V) -- per 8 pairs with a given
+// rotation, which then share each load of R: lane l holds elements l + 64k;
+// butterflies with h < 64 exchange across lanes.
 #include "akv_common.h"
 
 #pragma clang fp contract(off)
@@ -39,57 +44,102 @@ struct CompressParams {
   uint16_t* dst_vs;
   const int32_t* dst_table;
   int dst_num_blocks, dst_start;
+  const float* rot;  // nullptr: Walsh-Hadamard; else float32 [d][d] orthogonal R
 };
 
-// Encode token pair `pair` (tokens 2 pair, 2 pair + 1 of the range) of one
-// (kv head, K|V): one wavefront, lane l holding elements l + 64k.
+// E1 for token `tok` of the range (lane l takes elements l + 64k): zeros, and
+// false, past the range or for a block id outside the pool.  Exact-tier K is
+// token-major (a token's dims adjacent), V dim-major inside each 32-token
+// half block (dim t of token r at ((r / 32) * d + t) * 32 + r % 32).
 template <int D>
-__device__ inline void encode_pair(const CompressParams& p, int pair, int kv, int isv, int lane) {
-  constexpr int E = D / 64;  // elements per lane per token
-  const int first = 2 * pair;
-  const int ntok = min(2, p.n_tokens - first);
-  const float rd = inv_sqrt_d(D);
+__device__ inline bool load_token(const CompressParams& p, int isv, int kv, int tok, int lane, float (&x)[D / 64]) {
+  constexpr int E = D / 64;
+  const uint16_t* src = nullptr;
+  const int dstride = isv ? kBlock / 2 : 1;
+  if (tok < p.n_tokens) {
+    const int s = p.src_start + tok;
+    const int blk = p.src_table[s >> 6];
+    if (blk >= 0 && blk < p.src_num_blocks) {
+      const size_t slab = (size_t)(blk * p.Hkv + kv) * kBlock * D;
+      src = isv ? p.src_v + slab + ((s & 63) >> 5) * (kBlock / 2) * D + (s & 31) : p.src_k + slab + (size_t)(s & 63) * D;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = src ? bf16_bits_to_float(src[(lane + 64 * e) * dstride]) : 0.0f;
+  return src != nullptr;
+}
 
-  float y[2][E];
-  int code[2][E];
-  uint16_t s16[2][E];
-  bool ok[2] = {false, false};
+// E2, Walsh-Hadamard: butterflies across lanes for h < 64, inside the lane
+// for h = 64.
+template <int D>
+__device__ inline void hadamard_rows(float (&x)[D / 64], int lane) {
+  constexpr int E = D / 64;
 #pragma unroll
-  for (int tk = 0; tk < 2; ++tk) {
-    float x[E];
-    // exact-tier K is token-major (a token's dims adjacent), V dim-major
-    // inside each 32-token half block (dim t of token r at
-    // ((r / 32) * d + t) * 32 + r % 32)
-    const uint16_t* src = nullptr;
-    const int dstride = isv ? kBlock / 2 : 1;
-    if (tk < ntok) {
-      int s = p.src_start + first + tk;
-      int blk = p.src_table[s >> 6];
-      if (blk >= 0 && blk < p.src_num_blocks) {
-        const size_t slab = (size_t)(blk * p.Hkv + kv) * kBlock * D;
-        src = isv ? p.src_v + slab + ((s & 63) >> 5) * (kBlock / 2) * D + (s & 31) : p.src_k + slab + (size_t)(s & 63) * D;
-        ok[tk] = true;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = src ? bf16_bits_to_float(src[(lane + 64 * e) * dstride]) : 0.0f;  // E1
-    // E2: butterflies across lanes for h < 64, inside the lane for h = 64
-#pragma unroll
-    for (int h = 1; h < 64 && h < D; h <<= 1) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float o = __shfl_xor(x[e], h);
-        x[e] = (lane & h) ? (o - x[e]) : (x[e] + o);
-      }
-    }
-    if (E == 2) {
-      float a = x[0], b = x[E - 1];
-      x[0] = a + b;
-      x[E - 1] = a - b;
-    }
+  for (int h = 1; h < 64 && h < D; h <<= 1) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      y[tk][e] = x[e] * rd;                                 // E3
+      float o = __shfl_xor(x[e], h);
+      x[e] = (lane & h) ? (o - x[e]) : (x[e] + o);
+    }
+  }
+  if (E == 2) {
+    float a = x[0], b = x[E - 1];
+    x[0] = a + b;
+    x[E - 1] = a - b;
+  }
+}
+
+// E2 with a given rotation R for NT tokens at once: y_i = (((0 + R_i0 x_0) +
+// R_i1 x_1) + ...), ascending k, one float32 multiply and one add per term
+// (no E3).  Lane l computes rows i = l + 64e; each float4 of R it loads
+// serves all NT tokens, whose values are broadcast from LDS (xs: NT * D
+// floats, this wavefront's own).
+template <int D, int NT>
+__device__ inline void dense_rows(const float* __restrict__ R, float (&x)[NT][D / 64], int lane, float* xs) {
+  constexpr int E = D / 64;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) xs[t * D + lane + 64 * e] = x[t][e];
+  __syncthreads();
+  float acc[NT][E];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
+  for (int k4 = 0; k4 < D / 4; ++k4) {
+    float4v r[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) r[e] = *reinterpret_cast<const float4v*>(R + (size_t)(lane + 64 * e) * D + 4 * k4);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float4v xv = *reinterpret_cast<const float4v*>(xs + t * D + 4 * k4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[t][e] = acc[t][e] + r[e][u] * xv[u];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[t][e] = acc[t][e];
+}
+
+// E4..E9 for token pair `pair` (tokens 2 pair, 2 pair + 1 of the range) of
+// one (kv head, K|V), given its rotated values y (lane l: elements l + 64k).
+template <int D>
+__device__ inline void finish_pair(const CompressParams& p, int pair, int kv, int isv, int lane,
+                                   const float (&y)[2][D / 64], const bool (&ok)[2]) {
+  constexpr int E = D / 64;
+  const int first = 2 * pair;
+  const int ntok = min(2, p.n_tokens - first);
+  int code[2][E];
+  uint16_t s16[2][E];
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
       float v = y[tk][e] * y[tk][e];                        // E4
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) {
@@ -150,9 +200,42 @@ __device__ inline void encode_pair(const CompressParams& p, int pair, int kv, in
   }
 }
 
-template <int D>
+// Encode token pairs pair0 .. pair0 + NP - 1 of one (kv head, K|V): one
+// wavefront, lane l holding elements l + 64k.  With a given rotation the NP
+// pairs share the loads of R (xs: 2 * NP * D floats of LDS).
+template <int D, int NP>
+__device__ inline void encode_pairs(const CompressParams& p, int pair0, int kv, int isv, int lane, float* xs) {
+  constexpr int E = D / 64;
+  const float rd = inv_sqrt_d(D);
+  float x[2 * NP][E];
+  bool ok[2 * NP];
+#pragma unroll
+  for (int i = 0; i < 2 * NP; ++i) ok[i] = load_token<D>(p, isv, kv, 2 * pair0 + i, lane, x[i]);   // E1
+  if (p.rot) {
+    dense_rows<D, 2 * NP>(p.rot, x, lane, xs);                                                       // E2
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2 * NP; ++i) hadamard_rows<D>(x[i], lane);                                  // E2
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    if (2 * (pair0 + j) >= p.n_tokens) break;
+    float y[2][E];
+    const bool okp[2] = {ok[2 * j], ok[2 * j + 1]};
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+      for (int e = 0; e < E; ++e) y[tk][e] = p.rot ? x[2 * j + tk][e] : x[2 * j + tk][e] * rd;       // E3 (Hadamard only)
+    finish_pair<D>(p, pair0 + j, kv, isv, lane, y, okp);
+  }
+}
+
+// grid (ceil(pairs / NP), Hkv, K|V), one wavefront each
+constexpr int kDensePairs = 8;
+template <int D, int NP>
 __global__ __launch_bounds__(64) void compress_kernel(CompressParams p) {
-  encode_pair<D>(p, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
+  __shared__ __attribute__((aligned(16))) float xs[2 * NP * D];
+  encode_pairs<D, NP>(p, blockIdx.x * NP, blockIdx.y, blockIdx.z, threadIdx.x, xs);
 }
 
 // ------------------------------------------------------------ per-step append / evict
@@ -172,6 +255,7 @@ struct StepParams {
   const int32_t* qtab;
   int32_t* qlen;
   int qmax, qnb;
+  const float* rot;
 };
 
 // What the step does to sequence b, decided from its lengths before the
@@ -197,6 +281,7 @@ __device__ inline StepPlan step_plan(const StepParams& p, int b) {
 // never touch the same bytes.
 template <int D>
 __global__ __launch_bounds__(64) void append_evict_kernel(StepParams p) {
+  __shared__ __attribute__((aligned(16))) float xs[2 * D];
   const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z >> 1, isv = blockIdx.z & 1, lane = threadIdx.x;
   const StepPlan s = step_plan(p, b);
   if (x == kBlock / 2) {
@@ -232,7 +317,8 @@ __global__ __launch_bounds__(64) void append_evict_kernel(StepParams p) {
   c.dst_table = p.qtab + (size_t)b * p.qmax;
   c.dst_num_blocks = p.qnb;
   c.dst_start = s.m;
-  encode_pair<D>(c, x, kv, isv, lane);
+  c.rot = p.rot;
+  encode_pairs<D, 1>(c, x, kv, isv, lane, xs);
 }
 
 // After the encode has read the old first block: lengths, and the rotation
@@ -275,11 +361,22 @@ hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream) {
   p.dst_table = d->dst_block_table;
   p.dst_num_blocks = d->dst_num_blocks;
   p.dst_start = d->dst_start;
-  dim3 grid((d->n_tokens + 1) / 2, d->Hkv, 2);
-  if (d->d == 64)
-    hipLaunchKernelGGL(compress_kernel<64>, grid, dim3(64), 0, stream, p);
-  else
-    hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(64), 0, stream, p);
+  p.rot = d->rotation;
+  // a given rotation: 8 pairs per wavefront share each load of R
+  const int pairs = (d->n_tokens + 1) / 2;
+  if (p.rot) {
+    dim3 grid((pairs + kDensePairs - 1) / kDensePairs, d->Hkv, 2);
+    if (d->d == 64)
+      hipLaunchKernelGGL((compress_kernel<64, kDensePairs>), grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((compress_kernel<128, kDensePairs>), grid, dim3(64), 0, stream, p);
+  } else {
+    dim3 grid(pairs, d->Hkv, 2);
+    if (d->d == 64)
+      hipLaunchKernelGGL((compress_kernel<64, 1>), grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((compress_kernel<128, 1>), grid, dim3(64), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -304,6 +401,7 @@ hipError_t launch_append_evict(const akv_append_desc* d, hipStream_t stream) {
   p.qlen = d->quant_lengths;
   p.qmax = d->quant_max_blocks;
   p.qnb = d->quant_num_blocks;
+  p.rot = d->rotation;
   dim3 grid(kBlock / 2 + 1, d->Hkv, 2 * d->B);
   if (d->d == 64)
     hipLaunchKernelGGL(append_evict_kernel<64>, grid, dim3(64), 0, stream, p);

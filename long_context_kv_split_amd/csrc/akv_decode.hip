@@ -475,7 +475,11 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   // rotation work split: wave w takes heads 2w, 2w+1; lane holds dims QV*(lane%32).. of head 2w + lane/32
   const int rh = 2 * w + (lane >> 5), rd0 = QV * (lane & 31);
   float qv[QV];
-  {
+  if (p.rot) {  // rotated once per call by qrot_kernel
+    const float* qsrc = p.qrot + ((size_t)b * p.Hq + kv * G + min(rh, G - 1)) * D + rd0;
+#pragma unroll
+    for (int e = 0; e < QV; ++e) qv[e] = qsrc[e];
+  } else {
     const uint16_t* qsrc = p.q + ((size_t)b * p.Hq + kv * G + min(rh, G - 1)) * D + rd0;
 #pragma unroll
     for (int e = 0; e < QV; ++e) qv[e] = bf16_bits_to_float(qsrc[e]);
@@ -525,24 +529,27 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
 
   // rotated, pre-scaled query q' = H q * (RN(1/sqrt d) * scale * log2 e):
   // butterflies inside the lane for h < QV, across lanes (xor h/QV) above
+  // (with a given rotation R, q' = (R q) * scale * log2 e, R q already done)
+  if (!p.rot) {
 #pragma unroll
-  for (int h = 1; h < QV; h <<= 1)
+    for (int h = 1; h < QV; h <<= 1)
 #pragma unroll
-    for (int e = 0; e < QV; ++e)
-      if (!(e & h)) {
-        float a = qv[e], c = qv[e + h];
-        qv[e] = a + c;
-        qv[e + h] = a - c;
-      }
+      for (int e = 0; e < QV; ++e)
+        if (!(e & h)) {
+          float a = qv[e], c = qv[e + h];
+          qv[e] = a + c;
+          qv[e + h] = a - c;
+        }
 #pragma unroll
-  for (int e = 0; e < QV; ++e) {
-    qv[e] = lane_butterfly<1>(qv[e], lane);
-    qv[e] = lane_butterfly<2>(qv[e], lane);
-    qv[e] = lane_butterfly<4>(qv[e], lane);
-    qv[e] = lane_butterfly<8>(qv[e], lane);
-    qv[e] = lane_butterfly<16>(qv[e], lane);
+    for (int e = 0; e < QV; ++e) {
+      qv[e] = lane_butterfly<1>(qv[e], lane);
+      qv[e] = lane_butterfly<2>(qv[e], lane);
+      qv[e] = lane_butterfly<4>(qv[e], lane);
+      qv[e] = lane_butterfly<8>(qv[e], lane);
+      qv[e] = lane_butterfly<16>(qv[e], lane);
+    }
   }
-  const float qmul = inv_sqrt_d(D) * p.qscale2;
+  const float qmul = (p.rot ? 1.0f : inv_sqrt_d(D)) * p.qscale2;
   // staged q' rows of D + 4 floats: the 8 rows read by one 128-bit LDS read
   // start in distinct banks
   constexpr int QP = D + 4;
@@ -802,13 +809,16 @@ __device__ inline float wave_max(float x) {
 //   (3) thread (phase, float4 column) sums w_s o_s over splits phase,
 //       phase + PH, ... with plain FMAs, the phases are added in order;
 //   (4) wave 0 inverse-rotates the compressed-tier output (once per head) and
-//       merges the two tiers.
+//       merges the two tiers.  With a given rotation R the inverse R^T o is
+//       a product of all threads between (3) and (4): thread (slice, float4
+//       column) takes rows slice*RR.. of R, requested at the start.
 // Inactive splits (past a sequence's length) are skipped, never multiplied,
 // so whatever their workspace rows hold cannot leak in.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
-  constexpr int C4 = D / 4, PH = kMergeThreads / C4, E = D / 64, K = 8;
+  constexpr int C4 = D / 4, PH = kMergeThreads / C4, E = D / 64, K = 8, RR = D / PH;
   __shared__ float wsh[AKV_MAX_SPLITS];
+  __shared__ float rot_in[D];  // compressed-tier output in rotated space (given rotation)
   __shared__ float stats[2][3];  // per tier: lse, nan flag, empty flag
   __shared__ __attribute__((aligned(16))) float4v phase[2][PH * C4];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -829,6 +839,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   for (int k = 0; k < K; ++k) {
     const int s = ph + k * PH;
     xo[k] = *reinterpret_cast<const float4v*>(p.part_o + (base + (s < S ? s : 0)) * D + 4 * c4);
+  }
+  float4v rr[RR];  // rows ph*RR.. of a given rotation, columns 4*c4..
+  if (p.rot) {
+#pragma unroll
+    for (int r = 0; r < RR; ++r)
+      rr[r] = *reinterpret_cast<const float4v*>(p.rot + (size_t)(ph * RR + r) * D + 4 * c4);
   }
   __syncthreads();
   // (2)
@@ -878,6 +894,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   phase[0][ph * C4 + c4] = aq;
   phase[1][ph * C4 + c4] = ae;
   __syncthreads();
+  if (p.rot) {
+    // R^T o_rot: the phases of o_rot added in order, then per slice
+    // sum_k R[k][t] o_rot[k] over its rows in ascending k; the slices'
+    // partials replace phase[0], so (4) adds them like phases
+    if (tid < D) {
+      const float* f0 = reinterpret_cast<const float*>(phase[0]);
+      float v = 0.0f;
+#pragma unroll
+      for (int k = 0; k < PH; ++k) v += f0[k * D + tid];
+      rot_in[tid] = v;
+    }
+    __syncthreads();
+    float4v acc = float4v{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < RR; ++r) acc += rr[r] * rot_in[ph * RR + r];
+    phase[0][ph * C4 + c4] = acc;
+    __syncthreads();
+  }
   if (tid >= 64) return;
   // (4) wave 0: lane l owns dims l + 64 e
   const float* fq = reinterpret_cast<const float*>(phase[0]);
@@ -896,21 +930,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
     oe[e] = ve;
   }
   // inverse rotation of the compressed-tier output: (H o_rot) * RN(1/sqrt d)
+  // (a given rotation's R^T o_rot is already in oq)
+  float rd = inv_sqrt_d(D);
+  if (p.rot) {
+    rd = 1.0f;
+  } else {
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    oq[e] = lane_butterfly<1>(oq[e], tid);
-    oq[e] = lane_butterfly<2>(oq[e], tid);
-    oq[e] = lane_butterfly<4>(oq[e], tid);
-    oq[e] = lane_butterfly<8>(oq[e], tid);
-    oq[e] = lane_butterfly<16>(oq[e], tid);
-    oq[e] = lane_butterfly<32>(oq[e], tid);
+    for (int e = 0; e < E; ++e) {
+      oq[e] = lane_butterfly<1>(oq[e], tid);
+      oq[e] = lane_butterfly<2>(oq[e], tid);
+      oq[e] = lane_butterfly<4>(oq[e], tid);
+      oq[e] = lane_butterfly<8>(oq[e], tid);
+      oq[e] = lane_butterfly<16>(oq[e], tid);
+      oq[e] = lane_butterfly<32>(oq[e], tid);
+    }
+    if (E == 2) {
+      float a = oq[0], c = oq[E - 1];
+      oq[0] = a + c;
+      oq[E - 1] = a - c;
+    }
   }
-  if (E == 2) {
-    float a = oq[0], c = oq[E - 1];
-    oq[0] = a + c;
-    oq[E - 1] = a - c;
-  }
-  const float rd = inv_sqrt_d(D);
   const bool nanq = stats[0][1] != 0.0f, nane = stats[1][1] != 0.0f;
   const float lq = nanq ? __builtin_nanf("") : stats[0][0];
   const float le = nane ? __builtin_nanf("") : stats[1][0];
@@ -965,9 +1004,42 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* op, const f
   }
 }
 
+// q' = R q for every (sequence, query head), once per call, when the
+// compressed tier uses a given rotation R: thread i takes row i of R.
+// The query value is requested first and the whole row after it, so one
+// round trip covers both.
+template <int D>
+__global__ __launch_bounds__(D) void qrot_kernel(AttnParams p) {
+  __shared__ float qs[D];
+  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+  const uint16_t qb = p.q[((size_t)b * p.Hq + h) * D + i];
+  const float4v* row = reinterpret_cast<const float4v*>(p.rot + (size_t)i * D);
+  float4v r[D / 4];
+#pragma unroll
+  for (int k4 = 0; k4 < D / 4; ++k4) r[k4] = row[k4];
+  qs[i] = bf16_bits_to_float(qb);
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int k4 = 0; k4 < D / 4; ++k4)
+    acc += r[k4][0] * qs[4 * k4] + r[k4][1] * qs[4 * k4 + 1] + r[k4][2] * qs[4 * k4 + 2] + r[k4][3] * qs[4 * k4 + 3];
+  p.qrot[((size_t)b * p.Hq + h) * D + i] = acc;
+}
+
+hipError_t launch_decode_qrot(const AttnParams& p, int D, hipStream_t stream) {
+  if (!p.rot) return hipSuccess;
+  if (D == 64)
+    hipLaunchKernelGGL(qrot_kernel<64>, dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(qrot_kernel<128>, dim3(p.Hq, p.B), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream) {
   dim3 grid(p.Sq + p.Se, p.Hkv, p.B);
   dim3 mgrid(p.Hq, p.B);
+  hipError_t e = launch_decode_qrot(p, D, stream);
+  if (e != hipSuccess) return e;
   if (D == 64) {
     hipLaunchKernelGGL(split_decode_kernel<64>, grid, dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);

@@ -37,6 +37,11 @@ struct AttnParams {
   // use Hkv*32*d and Hkv*2*d; per-block records (codes, codes, scales,
   // scales of one block together) use the record size for all four.
   size_t q_code_stride, q_scale_stride;
+  // Rotation of the compressed tier: nullptr = the normalized Walsh-Hadamard
+  // rotation; else a float32 [d][d] orthogonal matrix R (codes hold R x).
+  // qrot: [B][Hq][d] float32 workspace for the queries rotated by R.
+  const float* rot;
+  float* qrot;
 };
 
 }  // namespace akv

@@ -81,11 +81,17 @@ class Pools:
 
 
 class DeviceWorkload:
-    """A workload resident in HBM, ready for akv_attend_decode / akv_attend_chunk."""
+    """A workload resident in HBM, ready for akv_attend_decode / akv_attend_chunk.
 
-    def __init__(self, w: Workload, device: str = "cuda", fill_quant: bool = True):
+    ``rotation`` (float32 [d, d] orthogonal, or None for the Walsh-Hadamard one)
+    is the compressed tier's rotation: every descriptor built here carries it."""
+
+    def __init__(self, w: Workload, device: str = "cuda", fill_quant: bool = True,
+                 rotation: Optional[np.ndarray] = None):
         self.w = w
         self.device = device
+        self.rotation = None if rotation is None else \
+            torch.from_numpy(np.ascontiguousarray(rotation, dtype=np.float32)).to(device)
         d, hkv = w.d, w.Hkv
         self.q = _dev(w.q, device)
         self.exact_len = _dev(w.exact_len, device)
@@ -139,7 +145,7 @@ class DeviceWorkload:
                 dst_k_codes=ptr(self.pools[0].kc), dst_v_codes=ptr(self.pools[0].vc),
                 dst_k_scales=ptr(self.pools[0].ks), dst_v_scales=ptr(self.pools[0].vs),
                 dst_block_table=ptr(dst_t), dst_max_blocks=w.quant_table.shape[1],
-                dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=0)
+                dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=0, rotation=ptr(self.rotation))
             akv.check(akv.akv_compress_evicted(desc, stream or stream_handle()))
             torch.cuda.synchronize()
             del dk, dv, dt
@@ -154,7 +160,7 @@ class DeviceWorkload:
             exact_num_blocks=max(1, w.exact_pool_blocks), k_codes=ptr(P.kc), v_codes=ptr(P.vc),
             k_scales=ptr(P.ks), v_scales=ptr(P.vs), quant_table=ptr(self.quant_table),
             quant_lengths=ptr(self.quant_len), quant_max_blocks=w.quant_table.shape[1],
-            quant_num_blocks=max(1, w.quant_pool_blocks))
+            quant_num_blocks=max(1, w.quant_pool_blocks), rotation=ptr(self.rotation))
 
     def context_desc(self, replica: int = 0) -> akv.ContextDesc:
         """Descriptor of this workload's device state for checkpoint save / restore."""
@@ -219,7 +225,7 @@ class DeviceWorkload:
             src_start=src_start, n_tokens=n,
             dst_k_codes=ptr(P.kc), dst_v_codes=ptr(P.vc), dst_k_scales=ptr(P.ks), dst_v_scales=ptr(P.vs),
             dst_block_table=ptr(self.quant_table[b]), dst_max_blocks=w.quant_table.shape[1],
-            dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=dst_start)
+            dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=dst_start, rotation=ptr(self.rotation))
 
     def read_codes(self, b: int, start: int = 0, n: Optional[int] = None, replica: int = 0):
         """Logical (codes, scales) of compressed tokens [start, start+n) of sequence b.
@@ -268,7 +274,7 @@ class DeviceWorkload:
         sq = w.split_tokens_quant if split_quant is None else split_quant
         return akv.AttnDesc(B=w.B, Hq=w.Hq, Hkv=w.Hkv, d=w.d, Tq=w.Tq, softmax_scale=0.0, q=ptr(self.q),
                             exact=exact, quant=quant, split_tokens_exact=se, split_tokens_quant=sq,
-                            o=ptr(self.o), lse=ptr(self.lse))
+                            o=ptr(self.o), lse=ptr(self.lse), rotation=ptr(self.rotation))
 
     def ensure_ws(self, desc: akv.AttnDesc, chunk: bool = False) -> None:
         need = (akv.akv_chunk_workspace_bytes if chunk else akv.akv_decode_workspace_bytes)(desc)

@@ -334,3 +334,20 @@ def test_staged_decode_validation_order():
     assert call(staged_desc, sd(ring=FAKE + 0xC000010)) == akv.AKV_ERR_ALIGN
     assert call(staged_desc, ws=0) == akv.AKV_ERR_WORKSPACE
     assert call(staged_desc, sd(ring_bytes=1 << 16)) == akv.AKV_ERR_WORKSPACE  # a slot below one split
+
+
+def test_rotation_field():
+    """A given rotation: 16-byte aligned, refused by the chunk, and the decode
+    workspace grows by the rotated queries (4 B * Hq * d bytes, 256-aligned)."""
+    d = good_desc()
+    need = akv.akv_decode_workspace_bytes(d)
+    dr = good_desc(rotation=FAKE + 0x800000)
+    need_r = akv.akv_decode_workspace_bytes(dr)
+    extra = 4 * d.B * d.Hq * d.d
+    assert need + extra <= need_r <= need + extra + 256
+    assert call(dr, ws_bytes=need_r - 1) == akv.AKV_ERR_WORKSPACE
+    assert call(good_desc(rotation=FAKE + 8)) == akv.AKV_ERR_ALIGN
+    assert call(good_desc(Tq=4, rotation=FAKE + 0x800000), chunk=True) == akv.AKV_ERR_UNSUPPORTED
+    assert "rotation" in akv.akv_last_error()
+    assert akv.akv_compress_evicted(compress_desc(rotation=FAKE + 4)) == akv.AKV_ERR_ALIGN
+    assert akv.akv_append_evict(append_desc(rotation=FAKE + 4)) == akv.AKV_ERR_ALIGN
