@@ -21,6 +21,9 @@ precision):
   bit for bit, the encoder emulates the float32 operation sequence of the
   encode steps E1-E9 exactly (each numpy float32 operation is one IEEE
   round-to-nearest-even operation, with no fused multiply-add);
+* the same compact form at 2 and 3 bits (``width``): the 4- and 8-level
+  Lloyd-Max tables for N(0,1) in place of the 16-level one, every other step
+  unchanged;
 * the log-sum-exp merge of normalized partials (the attention statistic added
   to the paged-attention path, "Bringing a serving stack up on new silicon",
   section "What I built"), for the standalone merge entry point.
@@ -42,6 +45,7 @@ import numpy as np
 
 GROUP = 32      # elements per scale group
 LEVELS = 16     # 4-bit codes
+WIDTHS = (2, 3, 4)  # code widths in bits (2 ** width levels)
 
 
 # ---------------------------------------------------------------- bit helpers
@@ -133,21 +137,30 @@ def _inv_upper_tail(p: float) -> float:
 _TABLE_CACHE: Dict[str, np.ndarray] = {}
 
 
-def centroids_f32() -> np.ndarray:
-    """The 16 Lloyd-Max levels rounded to float32 (the frozen table)."""
-    if "c" not in _TABLE_CACHE:
-        _TABLE_CACHE["c"] = lloyd_max_gaussian().astype(np.float32)
-    return _TABLE_CACHE["c"]
+def centroids_f32(width: int = 4) -> np.ndarray:
+    """The 2**width Lloyd-Max levels rounded to float32 (the frozen table)."""
+    if width not in WIDTHS:
+        raise ValueError(f"code width {width} not in {WIDTHS}")
+    key = f"c{width}"
+    if key not in _TABLE_CACHE:
+        _TABLE_CACHE[key] = lloyd_max_gaussian(2 ** width).astype(np.float32)
+    return _TABLE_CACHE[key]
 
 
-def thresholds_f32(c32: Optional[np.ndarray] = None) -> np.ndarray:
-    """T_k = largest float32 <= (C_k + C_{k+1}) / 2, k = 0..14.
+def zero_code(width: int = 4) -> int:
+    """The code of an all-zero group (scale 0, so u = 0): the lower of the two
+    levels nearest 0, as an exact tie goes to the lower index."""
+    return 2 ** (width - 1) - 1
+
+
+def thresholds_f32(c32: Optional[np.ndarray] = None, width: int = 4) -> np.ndarray:
+    """T_k = largest float32 <= (C_k + C_{k+1}) / 2, k = 0..2**width - 2.
 
     The midpoint of two float32 values is exact in float64.  With these
     thresholds, code = #{k : u > T_k} is the nearest level, exact ties going
     to the lower index.
     """
-    c = centroids_f32() if c32 is None else c32
+    c = centroids_f32(width) if c32 is None else c32
     mid = (c[:-1].astype(np.float64) + c[1:].astype(np.float64)) / 2.0
     t = mid.astype(np.float32)
     over = t.astype(np.float64) > mid
@@ -230,14 +243,15 @@ def f32_to_f16_sat(s: np.ndarray) -> np.ndarray:
     return s.astype(np.float16)
 
 
-def encode(bits: np.ndarray, rotation: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+def encode(bits: np.ndarray, rotation: Optional[np.ndarray] = None, width: int = 4) -> Tuple[np.ndarray, np.ndarray]:
     """E1-E8 for vectors of bf16 bit patterns shaped [..., d].
 
-    Returns (codes uint8 [..., d] in 0..15, scales as uint16 fp16 bit patterns
-    [..., d/32]).  Nibble packing (E9) is a storage detail: see pack_nibbles.
-    With ``rotation`` (float32 [d, d], orthogonal) E2 is dense_rotate_f32 and
-    E3 is skipped; otherwise E2 is the Hadamard butterflies and E3 the
-    1/sqrt(d) normalization.
+    Returns (codes uint8 [..., d] in 0..2**width - 1, scales as uint16 fp16
+    bit patterns [..., d/32]).  Packing (E9) is a storage detail: see
+    pack_nibbles.  With ``rotation`` (float32 [d, d], orthogonal) E2 is
+    dense_rotate_f32 and E3 is skipped; otherwise E2 is the Hadamard
+    butterflies and E3 the 1/sqrt(d) normalization.  ``width`` picks the
+    Lloyd-Max table (E8); every other step is the same at every width.
     """
     bits = np.asarray(bits, dtype=np.uint16)
     d = bits.shape[-1]
@@ -253,18 +267,18 @@ def encode(bits: np.ndarray, rotation: Optional[np.ndarray] = None) -> Tuple[np.
     yg = y.reshape(*y.shape[:-1], d // GROUP, GROUP)
     with np.errstate(divide="ignore", invalid="ignore"):
         u = yg / s[..., None]                             # E7
-    codes = nearest_code(u)                               # E8
-    codes[s == 0] = 7                                     # zero scale: u == 0 -> lower of C7/C8
+    codes = nearest_code(u, width)                        # E8
+    codes[s == 0] = zero_code(width)                      # zero scale: u == 0 -> lower of the two middle levels
     return codes.reshape(bits.shape), s16.view(np.uint16)
 
 
-def nearest_code(u: np.ndarray) -> np.ndarray:
+def nearest_code(u: np.ndarray, width: int = 4) -> np.ndarray:
     """E8: index of the nearest float32 level to float32 u, exact ties to the lower index.
 
     Equals #{k : u > T_k} with the round-down midpoints T_k (a binary search
     over the sorted thresholds counts them).
     """
-    t = thresholds_f32()
+    t = thresholds_f32(width=width)
     return np.searchsorted(t, np.asarray(u, dtype=np.float32), side="left").astype(np.uint8)
 
 
@@ -282,19 +296,20 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant_rotated(codes: np.ndarray, scales16: np.ndarray) -> np.ndarray:
+def dequant_rotated(codes: np.ndarray, scales16: np.ndarray, width: int = 4) -> np.ndarray:
     """Rotated-space reconstruction C[code] * scale, exact in float64."""
-    c = centroids_f32().astype(np.float64)
+    c = centroids_f32(width).astype(np.float64)
     d = codes.shape[-1]
     s = f16_bits_to_f64(scales16)
     vals = c[codes.astype(np.int64)].reshape(*codes.shape[:-1], d // GROUP, GROUP)
     return (vals * s[..., None]).reshape(codes.shape)
 
 
-def dequant(codes: np.ndarray, scales16: np.ndarray, rotation: Optional[np.ndarray] = None) -> np.ndarray:
+def dequant(codes: np.ndarray, scales16: np.ndarray, rotation: Optional[np.ndarray] = None,
+            width: int = 4) -> np.ndarray:
     """Unrotated reconstruction: (H/sqrt(d)) @ rotated with the explicit matrix, or
     R^T @ rotated for a given rotation R (orthogonal, so R^T undoes it)."""
-    r = dequant_rotated(codes, scales16)
+    r = dequant_rotated(codes, scales16, width)
     d = r.shape[-1]
     if rotation is not None:
         return r @ np.asarray(rotation, dtype=np.float64)   # row-vector form of R^T @ r
@@ -327,12 +342,12 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 def history_f64(k_exact_bits: np.ndarray, v_exact_bits: np.ndarray,
                 kq_codes: Optional[np.ndarray], kq_scales: Optional[np.ndarray],
                 vq_codes: Optional[np.ndarray], vq_scales: Optional[np.ndarray],
-                head: int, rotation: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+                head: int, rotation: Optional[np.ndarray] = None, width: int = 4) -> Tuple[np.ndarray, np.ndarray]:
     """Attended history of one kv head: compressed tier first, then exact tier."""
     ks, vs = [], []
     if kq_codes is not None and kq_codes.shape[0]:
-        ks.append(dequant(kq_codes[:, head], kq_scales[:, head], rotation))
-        vs.append(dequant(vq_codes[:, head], vq_scales[:, head], rotation))
+        ks.append(dequant(kq_codes[:, head], kq_scales[:, head], rotation, width))
+        vs.append(dequant(vq_codes[:, head], vq_scales[:, head], rotation, width))
     if k_exact_bits.shape[0]:
         ks.append(bf16_to_f64(k_exact_bits[:, head]))
         vs.append(bf16_to_f64(v_exact_bits[:, head]))
@@ -345,7 +360,8 @@ def history_f64(k_exact_bits: np.ndarray, v_exact_bits: np.ndarray,
 def decode_sequence(q_bits: np.ndarray, k_exact_bits, v_exact_bits,
                     kq_codes, kq_scales, vq_codes, vq_scales,
                     scale: Optional[float] = None, causal_tail: int = 0,
-                    heads: Optional[Sequence[int]] = None, rotation: Optional[np.ndarray] = None):
+                    heads: Optional[Sequence[int]] = None, rotation: Optional[np.ndarray] = None,
+                    width: int = 4):
     """Attention of one sequence's queries over its whole two-tier history.
 
     q_bits [Tq, Hq, d] bf16; exact tier [Ne, Hkv, d] bf16; compressed tier as
@@ -367,7 +383,8 @@ def decode_sequence(q_bits: np.ndarray, k_exact_bits, v_exact_bits,
         hs = [h for h in range(kv * G, (kv + 1) * G) if h in want]
         if not hs:
             continue
-        k, v = history_f64(k_exact_bits, v_exact_bits, kq_codes, kq_scales, vq_codes, vq_scales, kv, rotation)
+        k, v = history_f64(k_exact_bits, v_exact_bits, kq_codes, kq_scales, vq_codes, vq_scales, kv, rotation,
+                           width)
         mask = None
         if causal_tail:
             n = k.shape[0]
@@ -421,7 +438,7 @@ def encode_tier(src_bits: List[np.ndarray]):
     return [encode(x) for x in src_bits]
 
 
-def reference_outputs(w, encoded_k=None, encoded_v=None, heads=None, seqs=None, rotation=None):
+def reference_outputs(w, encoded_k=None, encoded_v=None, heads=None, seqs=None, rotation=None, width=4):
     """o [B, Tq, Hq, d] and lse [B, Tq, Hq] (float64) for a synth.Workload-like object.
 
     ``w`` needs: q, exact_k, exact_v, quant_k_src, quant_v_src, causal_tail.
@@ -433,13 +450,13 @@ def reference_outputs(w, encoded_k=None, encoded_v=None, heads=None, seqs=None, 
     lse = np.full((B, Tq, Hq), np.nan)
     for b in (range(B) if seqs is None else seqs):
         if encoded_k is None:
-            kc, ks = encode(w.quant_k_src[b], rotation)
-            vc, vs = encode(w.quant_v_src[b], rotation)
+            kc, ks = encode(w.quant_k_src[b], rotation, width)
+            vc, vs = encode(w.quant_v_src[b], rotation, width)
         else:
             kc, ks = encoded_k[b]
             vc, vs = encoded_v[b]
         ob, lb = decode_sequence(w.q[b], w.exact_k[b], w.exact_v[b], kc, ks, vc, vs,
-                                 causal_tail=w.causal_tail, heads=heads, rotation=rotation)
+                                 causal_tail=w.causal_tail, heads=heads, rotation=rotation, width=width)
         o[b], lse[b] = ob, lb
     return o, lse
 

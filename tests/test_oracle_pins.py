@@ -587,3 +587,93 @@ def test_qr_round_trip_and_attention_are_lloyd_max_sized():
     oe, le = O.attention(q, x, x, 1 / np.sqrt(d))
     oq, lq = O.attention(q, xh, xh, 1 / np.sqrt(d))
     assert np.max(np.abs(le - lq)) < 0.5 and np.max(np.abs(oe - oq)) < 0.2
+
+
+# ----------------------------------------------- code widths 2 and 3 (4 / 8 levels)
+
+# Max (1960), "Quantizing for minimum distortion", table of the minimum
+# mean-square-error quantizer for a unit Gaussian: output levels (positive
+# half) and the distortion, to the printed precision.
+MAX_1960 = {2: ([0.4528, 1.510], 0.1175), 3: ([0.2451, 0.7560, 1.344, 2.152], 0.03455)}
+
+
+@pytest.mark.parametrize("width", [2, 3])
+def test_lloyd_max_narrow_tables_match_max_1960_and_fixed_point(width):
+    from scipy import integrate, stats
+    n_lv = 2 ** width
+    c = O.lloyd_max_gaussian(n_lv)
+    assert np.all(np.diff(c) > 0) and np.array_equal(c, -c[::-1])
+    levels, mse_ref = MAX_1960[width]
+    assert np.allclose(c[n_lv // 2:], levels, atol=6e-4, rtol=0)
+    edges = np.concatenate([[-np.inf], (c[:-1] + c[1:]) / 2, [np.inf]])
+    n = stats.norm
+    mse = 0.0
+    for k in range(n_lv):
+        mass = integrate.quad(n.pdf, edges[k], edges[k + 1], epsabs=1e-15, epsrel=1e-13)[0]
+        mom = integrate.quad(lambda x: x * n.pdf(x), edges[k], edges[k + 1], epsabs=1e-15, epsrel=1e-13)[0]
+        assert abs(mom / mass - c[k]) < 1e-12
+        mse += integrate.quad(lambda x: (x - c[k]) ** 2 * n.pdf(x), edges[k], edges[k + 1], epsabs=1e-15)[0]
+    assert abs(mse - mse_ref) < 6e-5
+
+
+@pytest.mark.parametrize("width", [2, 3])
+def test_narrow_thresholds_and_nearest_code_brute_force(width):
+    n_lv = 2 ** width
+    c32 = O.centroids_f32(width)
+    assert np.array_equal(c32, O.lloyd_max_gaussian(n_lv).astype(np.float32))
+    t = O.thresholds_f32(width=width)
+    assert t.shape == (n_lv - 1,) and t[n_lv // 2 - 1] == 0.0
+    c = [Fraction(float(v)) for v in c32]
+    for k in range(n_lv - 1):
+        mid = (c[k] + c[k + 1]) / 2
+        assert Fraction(float(t[k])) <= mid < Fraction(float(np.nextafter(t[k], np.float32(np.inf))))
+    us = list(RNG.normal(0, 1.5, 2000).astype(np.float32))
+    for k in range(n_lv - 1):
+        f = np.float32(float((c[k] + c[k + 1]) / 2))
+        us += [f, np.nextafter(f, np.float32(-9)), np.nextafter(f, np.float32(9))]
+    us += [np.float32(0.0), np.float32(-0.0), np.float32(40.0), np.float32(-40.0)]
+    u = np.array(us, dtype=np.float32)
+    got = O.nearest_code(u, width)
+    for ui, gi in zip(u, got):
+        fu = Fraction(float(ui))
+        best = min(range(n_lv), key=lambda k: (abs(fu - c[k]), k))
+        assert gi == best, (width, ui, gi, best)
+
+
+@pytest.mark.parametrize("width", [2, 3])
+def test_narrow_encoder_zero_group_and_ties(width):
+    """All-zero groups give scale 0 and the lower middle code; x = H y / 16
+    puts u exactly on 0 where y = 0 (the middle tie), on the sign side elsewhere."""
+    zc = O.zero_code(width)
+    codes, scales = O.encode(np.zeros((2, 64), dtype=np.uint16), width=width)
+    assert np.all(codes == zc) and np.all(scales == 0)
+    d = 128
+    h = O.sylvester_hadamard(d)
+    for _ in range(10):
+        y = RNG.integers(-3, 4, size=d)
+        y[RNG.choice(d, 16, replace=False)] = 0
+        bits = _bf16((h @ y) / 16.0)
+        codes, _ = O.encode(bits[None, :], width=width)
+        assert np.all(codes[0][y == 0] == zc)
+        assert np.all(codes[0][y > 0] > zc) and np.all(codes[0][y < 0] <= zc)
+        assert codes.max() < 2 ** width
+
+
+def test_narrow_round_trip_errors_follow_the_tables():
+    """Round-trip error of Gaussian vectors is near each table's distortion
+    (0.1175, 0.0346, 0.0095 of the signal power), and the same vectors
+    encoded at a lower width never reconstruct better."""
+    d = 128
+    x = _bf16(RNG.standard_normal((2000, d)))
+    xf = O.bf16_to_f64(x)
+    rel = {}
+    for width, lo, hi in ((2, 0.10, 0.14), (3, 0.029, 0.041), (4, 0.007, 0.013)):
+        codes, scales = O.encode(x, width=width)
+        rel[width] = np.sum((O.dequant(codes, scales, width=width) - xf) ** 2) / np.sum(xf ** 2)
+        assert lo < rel[width] < hi, (width, rel[width])
+        # scales do not depend on the width
+        assert np.array_equal(scales, O.encode(x)[1])
+    assert rel[2] > rel[3] > rel[4]
+    # decoding 2-bit codes with the 4-bit table is far off
+    codes, scales = O.encode(x, width=2)
+    assert np.sum((O.dequant(codes, scales) - xf) ** 2) / np.sum(xf ** 2) > 0.3
