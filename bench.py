@@ -113,12 +113,12 @@ def cpu_baseline(w, budget_s: float = 12.0):
 
 
 def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None, split_quant=None, split_exact=None,
-                 rotation=None):
+                 rotation=None, width=4):
     import torch
     from long_context_kv_split_amd import akv, harness, synth
     w = synth.make(name) if w is None else w
-    dw = harness.DeviceWorkload(w, rotation=rotation)
-    kv_bytes = w.kv_bytes()
+    dw = harness.DeviceWorkload(w, rotation=rotation, width=width)
+    kv_bytes = w.kv_bytes(width)
     n_rep = max(1, -(-min_bytes // kv_bytes))
     dw.add_replicas(n_rep)
     descs = [dw.desc(r, split_exact=split_exact, split_quant=split_quant) for r in range(n_rep)]
@@ -281,6 +281,24 @@ def bench_rotation(w, ev_hadamard_ms, stream, steps=500, warmup=20):
             "encode_gbps_hadamard": enc_bytes / (enc["hadamard"] * 1e-6) / 1e9}
 
 
+def bench_widths(w, ev4_ms, stream, steps=500, warmup=20):
+    """hybrid128k decode with the compressed tier at 2- and 3-bit codes (4- and
+    8-level Lloyd-Max tables) against the 4-bit call."""
+    out = {"workload": "hybrid128k decode, compressed tier at code widths 2, 3 (4: the headline call)",
+           "4": {"us_per_call": ev4_ms * 1e3, "kv_bytes": w.kv_bytes(4),
+                 "kv_gbps": w.kv_bytes(4) / (ev4_ms * 1e-3) / 1e9}}
+    for width in (3, 2):
+        _, dw, kv_bytes, n_rep, ev_ms, _ = bench_decode("hybrid128k", steps, warmup, stream, w=w, width=width)
+        out[str(width)] = {"us_per_call": ev_ms * 1e3, "kv_bytes": kv_bytes,
+                           "kv_gbps": kv_bytes / (ev_ms * 1e-3) / 1e9, "replicas": n_rep}
+        if width == 2:  # fewer bytes over the host link for the staged call
+            st = bench_staged(w, dw, ev_ms, stream)
+            out["2"]["staged"] = {k: st[k] for k in ("ring", "us_per_call", "host_to_device_bytes_per_call",
+                                                     "host_to_device_gbps", "plain_copy_gbps")}
+        del dw
+    return out
+
+
 def chunk_flops(w) -> float:
     """QK^T + PV multiply-adds x 2 of one chunk call: every query sees the whole
     history before the chunk plus, causally, (Tq + 1) / 2 chunk tokens on average."""
@@ -372,7 +390,7 @@ def main():
                              "kv_gbps": b2 / (e2 * 1e-3) / 1e9, "replicas": r2,
                              "decode_tokens_per_s": w2.B / (e2 * 1e-3)}
                 log(f"bench: {name} {e2 * 1e3:.2f} us/call")
-        staged = ckpt = step = rot = None
+        staged = ckpt = step = rot = widths = None
         if not args.no_extra:
             log("bench: host-staged decode")
             staged = bench_staged(w, dw, ev_ms, stream)
@@ -388,6 +406,10 @@ def main():
             rot = bench_rotation(w, ev_ms, stream)
             log(f"bench: QR decode {rot['decode_us_per_call']:.2f} us (Hadamard {rot['decode_us_per_call_hadamard']:.2f}), "
                 f"encode {rot['encode_us']:.1f} us (Hadamard {rot['encode_us_hadamard']:.1f})")
+            log("bench: code widths")
+            widths = bench_widths(w, ev_ms, stream)
+            log("bench: widths " + ", ".join(f"{k}-bit {v['us_per_call']:.2f} us ({v['kv_bytes'] / 1e6:.1f} MB)"
+                                            for k, v in widths.items() if k != "workload"))
         chunk = None
         if not args.no_chunk:
             log("bench: building chunk workload")
@@ -442,6 +464,7 @@ def main():
         out["staged"] = staged
         out["checkpoint"] = ckpt
         out["rotation"] = rot
+        out["code_widths"] = widths
         out["step"] = {"workload": "akv_append_evict per decode step, Hkv 4, d 128 (B1: window 4096; "
                                "B32: window 2048); one block move per sequence every 64 steps", **step}
     if chunk:

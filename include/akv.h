@@ -81,6 +81,28 @@
  * R^T times the rotated one.  The same R must be used to encode and to
  * attend.  akv_attend_chunk takes NULL only (AKV_ERR_UNSUPPORTED otherwise).
  *
+ * Code width: every descriptor that encodes or reads the compressed tier has
+ * a `code_bits` field, w = 4 (or 0) for the 16-level table and layout above,
+ * 2 or 3 for the 4- or 8-level Lloyd-Max table for N(0,1); only the table and
+ * the code bytes change, scales and every other step do not (an all-zero
+ * group gets code 2^(w-1) - 1).  A width-w code slab has 8*w*d bytes per
+ * (block p, kv head k), at byte offset (p*Hkv + k)*8*w*d.
+ *   w = 2: a pair plane.  A 4-bit field holds two codes (first | second << 2)
+ *     and a byte two fields (bits 0..3 and 4..7, h = 0 and 1):
+ *     K: token r owns bytes [r*d/4, (r+1)*d/4); byte (d/16)*a + 4*n + b holds
+ *       in field h dims 32(2n + h) + 8a + 2b and + 1;
+ *     V: byte ((c*4 + a)*16 + i)*(d/8) + 4*n + b holds in field h dim
+ *       16(2n + h) + i of tokens 32c + 8a + 2b and + 1.
+ *   w = 3: the pair plane of the codes' low two bits (16*d bytes), then a high
+ *     plane of their top bits (8*d bytes) where a 2-bit field holds the top
+ *     bits of two codes (first | second << 1):
+ *     K: token r owns bytes [r*d/8, (r+1)*d/8) of the high plane; with
+ *       M = d/32, row bits 8*M*a + 2*M*b + 2*m + {0, 1} hold dims
+ *       32m + 8a + 2b and + 1;
+ *     V: byte ((c*4 + a)*16 + i)*(d/16) + 4*n + b, bits 2*h + {0, 1}, holds
+ *       dim 16(4n + h) + i of tokens 32c + 8a + 2b and + 1.
+ * akv_attend_chunk takes w = 4 only (AKV_ERR_UNSUPPORTED otherwise).
+ *
  * Block tables: int32 [B][max_blocks]; entry j of row b is the pool block of
  * tier-local tokens [64j, 64j+64) of sequence b.  Tier lengths: int32 [B].
  * In the attended history of a sequence the compressed tier comes first
@@ -148,7 +170,8 @@ typedef struct akv_exact_tier {
   int32_t num_blocks;          /* blocks in each pool */
 } akv_exact_tier;
 
-/* Compressed (4-bit) tier of a batch.  Absent when max_blocks == 0. */
+/* Compressed tier of a batch (code width: akv_attn_desc.code_bits).  Absent
+ * when max_blocks == 0. */
 typedef struct akv_quant_tier {
   const uint8_t* k_codes;
   const uint8_t* v_codes;
@@ -177,6 +200,7 @@ typedef struct akv_attn_desc {
   float* o;                    /* fp32 [B][Tq][Hq][d] normalized output */
   float* lse;                  /* fp32 [B][Tq][Hq] natural-log sum of exp(scores) */
   const float* rotation;       /* NULL, or the compressed tier's rotation R (see "Rotation") */
+  int32_t code_bits;           /* compressed-tier code width: 0 or 4, 3, 2 (see "Code width") */
 } akv_attn_desc;
 
 typedef akv_attn_desc akv_decode_desc;
@@ -189,8 +213,8 @@ typedef akv_attn_desc akv_chunk_desc;
  * Walsh-Hadamard butterflies in fp32, scaled by RN(1/sqrt(d)), each 32-group
  * gets scale = fp16(sqrt(mean of squares)) and every element the index of
  * the nearest Lloyd-Max level to value/scale (exact ties to the lower index;
- * all-zero groups give index 7).  Codes and scales are bit-exact functions of
- * the input.  Source tokens [src_start, src_start+n_tokens) of the exact
+ * all-zero groups give index 7, or 2^(w-1) - 1 at code width w).  Codes and
+ * scales are bit-exact functions of the input.  Source tokens [src_start, src_start+n_tokens) of the exact
  * tier's block table land at compressed positions [dst_start, dst_start +
  * n_tokens).  dst_start must be even (two tokens share a V byte); for odd
  * n_tokens the unused half of the last V byte is written as 0. */
@@ -210,6 +234,7 @@ typedef struct akv_compress_desc {
   int32_t dst_max_blocks, dst_num_blocks;
   int32_t dst_start;
   const float* rotation;       /* NULL, or the rotation R (see "Rotation") */
+  int32_t code_bits;           /* 0 or 4, 3, 2 (see "Code width") */
 } akv_compress_desc;
 
 /* ABI version of the loaded library (AKV_ABI_VERSION at build time). */
@@ -232,8 +257,9 @@ akv_status akv_split_plan(const akv_attn_desc* desc, int32_t chunk, int32_t* out
 
 /* One sequence's compressed tier held in pinned host memory (hipHostMalloc):
  * ceil(length / 64) block records in token order (record i holds tokens
- * [64i, 64i + 64)), each 72*Hkv*d bytes: Hkv K-code slabs (32*d bytes each),
- * Hkv V-code slabs, Hkv K-scale slabs (2*d fp16 each), Hkv V-scale slabs,
+ * [64i, 64i + 64)), each (16w + 8)*Hkv*d bytes for code width w (72*Hkv*d
+ * at w = 4): Hkv K-code slabs (8*w*d bytes each), Hkv V-code slabs, Hkv
+ * K-scale slabs (2*d fp16 each), Hkv V-scale slabs,
  * with the per-slab layouts above.  This is the record layout of a
  * checkpoint image's compressed slots, so a sequence's slots of an image in
  * pinned memory serve directly. */
@@ -357,6 +383,7 @@ typedef struct akv_append_desc {
   int32_t* quant_lengths;      /* [B], updated in place */
   int32_t quant_max_blocks, quant_num_blocks;
   const float* rotation;       /* NULL, or the rotation R (see "Rotation") */
+  int32_t code_bits;           /* 0 or 4, 3, 2 (see "Code width") */
 } akv_append_desc;
 
 akv_status akv_append_evict(const akv_append_desc* desc, void* stream);
@@ -365,14 +392,16 @@ akv_status akv_append_evict(const akv_append_desc* desc, void* stream);
  * context is suspended and resumed without recomputing it).  The image of a
  * batch is a fixed-size byte string, every field little-endian:
  *   [0, 256)   header: "AKVCTX01" (8 bytes), then int32 B, Hkv, d,
- *              exact_max_blocks, quant_max_blocks, zeros up to 256;
+ *              exact_max_blocks, quant_max_blocks, code width w (2, 3
+ *              or 4), zeros up to 256;
  *   [256, 256 + 8B) int32 exact_lengths[b], quant_lengths[b] for b = 0..B-1,
  *              zeros up to the next multiple of 256 (offset E);
  *   at E:      for b, then slot j < exact_max_blocks: the exact block of
  *              tokens [64j, 64j + 64) as Hkv K slabs then Hkv V slabs
  *              (256*Hkv*d bytes, pool layouts above);
  *   then:      for b, then slot j < quant_max_blocks: K codes, V codes
- *              (32*d*Hkv bytes each), K scales, V scales (4*d*Hkv bytes each).
+ *              (8*w*d*Hkv bytes each), K scales, V scales (4*d*Hkv bytes
+ *              each).
  * Slots at or past ceil(length / 64) are zeros, as are the bytes of a slot
  * whose table entry is outside [0, num_blocks).  The image depends only on
  * the tokens (not on which pool blocks hold them), so a context restored into
@@ -392,6 +421,7 @@ typedef struct akv_context_desc {
   const int32_t* quant_table;  /* [B][quant_max_blocks] */
   int32_t* quant_lengths;      /* [B] */
   int32_t quant_max_blocks, quant_num_blocks;
+  int32_t code_bits;           /* 0 or 4, 3, 2 (see "Code width") */
 } akv_context_desc;
 
 /* Bytes of the image for desc's shape; 0 if desc is invalid. */

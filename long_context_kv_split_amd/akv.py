@@ -53,7 +53,7 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("struct_size", c_uint32), ("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("d", c_int32),
                 ("Tq", c_int32), ("softmax_scale", c_float), ("q", c_void_p), ("exact", ExactTier),
                 ("quant", QuantTier), ("split_tokens_exact", c_int32), ("split_tokens_quant", c_int32),
-                ("o", c_void_p), ("lse", c_void_p), ("rotation", c_void_p)]
+                ("o", c_void_p), ("lse", c_void_p), ("rotation", c_void_p), ("code_bits", c_int32)]
 
     def __init__(self, **kw):
         super().__init__(struct_size=ctypes.sizeof(AttnDesc), **kw)
@@ -65,7 +65,8 @@ class CompressDesc(ctypes.Structure):
                 ("src_num_blocks", c_int32), ("src_start", c_int32), ("n_tokens", c_int32),
                 ("dst_k_codes", c_void_p), ("dst_v_codes", c_void_p), ("dst_k_scales", c_void_p),
                 ("dst_v_scales", c_void_p), ("dst_block_table", c_void_p), ("dst_max_blocks", c_int32),
-                ("dst_num_blocks", c_int32), ("dst_start", c_int32), ("rotation", c_void_p)]
+                ("dst_num_blocks", c_int32), ("dst_start", c_int32), ("rotation", c_void_p),
+                ("code_bits", c_int32)]
 
     def __init__(self, **kw):
         super().__init__(struct_size=ctypes.sizeof(CompressDesc), **kw)
@@ -78,7 +79,7 @@ class AppendDesc(ctypes.Structure):
                 ("exact_num_blocks", c_int32), ("k_codes", c_void_p), ("v_codes", c_void_p),
                 ("k_scales", c_void_p), ("v_scales", c_void_p), ("quant_table", c_void_p),
                 ("quant_lengths", c_void_p), ("quant_max_blocks", c_int32), ("quant_num_blocks", c_int32),
-                ("rotation", c_void_p)]
+                ("rotation", c_void_p), ("code_bits", c_int32)]
 
     def __init__(self, **kw):
         super().__init__(struct_size=ctypes.sizeof(AppendDesc), **kw)
@@ -89,7 +90,8 @@ class ContextDesc(ctypes.Structure):
                 ("exact_k", c_void_p), ("exact_v", c_void_p), ("exact_table", c_void_p), ("exact_lengths", c_void_p),
                 ("exact_max_blocks", c_int32), ("exact_num_blocks", c_int32), ("k_codes", c_void_p),
                 ("v_codes", c_void_p), ("k_scales", c_void_p), ("v_scales", c_void_p), ("quant_table", c_void_p),
-                ("quant_lengths", c_void_p), ("quant_max_blocks", c_int32), ("quant_num_blocks", c_int32)]
+                ("quant_lengths", c_void_p), ("quant_max_blocks", c_int32), ("quant_num_blocks", c_int32),
+                ("code_bits", c_int32)]
 
     def __init__(self, **kw):
         super().__init__(struct_size=ctypes.sizeof(ContextDesc), **kw)

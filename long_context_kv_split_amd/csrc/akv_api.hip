@@ -46,6 +46,7 @@ akv_status fail(akv_status s, const char* fmt, ...) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool width_ok(int code_bits) { return code_bits == 0 || code_bits == 2 || code_bits == 3 || code_bits == 4; }
 
 int split_tokens(int v, int dflt) { return v ? v : dflt; }
 
@@ -93,6 +94,8 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   if (chunk && d->Tq > AKV_MAX_CHUNK) return fail(AKV_ERR_UNSUPPORTED, "chunk Tq %d > %d", d->Tq, AKV_MAX_CHUNK);
   if (chunk && e.max_blocks == 0) return fail(AKV_ERR_UNSUPPORTED, "chunk needs the exact tier (it holds the chunk)");
   if (chunk && d->rotation) return fail(AKV_ERR_UNSUPPORTED, "the chunk takes the Walsh-Hadamard rotation only");
+  if (!width_ok(d->code_bits)) return fail(AKV_ERR_UNSUPPORTED, "code_bits %d (supported: 2, 3, 4)", d->code_bits);
+  if (chunk && akv::code_width(d->code_bits) != 4) return fail(AKV_ERR_UNSUPPORTED, "the chunk takes 4-bit codes only");
   if (d->B > 65535 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
   int Pe, Pq;
   if (!chunk) {
@@ -213,7 +216,8 @@ akv::AttnParams make_params(const akv_attn_desc* d, const Plan& plan, void* ws) 
   p.part_base = 0;
   p.part_stride = plan.Sq + plan.Se;
   p.qlen_fixed = -1;
-  p.q_code_stride = (size_t)d->Hkv * 32 * d->d;
+  p.qw = akv::code_width(d->code_bits);
+  p.q_code_stride = (size_t)d->Hkv * 8 * p.qw * d->d;
   p.q_scale_stride = (size_t)d->Hkv * 2 * d->d;
   p.rot = d->rotation;
   p.qrot = d->rotation ? reinterpret_cast<float*>(base + plan.qrot_off) : nullptr;
@@ -337,9 +341,10 @@ akv_status akv_attend_decode_staged(const akv_attn_desc* desc, const akv_staging
   if ((s = check_ws(plan, ws, ws_bytes)) != AKV_OK) return s;
   const akv_quant_tier& q = desc->quant;
   // ring slots of whole compressed splits; a block is one record of
-  // Hkv*32*d K-code, Hkv*32*d V-code, Hkv*2*d K-scale and Hkv*2*d V-scale bytes / halves
+  // Hkv*8*w*d K-code, Hkv*8*w*d V-code (code width w), Hkv*2*d K-scale and
+  // Hkv*2*d V-scale bytes / halves
   const int D = desc->d, H = desc->Hkv;
-  const size_t code_bytes = (size_t)H * 32 * D, scale_bytes = (size_t)H * 4 * D;
+  const size_t code_bytes = (size_t)H * 8 * akv::code_width(desc->code_bits) * D, scale_bytes = (size_t)H * 4 * D;
   const size_t block_bytes = 2 * code_bytes + 2 * scale_bytes;
   const size_t slot_bytes = (st->ring_bytes / st->slots) & ~(size_t)255;
   const int slot_blocks = (int)std::min<size_t>(slot_bytes / block_bytes, 1 << 30);
@@ -445,6 +450,7 @@ akv_status akv_compress_evicted(const akv_compress_desc* d, void* stream) {
       (long long)d->dst_start + d->n_tokens > (long long)d->dst_max_blocks * AKV_BLOCK_TOKENS)
     return fail(AKV_ERR_SHAPE, "token range exceeds a block table");
   if (d->d != 64 && d->d != 128) return fail(AKV_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  if (!width_ok(d->code_bits)) return fail(AKV_ERR_UNSUPPORTED, "code_bits %d (supported: 2, 3, 4)", d->code_bits);
   if (d->dst_start & 1) return fail(AKV_ERR_UNSUPPORTED, "dst_start must be even");
   if (d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "Hkv must be <= 65535");
   if (!aligned(d->src_k, 2) || !aligned(d->src_v, 2) || !aligned(d->dst_k_scales, 2) ||
@@ -471,6 +477,7 @@ akv_status akv_append_evict(const akv_append_desc* d, void* stream) {
     return fail(AKV_ERR_SHAPE, "window %d needs %d exact-table entries (have %d)", d->window,
                 d->window / AKV_BLOCK_TOKENS + 1, d->exact_max_blocks);
   if (d->d != 64 && d->d != 128) return fail(AKV_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  if (!width_ok(d->code_bits)) return fail(AKV_ERR_UNSUPPORTED, "code_bits %d (supported: 2, 3, 4)", d->code_bits);
   if (d->B > 32767 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B must be <= 32767 and Hkv <= 65535");
   if (!aligned(d->new_k, 2) || !aligned(d->new_v, 2) || !aligned(d->exact_k, 2) || !aligned(d->exact_v, 2) ||
       !aligned(d->k_scales, 2) || !aligned(d->v_scales, 2) || !aligned(d->exact_table, 4) ||
@@ -496,6 +503,7 @@ static akv_status check_context(const akv_context_desc* d, const void* image, bo
   if ((d->exact_max_blocks > 0 && d->exact_num_blocks < 1) || (d->quant_max_blocks > 0 && d->quant_num_blocks < 1))
     return fail(AKV_ERR_SHAPE, "a present tier needs num_blocks >= 1");
   if (d->d != 64 && d->d != 128) return fail(AKV_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  if (!width_ok(d->code_bits)) return fail(AKV_ERR_UNSUPPORTED, "code_bits %d (supported: 2, 3, 4)", d->code_bits);
   if (d->B > 65535 || d->exact_max_blocks > (1 << 30) || d->quant_max_blocks > (1 << 30))
     return fail(AKV_ERR_UNSUPPORTED, "B must be <= 65535");
   if (!aligned(d->exact_k, 16) || !aligned(d->exact_v, 16) || !aligned(d->k_codes, 16) || !aligned(d->v_codes, 16) ||

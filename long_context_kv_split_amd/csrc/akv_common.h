@@ -30,6 +30,32 @@ __device__ __constant__ const uint32_t kThreshBits[15] = {
     0xBF05BC40u, 0xBE8435A2u, 0x00000000u, 0x3E8435A1u, 0x3F05BC40u,
     0x3F4CAF4Bu, 0x3F8CB565u, 0x3FB7F42Au, 0x3FEBF8D9u, 0x4019A6C3u};
 
+// The 4- and 8-level Lloyd-Max quantizers for N(0,1) (code widths 2 and 3),
+// solved and rounded the same way, with their round-down midpoints.
+__device__ __constant__ const uint32_t kLevelBits2[4] = {0xBFC1555Du, 0xBEE7D2C9u, 0x3EE7D2C9u, 0x3FC1555Du};
+__device__ __constant__ const uint32_t kThreshBits2[3] = {0xBF7B4A10u, 0x00000000u, 0x3F7B4A0Fu};
+__device__ __constant__ const uint32_t kLevelBits3[8] = {
+    0xC009B97Au, 0xBFAC0538u, 0xBF418990u, 0xBE7AF9F8u, 0x3E7AF9F8u, 0x3F418990u, 0x3FAC0538u, 0x4009B97Au};
+__device__ __constant__ const uint32_t kThreshBits3[7] = {
+    0xBFDFBC16u, 0xBF866500u, 0xBF002407u, 0x00000000u, 0x3F002407u, 0x3F866500u, 0x3FDFBC16u};
+
+// Code width of a descriptor's code_bits field (0 means 4).
+__host__ __device__ inline int code_width(int code_bits) { return code_bits == 0 ? 4 : code_bits; }
+
+// Level and threshold table of code width W.
+template <int W>
+__device__ inline const uint32_t* level_bits() {
+  if constexpr (W == 2) return kLevelBits2;
+  else if constexpr (W == 3) return kLevelBits3;
+  else return kLevelBits;
+}
+template <int W>
+__device__ inline const uint32_t* thresh_bits() {
+  if constexpr (W == 2) return kThreshBits2;
+  else if constexpr (W == 3) return kThreshBits3;
+  else return kThreshBits;
+}
+
 // RN_32(1/sqrt(d)) for the supported head dims.
 __host__ __device__ inline float inv_sqrt_d(int d) {
   return d == 64 ? 0.125f : __builtin_bit_cast(float, 0x3DB504F3u);

@@ -126,11 +126,77 @@ __device__ inline void dense_rows(const float* __restrict__ R, float (&x)[NT][D 
     for (int e = 0; e < E; ++e) x[t][e] = acc[t][e];
 }
 
+// E9 at code width W < 4 (the pair plane, then for W = 3 the high plane; the
+// layouts are those of include/akv.h): the pair's codes go to LDS (0 for a
+// missing token), then each lane assembles whole output bytes.  K rows of
+// missing tokens are not written; a V byte always is.
+template <int D, int W>
+__device__ inline void store_narrow(const CompressParams& p, size_t slab, int r0, int ntok, int isv, int lane,
+                                    const int (&code)[2][D / 64], const bool (&ok)[2], unsigned char* cs) {
+  constexpr int E = D / 64, M = D / 32;
+  __syncthreads();  // the previous pair's reads of cs are done
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+    for (int e = 0; e < E; ++e) cs[tk * D + lane + 64 * e] = (tk < ntok && ok[tk]) ? (unsigned char)code[tk][e] : 0;
+  __syncthreads();
+  if (!isv) {
+    uint8_t* kslab = p.dst_kc + slab * (8 * W * D);
+    for (int tk = 0; tk < 2; ++tk) {
+      if (!(tk < ntok && ok[tk])) continue;
+      const unsigned char* ct = cs + tk * D;
+      if (lane < D / 4) {  // pair plane: byte (d/16) a + 4 n + b of the row
+        const int a = lane / (D / 16), r = lane % (D / 16), n = r >> 2, b = r & 3;
+        int byte = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) byte |= (ct[32 * (2 * n + h) + 8 * a + 2 * b + e] & 3) << (4 * h + 2 * e);
+        kslab[(r0 + tk) * (D / 4) + lane] = (uint8_t)byte;
+      }
+      if (W == 3 && lane < D / 8) {  // high plane: row bit 8Ma + 2Mb + 2m + e
+        const int a = lane / M, q = lane % M;
+        int byte = 0;
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+          const int g = 8 * q + bit, b = g / (2 * M), rem = g % (2 * M), m = rem >> 1, e = rem & 1;
+          byte |= ((ct[32 * m + 8 * a + 2 * b + e] >> 2) & 1) << bit;
+        }
+        kslab[16 * D + (r0 + tk) * (D / 8) + lane] = (uint8_t)byte;
+      }
+    }
+  } else {
+    uint8_t* vslab = p.dst_vc + slab * (8 * W * D);
+    const int c = r0 >> 5, a = (r0 >> 3) & 3, b = (r0 >> 1) & 3;
+    for (int l = lane; l < D / 2; l += 64) {  // pair plane: dim 16(2n + h) + i
+      const int i = l & 15, n = l >> 4;
+      int byte = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) byte |= (cs[e * D + 16 * (2 * n + h) + i] & 3) << (4 * h + 2 * e);
+      vslab[((c * 4 + a) * 16 + i) * (D / 8) + 4 * n + b] = (uint8_t)byte;
+    }
+    if (W == 3) {
+      for (int l = lane; l < D / 4; l += 64) {  // high plane: dim 16(4n + h) + i
+        const int i = l & 15, n = l >> 4;
+        int byte = 0;
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) byte |= ((cs[e * D + 16 * (4 * n + h) + i] >> 2) & 1) << (2 * h + e);
+        vslab[16 * D + ((c * 4 + a) * 16 + i) * (D / 16) + 4 * n + b] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
 // E4..E9 for token pair `pair` (tokens 2 pair, 2 pair + 1 of the range) of
-// one (kv head, K|V), given its rotated values y (lane l: elements l + 64k).
-template <int D>
+// one (kv head, K|V), given its rotated values y (lane l: elements l + 64k),
+// at code width W (cs: 2 * D bytes of LDS, this wavefront's own).
+template <int D, int W>
 __device__ inline void finish_pair(const CompressParams& p, int pair, int kv, int isv, int lane,
-                                   const float (&y)[2][D / 64], const bool (&ok)[2]) {
+                                   const float (&y)[2][D / 64], const bool (&ok)[2], unsigned char* cs) {
   constexpr int E = D / 64;
   const int first = 2 * pair;
   const int ntok = min(2, p.n_tokens - first);
@@ -153,12 +219,12 @@ __device__ inline void finish_pair(const CompressParams& p, int pair, int kv, in
       hb = (uint16_t)__shfl((int)hb, lane & 32);            // broadcast group scale
       s16[tk][e] = hb;
       float s = __half2float(__ushort_as_half(hb));         // E6
-      int c = 7;
+      int c = (1 << (W - 1)) - 1;                           // the lower middle level
       if (s != 0.0f) {
         float u = y[tk][e] / s;                             // E7
         c = 0;
 #pragma unroll
-        for (int k = 0; k < 15; ++k) c += (u > __builtin_bit_cast(float, kThreshBits[k])) ? 1 : 0;  // E8
+        for (int k = 0; k < (1 << W) - 1; ++k) c += (u > __builtin_bit_cast(float, thresh_bits<W>()[k])) ? 1 : 0;  // E8
       }
       code[tk][e] = c;
     }
@@ -171,6 +237,15 @@ __device__ inline void finish_pair(const CompressParams& p, int pair, int kv, in
   const int r0 = pos0 & 63;
   const size_t slab = (size_t)dblk * p.Hkv + kv;
   uint16_t* scales = (isv ? p.dst_vs : p.dst_ks) + slab * (2 * D);
+  if constexpr (W < 4) {
+    store_narrow<D, W>(p, slab, r0, ntok, isv, lane, code, ok, cs);
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (tk < ntok && ok[tk] && (lane & 31) == 0) scales[((lane + 64 * e) >> 5) * kBlock + r0 + tk] = s16[tk][e];
+    return;
+  }
   if (!isv) {
     uint8_t* codes = p.dst_kc + slab * (32 * D);
 #pragma unroll
@@ -203,8 +278,9 @@ __device__ inline void finish_pair(const CompressParams& p, int pair, int kv, in
 // Encode token pairs pair0 .. pair0 + NP - 1 of one (kv head, K|V): one
 // wavefront, lane l holding elements l + 64k.  With a given rotation the NP
 // pairs share the loads of R (xs: 2 * NP * D floats of LDS).
-template <int D, int NP>
-__device__ inline void encode_pairs(const CompressParams& p, int pair0, int kv, int isv, int lane, float* xs) {
+template <int D, int NP, int W>
+__device__ inline void encode_pairs(const CompressParams& p, int pair0, int kv, int isv, int lane, float* xs,
+                                    unsigned char* cs) {
   constexpr int E = D / 64;
   const float rd = inv_sqrt_d(D);
   float x[2 * NP][E];
@@ -226,16 +302,17 @@ __device__ inline void encode_pairs(const CompressParams& p, int pair0, int kv, 
     for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
       for (int e = 0; e < E; ++e) y[tk][e] = p.rot ? x[2 * j + tk][e] : x[2 * j + tk][e] * rd;       // E3 (Hadamard only)
-    finish_pair<D>(p, pair0 + j, kv, isv, lane, y, okp);
+    finish_pair<D, W>(p, pair0 + j, kv, isv, lane, y, okp, cs);
   }
 }
 
 // grid (ceil(pairs / NP), Hkv, K|V), one wavefront each
 constexpr int kDensePairs = 8;
-template <int D, int NP>
+template <int D, int NP, int W>
 __global__ __launch_bounds__(64) void compress_kernel(CompressParams p) {
   __shared__ __attribute__((aligned(16))) float xs[2 * NP * D];
-  encode_pairs<D, NP>(p, blockIdx.x * NP, blockIdx.y, blockIdx.z, threadIdx.x, xs);
+  __shared__ unsigned char cs[2 * D];
+  encode_pairs<D, NP, W>(p, blockIdx.x * NP, blockIdx.y, blockIdx.z, threadIdx.x, xs, cs);
 }
 
 // ------------------------------------------------------------ per-step append / evict
@@ -279,9 +356,10 @@ __device__ inline StepPlan step_plan(const StepParams& p, int b) {
 // the sequence evicts), x == 32 writes the new token; z = 2 b + (K|V).  The
 // append writes block n / 64 >= 1 while the encode reads block 0, so the two
 // never touch the same bytes.
-template <int D>
+template <int D, int W>
 __global__ __launch_bounds__(64) void append_evict_kernel(StepParams p) {
   __shared__ __attribute__((aligned(16))) float xs[2 * D];
+  __shared__ unsigned char cs[2 * D];
   const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z >> 1, isv = blockIdx.z & 1, lane = threadIdx.x;
   const StepPlan s = step_plan(p, b);
   if (x == kBlock / 2) {
@@ -318,7 +396,7 @@ __global__ __launch_bounds__(64) void append_evict_kernel(StepParams p) {
   c.dst_num_blocks = p.qnb;
   c.dst_start = s.m;
   c.rot = p.rot;
-  encode_pairs<D, 1>(c, x, kv, isv, lane, xs);
+  encode_pairs<D, 1, W>(c, x, kv, isv, lane, xs, cs);
 }
 
 // After the encode has read the old first block: lengths, and the rotation
@@ -345,6 +423,26 @@ __global__ __launch_bounds__(64) void step_commit_kernel(StepParams p) {
   p.qlen[b] = s.m + kBlock;
 }
 
+template <int D, int NP>
+void launch_compress_w(int W, dim3 grid, hipStream_t stream, const CompressParams& p) {
+  if (W == 2)
+    hipLaunchKernelGGL((compress_kernel<D, NP, 2>), grid, dim3(64), 0, stream, p);
+  else if (W == 3)
+    hipLaunchKernelGGL((compress_kernel<D, NP, 3>), grid, dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((compress_kernel<D, NP, 4>), grid, dim3(64), 0, stream, p);
+}
+
+template <int D>
+void launch_append_w(int W, dim3 grid, hipStream_t stream, const StepParams& p) {
+  if (W == 2)
+    hipLaunchKernelGGL((append_evict_kernel<D, 2>), grid, dim3(64), 0, stream, p);
+  else if (W == 3)
+    hipLaunchKernelGGL((append_evict_kernel<D, 3>), grid, dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((append_evict_kernel<D, 4>), grid, dim3(64), 0, stream, p);
+}
+
 hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream) {
   CompressParams p;
   p.Hkv = d->Hkv;
@@ -364,18 +462,19 @@ hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream) {
   p.rot = d->rotation;
   // a given rotation: 8 pairs per wavefront share each load of R
   const int pairs = (d->n_tokens + 1) / 2;
+  const int W = code_width(d->code_bits);
   if (p.rot) {
     dim3 grid((pairs + kDensePairs - 1) / kDensePairs, d->Hkv, 2);
     if (d->d == 64)
-      hipLaunchKernelGGL((compress_kernel<64, kDensePairs>), grid, dim3(64), 0, stream, p);
+      launch_compress_w<64, kDensePairs>(W, grid, stream, p);
     else
-      hipLaunchKernelGGL((compress_kernel<128, kDensePairs>), grid, dim3(64), 0, stream, p);
+      launch_compress_w<128, kDensePairs>(W, grid, stream, p);
   } else {
     dim3 grid(pairs, d->Hkv, 2);
     if (d->d == 64)
-      hipLaunchKernelGGL((compress_kernel<64, 1>), grid, dim3(64), 0, stream, p);
+      launch_compress_w<64, 1>(W, grid, stream, p);
     else
-      hipLaunchKernelGGL((compress_kernel<128, 1>), grid, dim3(64), 0, stream, p);
+      launch_compress_w<128, 1>(W, grid, stream, p);
   }
   return hipGetLastError();
 }
@@ -403,10 +502,11 @@ hipError_t launch_append_evict(const akv_append_desc* d, hipStream_t stream) {
   p.qnb = d->quant_num_blocks;
   p.rot = d->rotation;
   dim3 grid(kBlock / 2 + 1, d->Hkv, 2 * d->B);
+  const int W = code_width(d->code_bits);
   if (d->d == 64)
-    hipLaunchKernelGGL(append_evict_kernel<64>, grid, dim3(64), 0, stream, p);
+    launch_append_w<64>(W, grid, stream, p);
   else
-    hipLaunchKernelGGL(append_evict_kernel<128>, grid, dim3(64), 0, stream, p);
+    launch_append_w<128>(W, grid, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(step_commit_kernel, dim3((d->B + 63) / 64), dim3(64), 0, stream, p);

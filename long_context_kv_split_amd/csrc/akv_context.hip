@@ -27,6 +27,7 @@ struct CtxParams {
   const int32_t* qtab;
   int32_t* qlen;
   int qmax, qnb;
+  int qw;                                 // code width (2, 3 or 4)
   size_t lens_off, exact_off, quant_off;  // image offsets
   size_t eslot, qslot;                    // bytes per slot
 };
@@ -46,7 +47,7 @@ __device__ inline int slot_regions(const CtxParams& p, int tier, int pb, Region 
     r[1] = {reinterpret_cast<unsigned char*>(p.ev) + pb * n, n};
     return 2;
   }
-  const size_t nc = H * 32 * D, ns = H * 4 * D;
+  const size_t nc = H * 8 * p.qw * D, ns = H * 4 * D;
   r[0] = {p.kc + pb * nc, nc};
   r[1] = {p.vc + pb * nc, nc};
   r[2] = {reinterpret_cast<unsigned char*>(p.ks) + pb * ns, ns};
@@ -91,9 +92,9 @@ __global__ __launch_bounds__(kCtxThreads) void ctx_save_kernel(CtxParams p, unsi
       uint32_t v = 0;
       if (i == 0) v = kCtxMagic0;
       else if (i == 4) v = kCtxMagic1;
-      else if (i >= 8 && i < 28) {
+      else if (i >= 8 && i < 32) {
         const int f = (int)(i - 8) / 4;
-        v = (uint32_t)(f == 0 ? p.B : f == 1 ? p.Hkv : f == 2 ? p.d : f == 3 ? p.emax : p.qmax);
+        v = (uint32_t)(f == 0 ? p.B : f == 1 ? p.Hkv : f == 2 ? p.d : f == 3 ? p.emax : f == 4 ? p.qmax : p.qw);
       } else if (i >= p.lens_off && i < p.lens_off + 8 * (size_t)p.B) {
         const int k = (int)(i - p.lens_off) / 4;
         v = (uint32_t)((k & 1) ? p.qlen[k >> 1] : p.elen[k >> 1]);
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kCtxThreads) void ctx_save_kernel(CtxParams p, unsi
 __device__ inline bool header_ok(const CtxParams& p, const unsigned char* img) {
   const uint32_t* h = reinterpret_cast<const uint32_t*>(img);
   return h[0] == kCtxMagic0 && h[1] == kCtxMagic1 && (int)h[2] == p.B && (int)h[3] == p.Hkv && (int)h[4] == p.d &&
-         (int)h[5] == p.emax && (int)h[6] == p.qmax;
+         (int)h[5] == p.emax && (int)h[6] == p.qmax && (int)h[7] == p.qw;
 }
 
 __global__ __launch_bounds__(kCtxThreads) void ctx_restore_kernel(CtxParams p, const unsigned char* img) {
@@ -167,7 +168,7 @@ void ctx_layout(const akv_context_desc* d, size_t* lens_off, size_t* exact_off, 
   *lens_off = 256;
   *exact_off = 256 + ((8 * B + 255) / 256) * 256;
   *eslot = 256 * H * D;
-  *qslot = 72 * H * D;
+  *qslot = (16 * (size_t)code_width(d->code_bits) + 8) * H * D;
   *quant_off = *exact_off + B * (size_t)d->exact_max_blocks * *eslot;
   *total = *quant_off + B * (size_t)d->quant_max_blocks * *qslot;
 }
@@ -191,6 +192,7 @@ static CtxParams ctx_params(const akv_context_desc* d) {
   p.qlen = d->quant_lengths;
   p.qmax = d->quant_max_blocks;
   p.qnb = d->quant_num_blocks;
+  p.qw = code_width(d->code_bits);
   size_t total;
   ctx_layout(d, &p.lens_off, &p.exact_off, &p.quant_off, &p.eslot, &p.qslot, &total);
   return p;

@@ -273,36 +273,83 @@ __device__ void split_epilogue(const AttnParams& p, const Lds& L, int b, int kv,
 }
 
 // ------------------------------------------------------------- quant tier
-template <int D>
+// Code words of one 32-token unit at code width W (layouts in include/akv.h).
+// W = 4: one dword per (tile, group) of K and per value tile of V, each byte
+// one table field (two codes).  W < 4: dwords of the pair plane, each byte
+// the fields of two groups (K) or two value tiles (V) in its nibbles, and
+// for W = 3 the high-plane bits, merged into the fields when used.
+template <int D, int W>
 struct QUnit {
-  uint32_t kw[2][D / 32];  // K code dwords: [tile][group]
-  uint32_t vw[D / 16];     // V code dwords: [value tile]
+  static constexpr int KW = W == 4 ? D / 32 : D / 64;
+  static constexpr int VW = W == 4 ? D / 16 : D / 32;
+  uint32_t kw[2][KW];      // K code dwords: [tile][group or group pair]
+  uint32_t vw[VW];         // V code dwords: [value tile or tile pair]
+  uint32_t kh[2];          // W = 3: K high-plane bits of each tile (d = 64: 16 bits)
+  uint32_t vh[D / 64];     // W = 3: V high-plane dwords (4 value tiles each)
   u32x4 sc;                // this lane's 16-byte slice of the unit's K|V scales
 };
 
 // Issue the loads of one 32-token unit (half c of pool block pb).
-template <int D>
-__device__ inline void quant_load(QUnit<D>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq, int lane) {
+template <int D, int W>
+__device__ inline void quant_load(QUnit<D, W>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq,
+                                  int lane) {
   constexpr int M = D / 32, NT = D / 16;
-  const unsigned char* kcs = p.kc + (size_t)pb * p.q_code_stride + (size_t)kv * (32 * D);
-  const unsigned char* vcs = p.vc + (size_t)pb * p.q_code_stride + (size_t)kv * (32 * D);
+  const unsigned char* kcs = p.kc + (size_t)pb * p.q_code_stride + (size_t)kv * (8 * W * D);
+  const unsigned char* vcs = p.vc + (size_t)pb * p.q_code_stride + (size_t)kv * (8 * W * D);
 #pragma unroll
   for (int tp = 0; tp < 2; ++tp) {
     int row = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
-    const unsigned char* src = kcs + row * (D / 2) + (D / 8) * qq;
-    if constexpr (M == 4) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(src);
-      u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1]; u.kw[tp][2] = x[2]; u.kw[tp][3] = x[3];
+    if constexpr (W == 4) {
+      const unsigned char* src = kcs + row * (D / 2) + (D / 8) * qq;
+      if constexpr (M == 4) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(src);
+        u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1]; u.kw[tp][2] = x[2]; u.kw[tp][3] = x[3];
+      } else {
+        u32x2 x = *reinterpret_cast<const u32x2*>(src);
+        u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1];
+      }
     } else {
-      u32x2 x = *reinterpret_cast<const u32x2*>(src);
-      u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1];
+      const unsigned char* src = kcs + row * (D / 4) + (D / 16) * qq;
+      if constexpr (M == 4) {
+        u32x2 x = *reinterpret_cast<const u32x2*>(src);
+        u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1];
+      } else {
+        u.kw[tp][0] = *reinterpret_cast<const uint32_t*>(src);
+      }
+      if constexpr (W == 3) {
+        const unsigned char* hsrc = kcs + 16 * D + row * (D / 8) + (D / 32) * qq;
+        if constexpr (M == 4)
+          u.kh[tp] = *reinterpret_cast<const uint32_t*>(hsrc);
+        else
+          u.kh[tp] = *reinterpret_cast<const uint16_t*>(hsrc);
+      }
     }
   }
-  const u32x4* vsrc = reinterpret_cast<const u32x4*>(vcs + ((c * 4 + qq) * 16 + j) * (D / 4));
+  if constexpr (W == 4) {
+    const u32x4* vsrc = reinterpret_cast<const u32x4*>(vcs + ((c * 4 + qq) * 16 + j) * (D / 4));
 #pragma unroll
-  for (int v = 0; v < NT / 4; ++v) {
-    u32x4 x = vsrc[v];
-    u.vw[4 * v] = x[0]; u.vw[4 * v + 1] = x[1]; u.vw[4 * v + 2] = x[2]; u.vw[4 * v + 3] = x[3];
+    for (int v = 0; v < NT / 4; ++v) {
+      u32x4 x = vsrc[v];
+      u.vw[4 * v] = x[0]; u.vw[4 * v + 1] = x[1]; u.vw[4 * v + 2] = x[2]; u.vw[4 * v + 3] = x[3];
+    }
+  } else {
+    const unsigned char* vsrc = vcs + ((c * 4 + qq) * 16 + j) * (D / 8);
+    if constexpr (NT == 8) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(vsrc);
+      u.vw[0] = x[0]; u.vw[1] = x[1]; u.vw[2] = x[2]; u.vw[3] = x[3];
+    } else {
+      u32x2 x = *reinterpret_cast<const u32x2*>(vsrc);
+      u.vw[0] = x[0]; u.vw[1] = x[1];
+    }
+    if constexpr (W == 3) {
+      const unsigned char* hsrc = vcs + 16 * D + ((c * 4 + qq) * 16 + j) * (D / 16);
+      if constexpr (NT == 8) {
+        u32x2 x = *reinterpret_cast<const u32x2*>(hsrc);
+        u.vh[0] = x[0]; u.vh[1] = x[1];
+      } else {
+        u.vh[0] = *reinterpret_cast<const uint32_t*>(hsrc);
+      }
+    }
   }
   // scales of the unit: M K-groups then M V-groups, 64 bytes (32 tokens) each;
   // lane (seg, part) carries bytes [16 part, 16 part + 16) of segment seg
@@ -312,11 +359,40 @@ __device__ inline void quant_load(QUnit<D>& u, const AttnParams& p, int pb, int 
   u.sc = *reinterpret_cast<const u32x4*>(sb);
 }
 
+// Table fields (one per byte, two codes each) of K group m of tile tp and of
+// value tile t.  At W = 3 a field is the pair-plane nibble with the two top
+// bits above it (bits 4, 5).
+template <int D, int W>
+__device__ inline uint32_t kfields(const QUnit<D, W>& u, int tp, int m) {
+  if constexpr (W == 4) {
+    return u.kw[tp][m];
+  } else {
+    uint32_t f = (u.kw[tp][m >> 1] >> (4 * (m & 1))) & 0x0F0F0F0Fu;
+    if constexpr (W == 3) {
+      uint32_t h = u.kh[tp];
+      if constexpr (D == 64)  // nibble b of the 16 bits -> byte b
+        h = (h & 0xFu) | ((h << 4) & 0xF00u) | ((h << 8) & 0xF0000u) | ((h << 12) & 0xF000000u);
+      f |= ((h >> (2 * m)) & 0x03030303u) << 4;
+    }
+    return f;
+  }
+}
+template <int D, int W>
+__device__ inline uint32_t vfields(const QUnit<D, W>& u, int t) {
+  if constexpr (W == 4) {
+    return u.vw[t];
+  } else {
+    uint32_t f = (u.vw[t >> 1] >> (4 * (t & 1))) & 0x0F0F0F0Fu;
+    if constexpr (W == 3) f |= ((u.vh[t >> 2] >> (2 * (t & 3))) & 0x03030303u) << 4;
+    return f;
+  }
+}
+
 // This lane's group scales of one unit, parked in LDS and read back: lanes
 // < 8M hold the unit's 2M 64-byte segments (M K-groups, then M V-groups);
 // lane (col, qq) reads its 8 tokens 8qq.. of every group.
-template <int D>
-__device__ inline void quant_scales(const QUnit<D>& u, unsigned char* stage, int qq, int lane, u32x4 (&ksc)[D / 32],
+template <int D, int W>
+__device__ inline void quant_scales(const QUnit<D, W>& u, unsigned char* stage, int qq, int lane, u32x4 (&ksc)[D / 32],
                                     u32x4 (&vsc)[D / 32]) {
   constexpr int M = D / 32;
   if (lane < 8 * M) *reinterpret_cast<u32x4*>(stage + 16 * lane) = u.sc;
@@ -344,8 +420,8 @@ __device__ inline void mask_value_scales(u32x4 (&vsc)[D / 32], int nvalid, int q
 }
 
 // Scores (log2 units) of this lane's 8 tokens 8qq + e of one unit.
-template <int D>
-__device__ inline void quant_scores(const QUnit<D>& u, const u32x4 (&ksc)[D / 32], const half8 (&Q)[D / 32],
+template <int D, int W>
+__device__ inline void quant_scores(const QUnit<D, W>& u, const u32x4 (&ksc)[D / 32], const half8 (&Q)[D / 32],
                                     const unsigned char* lut, uint32_t loff, float (&s)[8]) {
   constexpr int M = D / 32;
 #pragma unroll
@@ -353,7 +429,7 @@ __device__ inline void quant_scores(const QUnit<D>& u, const u32x4 (&ksc)[D / 32
     float acc[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const uint32_t w = u.kw[tp][m];
+      const uint32_t w = kfields<D, W>(u, tp, m);
       const unsigned char* r0 = lut + lut_addr<0>(w, loff);
       const unsigned char* r1 = lut + lut_addr<1>(w, loff);
       const unsigned char* r2 = lut + lut_addr<2>(w, loff);
@@ -390,8 +466,8 @@ __device__ inline void quant_scores(const QUnit<D>& u, const u32x4 (&ksc)[D / 32
 // instead: value tile t (group t / 2) uses P_g = P * scale(., g), and the
 // table levels enter the matrix cores as they are (4 multiplies per group
 // instead of 4 per tile).
-template <int D>
-__device__ inline void quant_values(const QUnit<D>& u, const u32x4 (&vsc)[D / 32], half8 pb8, const unsigned char* lut,
+template <int D, int W>
+__device__ inline void quant_values(const QUnit<D, W>& u, const u32x4 (&vsc)[D / 32], half8 pb8, const unsigned char* lut,
                                     uint32_t loff, float4v (&O)[D / 16]) {
   constexpr int M = D / 32;
   const u32x4 pw = __builtin_bit_cast(u32x4, pb8);
@@ -405,7 +481,7 @@ __device__ inline void quant_values(const QUnit<D>& u, const u32x4 (&vsc)[D / 32
   }
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    const uint32_t w = u.vw[t];
+    const uint32_t w = vfields<D, W>(u, t);
     const uint32_t l0 = *reinterpret_cast<const uint32_t*>(lut + lut_addr<0>(w, loff));
     const uint32_t l1 = *reinterpret_cast<const uint32_t*>(lut + lut_addr<1>(w, loff));
     const uint32_t l2 = *reinterpret_cast<const uint32_t*>(lut + lut_addr<2>(w, loff));
@@ -418,16 +494,16 @@ __device__ inline void quant_values(const QUnit<D>& u, const u32x4 (&vsc)[D / 32
 // softmax step: the two units' table reads and matrix-core chains are
 // independent, so one wave keeps more of them in flight.  PARTIAL: only
 // the first nva / nvb tokens of a / b exist.
-template <int D, bool PARTIAL>
-__device__ inline void quant_block(const QUnit<D>& ua, const QUnit<D>& ub, int nva, int nvb, const half8 (&Q)[D / 32],
+template <int D, int W, bool PARTIAL>
+__device__ inline void quant_block(const QUnit<D, W>& ua, const QUnit<D, W>& ub, int nva, int nvb, const half8 (&Q)[D / 32],
                                    const unsigned char* lut, unsigned char* stage, uint32_t loff, int qq, int lane,
                                    SoftmaxState& st, float4v (&O)[D / 16]) {
   constexpr int M = D / 32;
   // scales of both units (LDS ops of a wave run in order)
   __builtin_amdgcn_wave_barrier();
   u32x4 ksa[M], vsa[M], ksb[M], vsb[M];
-  quant_scales<D>(ua, stage, qq, lane, ksa, vsa);
-  quant_scales<D>(ub, stage + 512, qq, lane, ksb, vsb);
+  quant_scales<D, W>(ua, stage, qq, lane, ksa, vsa);
+  quant_scales<D, W>(ub, stage + 512, qq, lane, ksb, vsb);
   __builtin_amdgcn_wave_barrier();
   if (PARTIAL) {
     mask_value_scales<D>(vsa, nva, qq);
@@ -436,8 +512,8 @@ __device__ inline void quant_block(const QUnit<D>& ua, const QUnit<D>& ub, int n
   float s[16];
   {
     float sa[8], sb[8];
-    quant_scores<D>(ua, ksa, Q, lut, loff, sa);
-    quant_scores<D>(ub, ksb, Q, lut, loff, sb);
+    quant_scores<D, W>(ua, ksa, Q, lut, loff, sa);
+    quant_scores<D, W>(ub, ksb, Q, lut, loff, sb);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       s[e] = (PARTIAL && 8 * qq + e >= nva) ? neg_inf() : sa[e];
@@ -452,11 +528,11 @@ __device__ inline void quant_block(const QUnit<D>& ua, const QUnit<D>& ub, int n
     pa8[e] = (_Float16)pr[e];
     pb8[e] = (_Float16)pr[8 + e];
   }
-  quant_values<D>(ua, vsa, pa8, lut, loff, O);
-  quant_values<D>(ub, vsb, pb8, lut, loff, O);
+  quant_values<D, W>(ua, vsa, pa8, lut, loff, O);
+  quant_values<D, W>(ub, vsb, pb8, lut, loff, O);
 }
 
-template <int D>
+template <int D, int W>
 __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, int sx, int s) {
   constexpr int M = D / 32;   // groups = score tiles per token tile
   constexpr int NT = D / 16;  // value tiles
@@ -484,9 +560,19 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
 #pragma unroll
     for (int e = 0; e < QV; ++e) qv[e] = bf16_bits_to_float(qsrc[e]);
   }
-  // the level pair of code byte tid, for the level table below
-  const float c0 = __builtin_bit_cast(float, kLevelBits[tid & 15]);
-  const float c1 = __builtin_bit_cast(float, kLevelBits[tid >> 4]);
+  // the level pair of table field tid (two codes: see kfields), for the
+  // level table below
+  constexpr int kRows = 1 << (2 * W);
+  int i0, i1;
+  if constexpr (W == 4) {
+    i0 = tid & 15, i1 = tid >> 4;
+  } else if constexpr (W == 3) {
+    i0 = (tid & 3) | (((tid >> 4) & 1) << 2), i1 = ((tid >> 2) & 3) | (((tid >> 5) & 1) << 2);
+  } else {
+    i0 = tid & 3, i1 = (tid >> 2) & 3;
+  }
+  const float c0 = __builtin_bit_cast(float, level_bits<W>()[i0 & ((1 << W) - 1)]);
+  const float c1 = __builtin_bit_cast(float, level_bits<W>()[i1 & ((1 << W) - 1)]);
   int ql, el;
   if (!tier_lengths(p, b, ql, el) || start >= ql) return;  // bad lengths, or an idle split
   const int end = min(start + p.Pq, ql);
@@ -494,9 +580,10 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   const int nblk_w = (nblk - w + kWaves - 1) / kWaves;
   const WaveBlocks wb = trim_blocks(wb_all, nblk_w, lane);
 
-  // level table (needs nothing loaded): row e (code byte) = 256 B: 32 x hi pair | 32 x lo pair
-  {
-    const int e = tid;  // 256 threads, 256 rows
+  // level table (needs nothing loaded): row e (table field) = 256 B: 32 x hi
+  // pair | 32 x lo pair; 4^W rows
+  if (tid < kRows) {
+    const int e = tid;
     _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
     _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
     const uint32_t hip = h2_as_u32(half2v{h0, h1});
@@ -516,14 +603,14 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   // loads on every path the compiler's wait counts stay exact instead of
   // draining all loads in flight where paths join
   const int klast = max(nblk_w - 1, 0);
-  auto load_block = [&](QUnit<D>& u0, QUnit<D>& u1, bool& ok, int k) {
+  auto load_block = [&](QUnit<D, W>& u0, QUnit<D, W>& u1, bool& ok, int k) {
     int pb = wb.get(min(k, klast));
     ok = pb >= 0 && pb < p.qnb;
     pb = ok ? pb : 0;
-    quant_load<D>(u0, p, pb, kv, 0, j, qq, lane);
-    quant_load<D>(u1, p, pb, kv, 1, j, qq, lane);
+    quant_load<D, W>(u0, p, pb, kv, 0, j, qq, lane);
+    quant_load<D, W>(u1, p, pb, kv, 1, j, qq, lane);
   };
-  QUnit<D> ra0, ra1, rb0, rb1;
+  QUnit<D, W> ra0, ra1, rb0, rb1;
   bool oka, okb;
   load_block(ra0, ra1, oka, 0);
 
@@ -594,13 +681,13 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   unsigned char* stage = L.stage + w * kScaleStage;
   // block k of this wave covers tokens tb .. tb + 63; a bad block id poisons
   // the split (its partial becomes NaN), the loads then read block 0
-  auto process = [&](const QUnit<D>& u0, const QUnit<D>& u1, bool ok, int k) {
+  auto process = [&](const QUnit<D, W>& u0, const QUnit<D, W>& u1, bool ok, int k) {
     const int tb = (blk0 + w + kWaves * k) * 64;
     poison |= !ok;
     if (end - tb >= 64)
-      quant_block<D, false>(u0, u1, 32, 32, Q, smem, stage, loff, qq, lane, st, O);
+      quant_block<D, W, false>(u0, u1, 32, 32, Q, smem, stage, loff, qq, lane, st, O);
     else
-      quant_block<D, true>(u0, u1, min(end - tb, 32), max(end - tb - 32, 0), Q, smem, stage, loff, qq, lane, st,
+      quant_block<D, W, true>(u0, u1, min(end - tb, 32), max(end - tb - 32, 0), Q, smem, stage, loff, qq, lane, st,
                            O);
   };
   // two blocks in a ring: block k + 1 is in flight while block k is computed
@@ -766,7 +853,7 @@ __device__ inline void merge_two(float oa, float la, float ob, float lb, float& 
   lse = M + __logf(W);
 }
 
-template <int D>
+template <int D, int W>
 __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   const Lds L = lds_layout(smem);
@@ -774,7 +861,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(AttnParams p)
   // the split reads its tier's length itself, in the same round trip as its
   // block ids and query
   if (sx < p.Sq)
-    quant_split<D>(p, L, b, kv, p.part_base + sx, sx);
+    quant_split<D, W>(p, L, b, kv, p.part_base + sx, sx);
   else
     exact_split<D>(p, L, b, kv, p.part_base + sx, sx - p.Sq);
 }
@@ -1035,16 +1122,26 @@ hipError_t launch_decode_qrot(const AttnParams& p, int D, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+static void launch_split_w(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  if (p.qw == 2)
+    hipLaunchKernelGGL((split_decode_kernel<D, 2>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.qw == 3)
+    hipLaunchKernelGGL((split_decode_kernel<D, 3>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((split_decode_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p);
+}
+
 hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream) {
   dim3 grid(p.Sq + p.Se, p.Hkv, p.B);
   dim3 mgrid(p.Hq, p.B);
   hipError_t e = launch_decode_qrot(p, D, stream);
   if (e != hipSuccess) return e;
   if (D == 64) {
-    hipLaunchKernelGGL(split_decode_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+    launch_split_w<64>(p, grid, stream);
     hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(split_decode_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+    launch_split_w<128>(p, grid, stream);
     hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
   }
   return hipGetLastError();
@@ -1055,9 +1152,9 @@ hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream) {
 hipError_t launch_decode_splits(const AttnParams& p, int D, int splits, int seqs, hipStream_t stream) {
   dim3 grid(splits, p.Hkv, seqs);
   if (D == 64)
-    hipLaunchKernelGGL(split_decode_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+    launch_split_w<64>(p, grid, stream);
   else
-    hipLaunchKernelGGL(split_decode_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+    launch_split_w<128>(p, grid, stream);
   return hipGetLastError();
 }
 

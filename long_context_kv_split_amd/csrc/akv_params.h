@@ -41,6 +41,7 @@ struct AttnParams {
   // rotation; else a float32 [d][d] orthogonal matrix R (codes hold R x).
   // qrot: [B][Hq][d] float32 workspace for the queries rotated by R.
   const float* rot;
+  int qw;  // compressed-tier code width (2, 3 or 4)
   float* qrot;
 };
 

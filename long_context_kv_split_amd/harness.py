@@ -36,6 +36,29 @@ def vcode_byte(d: int, tok: np.ndarray, dim: np.ndarray) -> np.ndarray:
     return ((c * 4 + a) * 16 + i) * (d >> 2) + 4 * t + b
 
 
+def narrow_code_bits(d: int, w: int, tok: np.ndarray, dim: np.ndarray, isv: bool):
+    """(byte, shift) pairs inside a width-w (2 or 3) code slab of the pair-plane
+    bits (2 per code) and, for w = 3, of the high-plane bit of (in-block token
+    `tok`, dim `dim`) (include/akv.h, "Code width")."""
+    e = tok & 1 if isv else dim & 1
+    if not isv:
+        m, a, b = dim >> 5, (dim >> 3) & 3, (dim >> 1) & 3
+        pb = tok * (d // 4) + (d // 16) * a + 4 * (m >> 1) + b
+        ps = 4 * (m & 1) + 2 * e
+        M = d // 32
+        bit = 8 * M * a + 2 * M * b + 2 * m + e
+        hb = 16 * d + tok * (d // 8) + (bit >> 3)
+        hs = bit & 7
+    else:
+        c, a, b = tok >> 5, (tok >> 3) & 3, (tok >> 1) & 3
+        t, i = dim >> 4, dim & 15
+        pb = ((c * 4 + a) * 16 + i) * (d // 8) + 4 * (t >> 1) + b
+        ps = 4 * (t & 1) + 2 * e
+        hb = 16 * d + ((c * 4 + a) * 16 + i) * (d // 16) + 4 * (t >> 2) + b
+        hs = 2 * (t & 3) + e
+    return pb, ps, hb, hs
+
+
 def pages_from_tokens(x: np.ndarray, n_blocks_pool: int, table_row: np.ndarray, out: np.ndarray,
                       dim_major: bool = False) -> None:
     """Scatter token-major x [n, Hkv, d] into a pool by a table row: [blocks, Hkv, 64, d]
@@ -84,12 +107,14 @@ class DeviceWorkload:
     """A workload resident in HBM, ready for akv_attend_decode / akv_attend_chunk.
 
     ``rotation`` (float32 [d, d] orthogonal, or None for the Walsh-Hadamard one)
-    is the compressed tier's rotation: every descriptor built here carries it."""
+    is the compressed tier's rotation and ``width`` (2, 3 or 4) its code width:
+    every descriptor built here carries both."""
 
     def __init__(self, w: Workload, device: str = "cuda", fill_quant: bool = True,
-                 rotation: Optional[np.ndarray] = None):
+                 rotation: Optional[np.ndarray] = None, width: int = 4):
         self.w = w
         self.device = device
+        self.width = width
         self.rotation = None if rotation is None else \
             torch.from_numpy(np.ascontiguousarray(rotation, dtype=np.float32)).to(device)
         d, hkv = w.d, w.Hkv
@@ -109,8 +134,8 @@ class DeviceWorkload:
         qnb = max(1, w.quant_pool_blocks)
         self.pools = [Pools(
             _dev(ek, device), _dev(ev, device),
-            torch.zeros((qnb, hkv, 32 * d), dtype=torch.uint8, device=device),
-            torch.zeros((qnb, hkv, 32 * d), dtype=torch.uint8, device=device),
+            torch.zeros((qnb, hkv, 8 * width * d), dtype=torch.uint8, device=device),
+            torch.zeros((qnb, hkv, 8 * width * d), dtype=torch.uint8, device=device),
             torch.zeros((qnb, hkv, 2 * d), dtype=torch.int16, device=device),
             torch.zeros((qnb, hkv, 2 * d), dtype=torch.int16, device=device))]
         B, Tq, Hq = w.B, w.Tq, w.Hq
@@ -145,7 +170,8 @@ class DeviceWorkload:
                 dst_k_codes=ptr(self.pools[0].kc), dst_v_codes=ptr(self.pools[0].vc),
                 dst_k_scales=ptr(self.pools[0].ks), dst_v_scales=ptr(self.pools[0].vs),
                 dst_block_table=ptr(dst_t), dst_max_blocks=w.quant_table.shape[1],
-                dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=0, rotation=ptr(self.rotation))
+                dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=0, rotation=ptr(self.rotation),
+                code_bits=self.width)
             akv.check(akv.akv_compress_evicted(desc, stream or stream_handle()))
             torch.cuda.synchronize()
             del dk, dv, dt
@@ -160,7 +186,7 @@ class DeviceWorkload:
             exact_num_blocks=max(1, w.exact_pool_blocks), k_codes=ptr(P.kc), v_codes=ptr(P.vc),
             k_scales=ptr(P.ks), v_scales=ptr(P.vs), quant_table=ptr(self.quant_table),
             quant_lengths=ptr(self.quant_len), quant_max_blocks=w.quant_table.shape[1],
-            quant_num_blocks=max(1, w.quant_pool_blocks), rotation=ptr(self.rotation))
+            quant_num_blocks=max(1, w.quant_pool_blocks), rotation=ptr(self.rotation), code_bits=self.width)
 
     def context_desc(self, replica: int = 0) -> akv.ContextDesc:
         """Descriptor of this workload's device state for checkpoint save / restore."""
@@ -171,7 +197,7 @@ class DeviceWorkload:
             exact_num_blocks=max(1, w.exact_pool_blocks), k_codes=ptr(P.kc), v_codes=ptr(P.vc),
             k_scales=ptr(P.ks), v_scales=ptr(P.vs), quant_table=ptr(self.quant_table),
             quant_lengths=ptr(self.quant_len), quant_max_blocks=self.qmax,
-            quant_num_blocks=max(1, w.quant_pool_blocks))
+            quant_num_blocks=max(1, w.quant_pool_blocks), code_bits=self.width)
 
     def host_tiers(self, replica: int = 0):
         """Each sequence's compressed tier copied to pinned host memory as block records
@@ -225,7 +251,8 @@ class DeviceWorkload:
             src_start=src_start, n_tokens=n,
             dst_k_codes=ptr(P.kc), dst_v_codes=ptr(P.vc), dst_k_scales=ptr(P.ks), dst_v_scales=ptr(P.vs),
             dst_block_table=ptr(self.quant_table[b]), dst_max_blocks=w.quant_table.shape[1],
-            dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=dst_start, rotation=ptr(self.rotation))
+            dst_num_blocks=max(1, w.quant_pool_blocks), dst_start=dst_start, rotation=ptr(self.rotation),
+            code_bits=self.width)
 
     def read_codes(self, b: int, start: int = 0, n: Optional[int] = None, replica: int = 0):
         """Logical (codes, scales) of compressed tokens [start, start+n) of sequence b.
@@ -238,6 +265,8 @@ class DeviceWorkload:
         tok = np.arange(start, start + n)
         blocks = w.quant_table[b][tok // BLOCK].astype(np.int64)
         r = tok % BLOCK
+        if self.width != 4:
+            return self._read_narrow(blocks, r, replica)
         kc = P.kc.cpu().numpy().reshape(P.kc.shape[0], w.Hkv, BLOCK, d // 2)
         vc = P.vc.cpu().numpy()
         ks = P.ks.cpu().numpy().view(np.uint16).reshape(-1, w.Hkv, d // 32, BLOCK)
@@ -252,6 +281,24 @@ class DeviceWorkload:
         kscales = ks[blocks, :, :, r]
         vscales = vs[blocks, :, :, r]
         return (kcodes.astype(np.uint8), kscales.copy(), vcodes.astype(np.uint8), vscales.copy())
+
+    def _read_narrow(self, blocks, r, replica):
+        w, P, d, wd = self.w, self.pools[replica], self.w.d, self.width
+        kc = P.kc.cpu().numpy()                                       # [blocks, Hkv, 8 w d]
+        vc = P.vc.cpu().numpy()
+        ks = P.ks.cpu().numpy().view(np.uint16).reshape(-1, w.Hkv, d // 32, BLOCK)
+        vs = P.vs.cpu().numpy().view(np.uint16).reshape(-1, w.Hkv, d // 32, BLOCK)
+        dims = np.arange(d)[None, :]
+        heads = np.arange(w.Hkv)[None, :, None]
+        out = []
+        for pool, isv in ((kc, False), (vc, True)):
+            pb, ps, hb, hs = narrow_code_bits(d, wd, r[:, None], dims, isv)   # [n, d]
+            blk = blocks[:, None, None]
+            codes = (pool[blk, heads, pb[:, None, :]] >> ps[:, None, :]) & 3
+            if wd == 3:
+                codes = codes | (((pool[blk, heads, hb[:, None, :]] >> hs[:, None, :]) & 1) << 2)
+            out.append(codes.astype(np.uint8))
+        return out[0], ks[blocks, :, :, r].copy(), out[1], vs[blocks, :, :, r].copy()
 
     # ------------------------------------------------------------- attention
     def add_replicas(self, n_total: int) -> None:
@@ -274,7 +321,7 @@ class DeviceWorkload:
         sq = w.split_tokens_quant if split_quant is None else split_quant
         return akv.AttnDesc(B=w.B, Hq=w.Hq, Hkv=w.Hkv, d=w.d, Tq=w.Tq, softmax_scale=0.0, q=ptr(self.q),
                             exact=exact, quant=quant, split_tokens_exact=se, split_tokens_quant=sq,
-                            o=ptr(self.o), lse=ptr(self.lse), rotation=ptr(self.rotation))
+                            o=ptr(self.o), lse=ptr(self.lse), rotation=ptr(self.rotation), code_bits=self.width)
 
     def ensure_ws(self, desc: akv.AttnDesc, chunk: bool = False) -> None:
         need = (akv.akv_chunk_workspace_bytes if chunk else akv.akv_decode_workspace_bytes)(desc)

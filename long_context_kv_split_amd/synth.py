@@ -103,10 +103,10 @@ class Workload:
     def group(self) -> int:
         return self.Hq // self.Hkv
 
-    def kv_bytes(self) -> int:
-        """Algorithmic K+V bytes one call streams (bf16 exact tier + 4-bit tier)."""
+    def kv_bytes(self, width: int = 4) -> int:
+        """Algorithmic K+V bytes one call streams (bf16 exact tier + width-bit tier)."""
         per_exact = 2 * self.d * 2                      # K and V, bf16
-        per_quant = 2 * (self.d // 2 + 2 * (self.d // 32))  # codes + fp16 scales, K and V
+        per_quant = 2 * (self.d * width // 8 + 2 * (self.d // 32))  # codes + fp16 scales, K and V
         return int(self.Hkv * (self.exact_len.sum() * per_exact + self.quant_len.sum() * per_quant))
 
 
