@@ -60,9 +60,10 @@
  *   K codes: token r owns bytes [r*d/2, (r+1)*d/2); inside that row, byte
  *     (d/8)*a + 4*m + b  (a = 0..3, m = 0..d/32-1, b = 0..3) holds dims
  *     32m + 8a + 2b (low nibble) and 32m + 8a + 2b + 1 (high nibble).
- *   V codes: byte ((c*4 + a)*16 + i)*(d/4) + 4*t + b  (c = 0..1, a = 0..3,
- *     i = 0..15, t = 0..d/16-1, b = 0..3) holds dim 16t + i of tokens
- *     32c + 8a + 2b (low nibble) and 32c + 8a + 2b + 1 (high nibble).
+ *   V codes: byte c*16*d + (t/4)*1024 + (a*16 + i)*16 + 4*(t%4) + b
+ *     (c = 0..1, a = 0..3, i = 0..15, t = 0..d/16-1, b = 0..3) holds dim
+ *     16t + i of tokens 32c + 8a + 2b (low nibble) and 32c + 8a + 2b + 1
+ *     (high nibble).
  *   K and V scales: fp16, element g*64 + r = group g (dims 32g..32g+31) of
  *     token r.
  * These orders put each lane's matrix-core operand in one contiguous load.

@@ -153,11 +153,14 @@ __device__ inline void quant_fetch(QRegs<D>& r, const AttnParams& p, int pb, int
       r.kc[u][k] = kcs[tok * (D / 8) + wi];
       r.ks[u][k] = kss[(wi % M) * 64 + tok];
     }
-    // V: slots run over i (dim within 16), then over 4 dword columns, then 8 token groups
+    // V: slots run over i (dim within 16), then over 4 dword columns, then 8
+    // token groups (c, a); dword of tile t at c*16D + (t/4)*1 KB + (16a + i)*16 + 4(t%4) bytes
     const int i = v & 15, tq = (v >> 4) & 3, ca = v >> 6;
-    const int row16 = ca * 16 + i;
 #pragma unroll
-    for (int k = 0; k < QRegs<D>::VDW; ++k) r.vc[u][k] = vcs[row16 * (D / 16) + tq * QRegs<D>::VDW + k];
+    for (int k = 0; k < QRegs<D>::VDW; ++k) {
+      const int tt = tq * QRegs<D>::VDW + k;
+      r.vc[u][k] = vcs[(ca >> 2) * 4 * D + (tt >> 2) * 256 + ((ca & 3) * 16 + i) * 4 + (tt & 3)];
+    }
     const int g = (16 * tq * QRegs<D>::VDW + i) >> 5;
     r.vs[u] = *reinterpret_cast<const u32x4*>(vss + g * 64 + 8 * ca);
   }

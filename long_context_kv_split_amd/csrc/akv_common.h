@@ -39,6 +39,13 @@ __device__ __constant__ const uint32_t kLevelBits3[8] = {
 __device__ __constant__ const uint32_t kThreshBits3[7] = {
     0xBFDFBC16u, 0xBF866500u, 0xBF002407u, 0x00000000u, 0x3F002407u, 0x3F866500u, 0x3FDFBC16u};
 
+// A load of data read once per call (streamed KV): non-temporal, so it does
+// not push reused lines out of the caches.
+template <class T>
+__device__ inline T stream_load(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
+
 // Code width of a descriptor's code_bits field (0 means 4).
 __host__ __device__ inline int code_width(int code_bits) { return code_bits == 0 ? 4 : code_bits; }
 
@@ -72,11 +79,12 @@ __host__ __device__ inline int kcode_byte(int d, int dim) {
   return (d >> 3) * a + 4 * m + b;
 }
 // Byte offset, inside a V-code slab, of the byte holding tokens
-// (32c + 8a + 2b, +1) of dim 16t + i.
+// (32c + 8a + 2b, +1) of dim 16t + i: per 32-token half c, 1 KB per group of
+// four value tiles, and in it 16 bytes per lane 16a + i (one dword per tile).
 __host__ __device__ inline int vcode_byte(int d, int tok, int dim) {
   int c = tok >> 5, a = (tok >> 3) & 3, b = (tok >> 1) & 3;
   int t = dim >> 4, i = dim & 15;
-  return ((c * 4 + a) * 16 + i) * (d >> 2) + 4 * t + b;
+  return c * 16 * d + (t >> 2) * 1024 + (a * 16 + i) * 16 + 4 * (t & 3) + b;
 }
 
 // ---------------------------------------------------------------- vectors

@@ -38,7 +38,6 @@ namespace akv {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMainLds = 65536;               // LUT / V staging / merge scratch
-constexpr int kMaxWaveBlocks = 128;           // blocks per wave per split (P <= 32768)
 constexpr int kScaleStage = 1056;             // per wave: two units' K and V scales (1024 B used)
 constexpr int kLdsBytes = kMainLds + kWaves * kScaleStage;
 
@@ -302,61 +301,65 @@ __device__ inline void quant_load(QUnit<D, W>& u, const AttnParams& p, int pb, i
     if constexpr (W == 4) {
       const unsigned char* src = kcs + row * (D / 2) + (D / 8) * qq;
       if constexpr (M == 4) {
-        u32x4 x = *reinterpret_cast<const u32x4*>(src);
+        u32x4 x = stream_load<u32x4>(src);
         u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1]; u.kw[tp][2] = x[2]; u.kw[tp][3] = x[3];
       } else {
-        u32x2 x = *reinterpret_cast<const u32x2*>(src);
+        u32x2 x = stream_load<u32x2>(src);
         u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1];
       }
     } else {
       const unsigned char* src = kcs + row * (D / 4) + (D / 16) * qq;
       if constexpr (M == 4) {
-        u32x2 x = *reinterpret_cast<const u32x2*>(src);
+        u32x2 x = stream_load<u32x2>(src);
         u.kw[tp][0] = x[0]; u.kw[tp][1] = x[1];
       } else {
-        u.kw[tp][0] = *reinterpret_cast<const uint32_t*>(src);
+        u.kw[tp][0] = stream_load<uint32_t>(src);
       }
       if constexpr (W == 3) {
         const unsigned char* hsrc = kcs + 16 * D + row * (D / 8) + (D / 32) * qq;
         if constexpr (M == 4)
-          u.kh[tp] = *reinterpret_cast<const uint32_t*>(hsrc);
+          u.kh[tp] = stream_load<uint32_t>(hsrc);
         else
-          u.kh[tp] = *reinterpret_cast<const uint16_t*>(hsrc);
+          u.kh[tp] = stream_load<uint16_t>(hsrc);
       }
     }
   }
   if constexpr (W == 4) {
-    const u32x4* vsrc = reinterpret_cast<const u32x4*>(vcs + ((c * 4 + qq) * 16 + j) * (D / 4));
+    // tiles 4v .. 4v + 3 of lane l: 16 bytes at 1 KB v + 16 l of the half
+    const u32x4* vsrc = reinterpret_cast<const u32x4*>(vcs + c * 16 * D) + lane;
 #pragma unroll
     for (int v = 0; v < NT / 4; ++v) {
-      u32x4 x = vsrc[v];
+      u32x4 x = stream_load<u32x4>(vsrc + 64 * v);
       u.vw[4 * v] = x[0]; u.vw[4 * v + 1] = x[1]; u.vw[4 * v + 2] = x[2]; u.vw[4 * v + 3] = x[3];
     }
   } else {
     const unsigned char* vsrc = vcs + ((c * 4 + qq) * 16 + j) * (D / 8);
     if constexpr (NT == 8) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(vsrc);
+      u32x4 x = stream_load<u32x4>(vsrc);
       u.vw[0] = x[0]; u.vw[1] = x[1]; u.vw[2] = x[2]; u.vw[3] = x[3];
     } else {
-      u32x2 x = *reinterpret_cast<const u32x2*>(vsrc);
+      u32x2 x = stream_load<u32x2>(vsrc);
       u.vw[0] = x[0]; u.vw[1] = x[1];
     }
     if constexpr (W == 3) {
       const unsigned char* hsrc = vcs + 16 * D + ((c * 4 + qq) * 16 + j) * (D / 16);
       if constexpr (NT == 8) {
-        u32x2 x = *reinterpret_cast<const u32x2*>(hsrc);
+        u32x2 x = stream_load<u32x2>(hsrc);
         u.vh[0] = x[0]; u.vh[1] = x[1];
       } else {
-        u.vh[0] = *reinterpret_cast<const uint32_t*>(hsrc);
+        u.vh[0] = stream_load<uint32_t>(hsrc);
       }
     }
   }
-  // scales of the unit: M K-groups then M V-groups, 64 bytes (32 tokens) each;
-  // lane (seg, part) carries bytes [16 part, 16 part + 16) of segment seg
-  const int lm = lane & (8 * M - 1), seg = lm >> 2, g = seg % M;
-  const uint16_t* sb = (seg < M ? p.ks : p.vs) + (size_t)pb * p.q_scale_stride + (size_t)kv * (2 * D) + g * 64 +
-                       32 * c + 8 * (lane & 3);
-  u.sc = *reinterpret_cast<const u32x4*>(sb);
+  // scales of the whole block, with the first unit: M K-groups then M
+  // V-groups, 128 bytes (64 tokens) each; lane (seg, part) carries bytes
+  // [16 part, 16 part + 16) of segment seg, so the load reads whole lines
+  if (c == 0) {
+    const int lm = lane & (16 * M - 1), seg = lm >> 3, g = seg % M;
+    const uint16_t* sb = (seg < M ? p.ks : p.vs) + (size_t)pb * p.q_scale_stride + (size_t)kv * (2 * D) + g * 64 +
+                         8 * (lane & 7);
+    u.sc = stream_load<u32x4>(sb);
+  }
 }
 
 // Table fields (one per byte, two codes each) of K group m of tile tp and of
@@ -388,20 +391,20 @@ __device__ inline uint32_t vfields(const QUnit<D, W>& u, int t) {
   }
 }
 
-// This lane's group scales of one unit, parked in LDS and read back: lanes
-// < 8M hold the unit's 2M 64-byte segments (M K-groups, then M V-groups);
-// lane (col, qq) reads its 8 tokens 8qq.. of every group.
+// The block's group scales, parked in LDS by the first unit's lanes < 16M
+// (2M 128-byte segments: M K-groups, then M V-groups), and read back per
+// unit: lane (col, qq) of unit c reads its 8 tokens 32c + 8qq.. of every
+// group.
 template <int D, int W>
-__device__ inline void quant_scales(const QUnit<D, W>& u, unsigned char* stage, int qq, int lane, u32x4 (&ksc)[D / 32],
-                                    u32x4 (&vsc)[D / 32]) {
+__device__ inline void park_scales(const QUnit<D, W>& u, unsigned char* stage, int lane) {
   constexpr int M = D / 32;
-  if (lane < 8 * M) *reinterpret_cast<u32x4*>(stage + 16 * lane) = u.sc;
-  __builtin_amdgcn_wave_barrier();
+  if (lane < 16 * M) *reinterpret_cast<u32x4*>(stage + 16 * lane) = u.sc;
+}
+template <int D>
+__device__ inline void unit_scales(const unsigned char* stage, int c, int isv, int qq, u32x4 (&sc)[D / 32]) {
+  constexpr int M = D / 32;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    ksc[m] = *reinterpret_cast<const u32x4*>(stage + 64 * m + 16 * qq);
-    vsc[m] = *reinterpret_cast<const u32x4*>(stage + 64 * (M + m) + 16 * qq);
-  }
+  for (int m = 0; m < M; ++m) sc[m] = *reinterpret_cast<const u32x4*>(stage + 128 * (isv * M + m) + 64 * c + 16 * qq);
 }
 
 // Zero the value scales of tokens >= nvalid, so 0 * garbage cannot appear.
@@ -502,13 +505,10 @@ __device__ inline void quant_block(const QUnit<D, W>& ua, const QUnit<D, W>& ub,
   // scales of both units (LDS ops of a wave run in order)
   __builtin_amdgcn_wave_barrier();
   u32x4 ksa[M], vsa[M], ksb[M], vsb[M];
-  quant_scales<D, W>(ua, stage, qq, lane, ksa, vsa);
-  quant_scales<D, W>(ub, stage + 512, qq, lane, ksb, vsb);
+  park_scales<D, W>(ua, stage, lane);
   __builtin_amdgcn_wave_barrier();
-  if (PARTIAL) {
-    mask_value_scales<D>(vsa, nva, qq);
-    mask_value_scales<D>(vsb, nvb, qq);
-  }
+  unit_scales<D>(stage, 0, 0, qq, ksa);
+  unit_scales<D>(stage, 1, 0, qq, ksb);
   float s[16];
   {
     float sa[8], sb[8];
@@ -522,6 +522,14 @@ __device__ inline void quant_block(const QUnit<D, W>& ua, const QUnit<D, W>& ub,
   }
   float pr[16];
   rescale(O, softmax_step<16>(st, s, pr));
+  // the value scales only now (fewer registers live through the scores)
+  unit_scales<D>(stage, 0, 1, qq, vsa);
+  unit_scales<D>(stage, 1, 1, qq, vsb);
+  __builtin_amdgcn_wave_barrier();
+  if (PARTIAL) {
+    mask_value_scales<D>(vsa, nva, qq);
+    mask_value_scales<D>(vsb, nvb, qq);
+  }
   half8 pa8, pb8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -598,10 +606,10 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
     }
   }
 
-  // the first block's loads as soon as the block ids are in; every ring
-  // step loads a block, past the wave's last one too (that block again): with
-  // loads on every path the compiler's wait counts stay exact instead of
-  // draining all loads in flight where paths join
+  // the first block's loads as soon as the block ids are in; the loads are
+  // unconditional (a bad id reads block 0 and poisons the split), so the
+  // compiler's wait counts stay exact instead of draining all loads in
+  // flight where paths join
   const int klast = max(nblk_w - 1, 0);
   auto load_block = [&](QUnit<D, W>& u0, QUnit<D, W>& u1, bool& ok, int k) {
     int pb = wb.get(min(k, klast));
@@ -610,8 +618,8 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
     quant_load<D, W>(u0, p, pb, kv, 0, j, qq, lane);
     quant_load<D, W>(u1, p, pb, kv, 1, j, qq, lane);
   };
-  QUnit<D, W> ra0, ra1, rb0, rb1;
-  bool oka, okb;
+  QUnit<D, W> ra0, ra1;
+  bool oka;
   load_block(ra0, ra1, oka, 0);
 
   // rotated, pre-scaled query q' = H q * (RN(1/sqrt d) * scale * log2 e):
@@ -690,13 +698,14 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
       quant_block<D, W, true>(u0, u1, min(end - tb, 32), max(end - tb - 32, 0), Q, smem, stage, loff, qq, lane, st,
                            O);
   };
-  // two blocks in a ring: block k + 1 is in flight while block k is computed
-  for (int k = 0; k < nblk_w; k += 2) {
-    load_block(rb0, rb1, okb, k + 1);
+  // one block per wave in flight: the wave computes block k, then requests
+  // block k + 1; the other waves of the compute unit keep its LDS and
+  // vector units busy meanwhile (a second register buffer per wave measured
+  // slower: it pushes the kernel to 256 VGPRs and spills)
+  for (int k = 0; k < nblk_w; ++k) {
     process(ra0, ra1, oka, k);
     if (k + 1 >= nblk_w) break;
-    load_block(ra0, ra1, oka, k + 2);
-    process(rb0, rb1, okb, k + 1);
+    load_block(ra0, ra1, oka, k + 1);
   }
   split_epilogue<D>(p, L, b, kv, sx, st, O, poison);
 }

@@ -33,7 +33,7 @@ def vcode_byte(d: int, tok: np.ndarray, dim: np.ndarray) -> np.ndarray:
     """Byte (inside a V-code slab) holding token `tok` (in-block) of dim `dim`."""
     c, a, b = tok >> 5, (tok >> 3) & 3, (tok >> 1) & 3
     t, i = dim >> 4, dim & 15
-    return ((c * 4 + a) * 16 + i) * (d >> 2) + 4 * t + b
+    return c * 16 * d + (t >> 2) * 1024 + (a * 16 + i) * 16 + 4 * (t & 3) + b
 
 
 def narrow_code_bits(d: int, w: int, tok: np.ndarray, dim: np.ndarray, isv: bool):

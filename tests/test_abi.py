@@ -390,3 +390,16 @@ def test_narrow_code_layouts_cover_each_bit_once(width, d):
         allbits = np.concatenate(bits)
         assert np.unique(allbits).size == allbits.size == 8 * width * d * 8
         assert allbits.min() == 0 and allbits.max() == 8 * width * d * 8 - 1
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_four_bit_code_layouts_cover_each_nibble_once(d):
+    """The 4-bit K and V code byte layouts (as the harness reads them) give
+    every (token, dim) code its own nibble of the 32 d-byte slab."""
+    from long_context_kv_split_amd.harness import kcode_byte, vcode_byte
+    tok, dim = np.meshgrid(np.arange(64), np.arange(d), indexing="ij")
+    k = 2 * (tok * (d // 2) + kcode_byte(d, dim)) + (dim & 1)
+    v = 2 * vcode_byte(d, tok, dim) + (tok & 1)
+    for nib in (k.ravel(), v.ravel()):
+        assert np.unique(nib).size == nib.size == 64 * d
+        assert nib.min() == 0 and nib.max() == 64 * d - 1
