@@ -289,7 +289,9 @@ struct QUnit {
 };
 
 // Issue the loads of one 32-token unit (half c of pool block pb).
-template <int D, int W>
+// PARTS: 1 = K codes and (with the first unit) the block's scales, 2 = V
+// codes, 3 = both.
+template <int D, int W, int PARTS = 3>
 __device__ inline void quant_load(QUnit<D, W>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq,
                                   int lane) {
   constexpr int M = D / 32, NT = D / 16;
@@ -297,6 +299,7 @@ __device__ inline void quant_load(QUnit<D, W>& u, const AttnParams& p, int pb, i
   const unsigned char* vcs = p.vc + (size_t)pb * p.q_code_stride + (size_t)kv * (8 * W * D);
 #pragma unroll
   for (int tp = 0; tp < 2; ++tp) {
+    if constexpr (!(PARTS & 1)) break;
     int row = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
     if constexpr (W == 4) {
       const unsigned char* src = kcs + row * (D / 2) + (D / 8) * qq;
@@ -324,7 +327,8 @@ __device__ inline void quant_load(QUnit<D, W>& u, const AttnParams& p, int pb, i
       }
     }
   }
-  if constexpr (W == 4) {
+  if constexpr (!(PARTS & 2)) {
+  } else if constexpr (W == 4) {
     // tiles 4v .. 4v + 3 of lane l: 16 bytes at 1 KB v + 16 l of the half
     const u32x4* vsrc = reinterpret_cast<const u32x4*>(vcs + c * 16 * D) + lane;
 #pragma unroll
@@ -354,7 +358,7 @@ __device__ inline void quant_load(QUnit<D, W>& u, const AttnParams& p, int pb, i
   // scales of the whole block, with the first unit: M K-groups then M
   // V-groups, 128 bytes (64 tokens) each; lane (seg, part) carries bytes
   // [16 part, 16 part + 16) of segment seg, so the load reads whole lines
-  if (c == 0) {
+  if ((PARTS & 1) && c == 0) {
     const int lm = lane & (16 * M - 1), seg = lm >> 3, g = seg % M;
     const uint16_t* sb = (seg < M ? p.ks : p.vs) + (size_t)pb * p.q_scale_stride + (size_t)kv * (2 * D) + g * 64 +
                          8 * (lane & 7);
@@ -497,10 +501,12 @@ __device__ inline void quant_values(const QUnit<D, W>& u, const u32x4 (&vsc)[D /
 // softmax step: the two units' table reads and matrix-core chains are
 // independent, so one wave keeps more of them in flight.  PARTIAL: only
 // the first nva / nvb tokens of a / b exist.
-template <int D, int W, bool PARTIAL>
+// reload_ks() runs once the K codes and the scales are consumed, reload_v()
+// once the V codes are: they may request the next block into ua / ub.
+template <int D, int W, bool PARTIAL, class RK, class RV>
 __device__ inline void quant_block(const QUnit<D, W>& ua, const QUnit<D, W>& ub, int nva, int nvb, const half8 (&Q)[D / 32],
                                    const unsigned char* lut, unsigned char* stage, uint32_t loff, int qq, int lane,
-                                   SoftmaxState& st, float4v (&O)[D / 16]) {
+                                   SoftmaxState& st, float4v (&O)[D / 16], RK&& reload_ks, RV&& reload_v) {
   constexpr int M = D / 32;
   // scales of both units (LDS ops of a wave run in order)
   __builtin_amdgcn_wave_barrier();
@@ -520,6 +526,7 @@ __device__ inline void quant_block(const QUnit<D, W>& ua, const QUnit<D, W>& ub,
       s[8 + e] = (PARTIAL && 8 * qq + e >= nvb) ? neg_inf() : sb[e];
     }
   }
+  reload_ks();
   float pr[16];
   rescale(O, softmax_step<16>(st, s, pr));
   // the value scales only now (fewer registers live through the scores)
@@ -538,6 +545,7 @@ __device__ inline void quant_block(const QUnit<D, W>& ua, const QUnit<D, W>& ub,
   }
   quant_values<D, W>(ua, vsa, pa8, lut, loff, O);
   quant_values<D, W>(ub, vsb, pb8, lut, loff, O);
+  reload_v();
 }
 
 template <int D, int W>
@@ -689,23 +697,36 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   unsigned char* stage = L.stage + w * kScaleStage;
   // block k of this wave covers tokens tb .. tb + 63; a bad block id poisons
   // the split (its partial becomes NaN), the loads then read block 0
-  auto process = [&](const QUnit<D, W>& u0, const QUnit<D, W>& u1, bool ok, int k) {
-    const int tb = (blk0 + w + kWaves * k) * 64;
-    poison |= !ok;
+  // one register buffer per wave, refilled in two parts while its block is
+  // computed: the next block's K codes and scales once the scores are done,
+  // its V codes once the values are (a second whole buffer measured slower:
+  // it pushes the kernel to 256 VGPRs and spills).  Only a wave's last block
+  // (which may be the split's partial one) requests nothing.
+  for (int k = 0; k + 1 < nblk_w; ++k) {
+    poison |= !oka;
+    int pbn = wb.get(k + 1);
+    const bool okn = pbn >= 0 && pbn < p.qnb;
+    pbn = okn ? pbn : 0;
+    auto rks = [&]() {
+      quant_load<D, W, 1>(ra0, p, pbn, kv, 0, j, qq, lane);
+      quant_load<D, W, 1>(ra1, p, pbn, kv, 1, j, qq, lane);
+    };
+    auto rv = [&]() {
+      quant_load<D, W, 2>(ra0, p, pbn, kv, 0, j, qq, lane);
+      quant_load<D, W, 2>(ra1, p, pbn, kv, 1, j, qq, lane);
+    };
+    quant_block<D, W, false>(ra0, ra1, 32, 32, Q, smem, stage, loff, qq, lane, st, O, rks, rv);
+    oka = okn;
+  }
+  if (nblk_w > 0) {
+    const int tb = (blk0 + w + kWaves * (nblk_w - 1)) * 64;
+    poison |= !oka;
+    auto none = []() {};
     if (end - tb >= 64)
-      quant_block<D, W, false>(u0, u1, 32, 32, Q, smem, stage, loff, qq, lane, st, O);
+      quant_block<D, W, false>(ra0, ra1, 32, 32, Q, smem, stage, loff, qq, lane, st, O, none, none);
     else
-      quant_block<D, W, true>(u0, u1, min(end - tb, 32), max(end - tb - 32, 0), Q, smem, stage, loff, qq, lane, st,
-                           O);
-  };
-  // one block per wave in flight: the wave computes block k, then requests
-  // block k + 1; the other waves of the compute unit keep its LDS and
-  // vector units busy meanwhile (a second register buffer per wave measured
-  // slower: it pushes the kernel to 256 VGPRs and spills)
-  for (int k = 0; k < nblk_w; ++k) {
-    process(ra0, ra1, oka, k);
-    if (k + 1 >= nblk_w) break;
-    load_block(ra0, ra1, oka, k + 1);
+      quant_block<D, W, true>(ra0, ra1, min(end - tb, 32), max(end - tb - 32, 0), Q, smem, stage, loff, qq, lane,
+                              st, O, none, none);
   }
   split_epilogue<D>(p, L, b, kv, sx, st, O, poison);
 }
