@@ -328,7 +328,6 @@ class DeviceWorkload:
         if need == 0:
             raise akv.AKVError(akv.AKV_ERR_SHAPE, akv.akv_last_error())
         if need > self.ws_bytes:
-            # zeroed: the counter prefix must start at zero (calls leave it zero)
             self.ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
             self.ws_bytes = need
 
