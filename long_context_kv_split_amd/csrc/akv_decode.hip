@@ -5,30 +5,36 @@
 // paged-attention path).
 //
 // One workgroup (4 waves) per (split, kv head, sequence).  A split is a fixed
-// run of P tokens of one tier; the waves take its 64-token blocks round-robin
-// and stream them in 32-token units, loading the next unit while computing
-// the current one.  The G <= 8 query heads sharing the kv head are the columns
-// of 16x16x32 matrix-core tiles:
+// run of P tokens of one tier; the waves take its 64-token blocks round-robin.
+// The G <= 8 query heads sharing the kv head are the columns of 16x16x32
+// matrix-core tiles:
 //   scores:  D[token][col] = K_tile[token][dims] x Q[dims][col]
 //   values:  O^T[dim][col] += V^T[dim][tokens] x P^T[tokens][col]
 // Compressed tier (QuantForge walkthrough, section 1: the query is rotated
 // once instead of inverse-rotating blocks): the query is rotated by the
-// Walsh-Hadamard butterflies in fp32 and split into fp16 hi + lo parts held
-// in columns 0..7 and 8..15, so the score keeps ~fp32 precision; K codes are
-// expanded through an LDS table into fp16 hi and lo parts of the Lloyd-Max
-// levels (two tiles per group) and the fp16 group scale multiplies the fp32
-// group partial score; V codes are expanded to fp16 level x scale.  The table
-// has one 256-byte row per code byte: 32 copies of the (level, level) fp16 hi
-// pair, then 32 copies of the lo pair; lane l reads copy l % 32, which keeps
-// the random-row lookups of a wave free of bank conflicts.  The value
-// sum stays in rotated space.  Exact tier: bf16 K and q feed bf16 tiles
-// directly (exact products); V is staged in LDS to form the transposed
-// operand.  Each wave keeps an online softmax (base 2); the four waves merge
-// in a fixed order.
+// Walsh-Hadamard butterflies in fp32 (or, for a caller-given rotation R, read
+// from a small kernel that forms R q once per call) and split into fp16 hi +
+// lo parts held in columns 0..7 and 8..15, so the score keeps ~fp32
+// precision.  K codes are expanded through an LDS table into fp16 hi and lo
+// parts of the Lloyd-Max levels (two tiles per group) and the fp16 group
+// scale multiplies the fp32 group partial score; V codes enter the value tile
+// as fp16 levels, their group scale multiplying the probabilities instead.
+// The table has one 256-byte row per table field (two codes): 32 copies of
+// the (level, level) fp16 hi pair, then 32 copies of the lo pair; lane l
+// reads copy l % 32, which keeps the random-row lookups of a wave free of
+// bank conflicts.  Code widths 2 and 3 use the same fields (4 or 64 rows'
+// worth of the 4- or 8-level table).  One register buffer per wave holds a
+// block; the next block's K codes and scales are requested as soon as the
+// scores are done and its V codes once the values are.  The value sum stays
+// in rotated space.  Exact tier: bf16 K and q feed bf16 tiles directly
+// (exact products), and the dim-major V layout makes each lane's V^T operand
+// one 16-byte load; two 32-token units per wave, one in flight while the
+// other is computed.  Each wave keeps an online softmax (base 2); the four
+// waves merge in a fixed order.
 //
 // A second kernel merges each (sequence, query head)'s partials: compressed-
-// tier splits (rotated space), one inverse rotation per head, exact-tier
-// splits, then the two tiers.  Its reduction tree is fixed, so repeated runs
+// tier splits (rotated space), one inverse rotation per head (R^T for a
+// given rotation), exact-tier splits, then the two tiers.  Its reduction tree is fixed, so repeated runs
 // are bit-identical.
 #include "akv_common.h"
 #include "akv_params.h"
@@ -37,7 +43,7 @@ namespace akv {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMainLds = 65536;               // LUT / V staging / merge scratch
+constexpr int kMainLds = 65536;               // LUT / epilogue scratch
 constexpr int kScaleStage = 1056;             // per wave: two units' K and V scales (1024 B used)
 constexpr int kLdsBytes = kMainLds + kWaves * kScaleStage;
 
