@@ -195,3 +195,30 @@ def test_narrow_chunk_refused():
     dw.ensure_ws(desc, chunk=False)
     st = akv.akv_attend_chunk(desc, harness.ptr(dw.ws), dw.ws_bytes, harness.stream_handle())
     assert st == akv.AKV_ERR_UNSUPPORTED, akv.akv_last_error()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("width,qr", [(3, False), (2, False), (4, True)])
+def test_hybrid128k_variants_kv_head_0(width, qr):
+    """The bench's hybrid128k decode (123,904 compressed + 4,096 exact tokens,
+    the library's own split plan) at a narrow width or with a QR rotation:
+    codes of kv head 0 bit-exact, and the attention of its 8 query heads
+    against the oracle over that kv head's whole history."""
+    akv, harness = _mods()
+    w = synth.make("hybrid128k")
+    R = synth.qr_rotation(w.d, seed=0) if qr else None
+    _say(f"hybrid128k width {width} qr {qr}: building")
+    dw = harness.DeviceWorkload(w, rotation=R, width=width)
+    akv.check(dw.attend())
+    torch.cuda.synchronize()
+    o, lse = dw.o.cpu().numpy(), dw.lse.cpu().numpy()
+    kc, ks = O.encode(w.quant_k_src[0][:, :1], R, width)
+    vc, vs = O.encode(w.quant_v_src[0][:, :1], R, width)
+    gk, gks, gv, gvs = dw.read_codes(0)
+    assert np.array_equal(gk[:, :1], kc) and np.array_equal(gks[:, :1], ks), "K codes / scales of kv head 0"
+    assert np.array_equal(gv[:, :1], vc) and np.array_equal(gvs[:, :1], vs), "V codes / scales of kv head 0"
+    G = w.Hq // w.Hkv
+    o_ref, lse_ref = O.decode_sequence(w.q[0][:, :G], w.exact_k[0][:, :1], w.exact_v[0][:, :1], kc, ks, vc, vs,
+                                       rotation=R, width=width)
+    assert_attention(o[0][:, :G], lse[0][:, :G], o_ref, lse_ref, f"hybrid128k width {width} qr {qr} kv 0")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
