@@ -82,6 +82,17 @@ __device__ inline uint32_t lut_addr(uint32_t w, uint32_t off) {
   return __builtin_amdgcn_perm(w, off, 0x0C0C0000u | ((4u + k) << 8));
 }
 
+// Issue priority from progress: a wave that has finished fewer blocks issues
+// first.  Two compressed-tier workgroups share each compute unit, and with
+// equal priority the older one's waves win every tie, so the younger one
+// falls a block behind and ends alone.
+__device__ inline void progress_prio(int k) {
+  if (k <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (k == 1) __builtin_amdgcn_s_setprio(2);
+  else if (k == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 struct SoftmaxState {
   float m;  // running max (log2 units)
   float l;  // this lane's share of the running sum
@@ -566,6 +577,7 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
 
   // requests first, none waiting for another: this wave's block ids, this
   // lane's query values and the tier lengths
+  progress_prio(0);
   const int start = s * p.Pq;
   const int blk0 = start >> 6;
   const WaveBlocks wb_all =
@@ -709,6 +721,7 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
   // it pushes the kernel to 256 VGPRs and spills).  Only a wave's last block
   // (which may be the split's partial one) requests nothing.
   for (int k = 0; k + 1 < nblk_w; ++k) {
+    progress_prio(k);
     poison |= !oka;
     int pbn = wb.get(k + 1);
     const bool okn = pbn >= 0 && pbn < p.qnb;
@@ -725,6 +738,7 @@ __device__ void quant_split(const AttnParams& p, const Lds& L, int b, int kv, in
     oka = okn;
   }
   if (nblk_w > 0) {
+    progress_prio(nblk_w - 1);
     const int tb = (blk0 + w + kWaves * (nblk_w - 1)) * 64;
     poison |= !oka;
     auto none = []() {};
