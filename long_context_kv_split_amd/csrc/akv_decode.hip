@@ -25,8 +25,9 @@
 // bank conflicts.  Code widths 2 and 3 use the same fields (4 or 64 rows'
 // worth of the 4- or 8-level table).  One register buffer per wave holds a
 // block; the next block's K codes and scales are requested as soon as the
-// scores are done and its V codes once the values are.  The value sum stays
-// in rotated space.  Exact tier: bf16 K and q feed bf16 tiles directly
+// scores are done and its V codes once the values are; a wave's issue
+// priority falls as it finishes blocks, so waves that are behind issue
+// first.  The value sum stays in rotated space.  Exact tier: bf16 K and q feed bf16 tiles directly
 // (exact products), and the dim-major V layout makes each lane's V^T operand
 // one 16-byte load; two 32-token units per wave, one in flight while the
 // other is computed.  Each wave keeps an online softmax (base 2); the four
@@ -34,8 +35,8 @@
 //
 // A second kernel merges each (sequence, query head)'s partials: compressed-
 // tier splits (rotated space), one inverse rotation per head (R^T for a
-// given rotation), exact-tier splits, then the two tiers.  Its reduction tree is fixed, so repeated runs
-// are bit-identical.
+// given rotation), exact-tier splits, then the two tiers.  Its reduction
+// tree is fixed, so repeated runs are bit-identical.
 #include "akv_common.h"
 #include "akv_params.h"
 
