@@ -760,10 +760,12 @@ struct EUnit {
 };
 
 // Issue the loads of one 32-token unit (half c of pool block pb).  K is
-// token-major, so lane (row j, qq) reads 8 dims of one token per tile; V is
-// dim-major inside each half block, so the same lane reads tokens
-// 32c + 8qq .. + 7 of dim 16t + j: both operands straight from HBM, 1 KB of
-// consecutive bytes per load instruction, no transposition.
+// token-major: score tile m takes dims 8 (4m + qq) .. + 7 on lane (row j,
+// qq), so one load instruction reads 64 consecutive bytes of each of its 16
+// rows (the query operand uses the same dim order).  V is dim-major inside
+// each half block, so the same lane reads tokens 32c + 8qq .. + 7 of dim
+// 16t + j, 1 KB of consecutive bytes per load instruction.  Both operands
+// come straight from HBM, with no transposition.
 template <int D>
 __device__ inline void exact_load(EUnit<D>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq, int lane) {
   constexpr int MK = D / 32, NT = D / 16;
@@ -772,9 +774,9 @@ __device__ inline void exact_load(EUnit<D>& u, const AttnParams& p, int pb, int 
 #pragma unroll
   for (int tp = 0; tp < 2; ++tp) {
     int row = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
-    const u32x4* src = reinterpret_cast<const u32x4*>(kslab + row * D + qq * (D / 4));
+    const u32x4* src = reinterpret_cast<const u32x4*>(kslab + row * D + 8 * qq);
 #pragma unroll
-    for (int m = 0; m < MK; ++m) u.kx[tp][m] = src[m];
+    for (int m = 0; m < MK; ++m) u.kx[tp][m] = src[4 * m];
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -834,14 +836,14 @@ __device__ void exact_split(const AttnParams& p, const Lds& L, int b, int kv, in
   const int start = s * p.Pe;
   const int blk0 = start >> 6;
   const WaveBlocks wb_all = load_split_blocks(p.etab + (size_t)b * p.emax, p.emax, blk0, p.Pe, w, lane);
-  // query operand: lane (col j, qq) holds dims qq*D/4 + 8m + e of head j
+  // query operand: lane (col j, qq) holds dims 8 (4m + qq) + e of head j
   bf16x8 Q[MK];
   {
     const int hj = min(j, G - 1);  // padded columns read a valid head, then zero
-    const uint16_t* qsrc = p.q + ((size_t)b * p.Hq + kv * G + hj) * D + qq * (D / 4);
+    const uint16_t* qsrc = p.q + ((size_t)b * p.Hq + kv * G + hj) * D + 8 * qq;
 #pragma unroll
     for (int m = 0; m < MK; ++m) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(qsrc + 8 * m);
+      u32x4 x = *reinterpret_cast<const u32x4*>(qsrc + 32 * m);
       if (j >= G) x = u32x4{0, 0, 0, 0};
       Q[m] = __builtin_bit_cast(bf16x8, x);
     }
