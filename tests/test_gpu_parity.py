@@ -207,6 +207,19 @@ def test_exact32k_single_split_within_tolerance(exact32k):
     assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "exact32k (1 split)")
 
 
+def _same_again(dw, label):
+    """A second call (outputs cleared first) gives the same bytes: fixed split
+    plan and fixed reduction order."""
+    akv, _ = _mods()
+    o1, l1 = dw.o.clone(), dw.lse.clone()
+    dw.o.fill_(float("nan"))
+    dw.lse.fill_(float("nan"))
+    akv.check(dw.attend())
+    torch.cuda.synchronize()
+    assert torch.equal(dw.o, o1) and torch.equal(dw.lse, l1), f"{label}: not bit-identical run to run"
+    _say(f"{label}: second call bit-identical")
+
+
 @pytest.mark.slow
 def test_hybrid128k():
     w = synth.make("hybrid128k")
@@ -214,6 +227,7 @@ def test_hybrid128k():
     o_ref, lse_ref, ek, ev = oracle_case(w)
     assert_codes(dw, w, ek, ev, "hybrid128k")
     assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "hybrid128k")
+    _same_again(dw, "hybrid128k")
 
 
 @pytest.mark.slow
@@ -227,6 +241,7 @@ def test_ragged_sampled():
     o, lse = dw.o.cpu().numpy(), dw.lse.cpu().numpy()
     assert_attention(o[seqs], lse[seqs], o_ref[seqs], lse_ref[seqs], f"ragged seqs {seqs}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    _same_again(dw, "ragged")
 
 
 # ------------------------------------------------------------------ merge
