@@ -221,7 +221,6 @@ __device__ inline void quant_stage_k(const QRegs<D>& r, unsigned char* smem, uns
 // Compressed V -> LDS as V^T (fp16 level pair x fp16 scale pair).
 template <int D>
 __device__ inline void quant_stage_v(const QRegs<D>& r, unsigned char* smem, unsigned char* buf, int nvalid) {
-  constexpr int VP = ChunkLds<D>::VP;
   const uint32_t* vlut = reinterpret_cast<const uint32_t*>(smem + ChunkLds<D>::VLUT);
 #pragma unroll
   for (int u = 0; u < kVT; ++u) {
@@ -298,7 +297,7 @@ template <int D, bool QUANT>
 __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, int tb, int end, const int (&climit)[kRT],
                                     const half8 (&Qh)[kRT][D / 32], const half8 (&Ql)[kRT][D / 32],
                                     const bf16x8 (&Qe)[kRT][D / 32], float qs, RowState<D>& rs) {
-  constexpr int M = D / 32, NT = D / 16, VP = ChunkLds<D>::VP;
+  constexpr int M = D / 32, NT = D / 16;
   const int lane = threadIdx.x & 63, j = lane & 15, qq = lane >> 4;
   // scores: row i of tile tp is token 32c + 8(i/4) + 4tp + i%4, so lane
   // (j, qq) ends up with tokens 32c + 8qq + 0..7 of row j
