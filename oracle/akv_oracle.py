@@ -475,11 +475,10 @@ def append_evict_step(exact_k: np.ndarray, exact_v: np.ndarray, quant_k: np.ndar
     token, so the codes of a moved token are ``encode`` of its bf16 values).
 
     The new token goes to the end of the exact tier.  When the exact tier then
-    holds window + 64 tokens, the compressed tier has room for 64 more and its
-    length is even (two tokens share a value-code byte), the 64 oldest exact
-    tokens move, in order, to the end of the compressed tier.  Capacities are
-    in tokens.  Returns the four new arrays, or None when the exact tier has no
-    room for the new token.
+    holds window + 64 tokens and the compressed tier has room for 64 more, the
+    64 oldest exact tokens move, in order, to the end of the compressed tier,
+    whatever its current length.  Capacities are in tokens.  Returns the four
+    new arrays, or None when the exact tier has no room for the new token.
     """
     n = exact_k.shape[0]
     if n + 1 > exact_capacity:
@@ -488,7 +487,7 @@ def append_evict_step(exact_k: np.ndarray, exact_v: np.ndarray, quant_k: np.ndar
     ev = np.concatenate([exact_v, new_v[None]], axis=0)
     qk, qv = quant_k, quant_v
     m = qk.shape[0]
-    if n + 1 >= window + 64 and m + 64 <= quant_capacity and m % 2 == 0:
+    if n + 1 >= window + 64 and m + 64 <= quant_capacity:
         qk = np.concatenate([qk, ek[:64]], axis=0)
         qv = np.concatenate([qv, ev[:64]], axis=0)
         ek, ev = ek[64:], ev[64:]

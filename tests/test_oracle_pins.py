@@ -470,13 +470,14 @@ def _run_steps(ek, ev, qk, qv, new_k, new_v, window, ecap, qcap):
     return ek, ev, qk, qv, lens
 
 
-@pytest.mark.parametrize("e0", [128, 150, 191])
-def test_append_evict_lengths_closed_form(e0):
+@pytest.mark.parametrize("e0,q0", [(128, 40), (150, 41), (191, 40), (191, 7)])
+def test_append_evict_lengths_closed_form(e0, q0):
     """With room everywhere the exact tier cycles through [W, W + 63] and every
-    64th append moves one block: after t steps it holds W + (e0 - W + t) mod 64
-    tokens and the compressed tier q0 + 64 * floor((e0 - W + t) / 64)."""
+    64th append moves one block, for an even or an odd compressed length alike:
+    after t steps the exact tier holds W + (e0 - W + t) mod 64 tokens and the
+    compressed tier q0 + 64 * floor((e0 - W + t) / 64)."""
     rng = np.random.default_rng(1)
-    W, q0, T = 128, 40, 150
+    W, T = 128, 150
     ek, ev = _tokens(rng, e0), _tokens(rng, e0)
     qk, qv = _tokens(rng, q0), _tokens(rng, q0)
     nk, nv = _tokens(rng, T), _tokens(rng, T)
@@ -498,7 +499,7 @@ def test_append_evict_conserves_the_history_order():
     assert gk.shape[0] > qk.shape[0]
 
 
-def test_append_evict_full_or_odd_compressed_tier_keeps_growing_the_window():
+def test_append_evict_full_compressed_tier_keeps_growing_the_window():
     rng = np.random.default_rng(3)
     ek, ev = _tokens(rng, 191), _tokens(rng, 191)
     nk, nv = _tokens(rng, 5), _tokens(rng, 5)
@@ -506,12 +507,23 @@ def test_append_evict_full_or_odd_compressed_tier_keeps_growing_the_window():
     qk, qv = _tokens(rng, 100), _tokens(rng, 100)
     fk, _, gk, _, lens = _run_steps(ek, ev, qk, qv, nk, nv, 128, 10 ** 6, 120)
     assert [l[0] for l in lens] == [192, 193, 194, 195, 196] and gk.shape[0] == 100
-    # odd compressed length: two tokens would share a value byte across calls
-    qk, qv = _tokens(rng, 99), _tokens(rng, 99)
-    *_, lens = _run_steps(ek, ev, qk, qv, nk, nv, 128, 10 ** 6, 10 ** 6)
-    assert [l[1] for l in lens] == [99] * 5
     # exact tier at capacity: the step is refused
     assert O.append_evict_step(ek, ev, qk, qv, nk[0], nv[0], 128, 191, 10 ** 6) is None
+
+
+def test_append_evict_moves_a_block_onto_an_odd_compressed_length():
+    """The tiers are token lists: how many tokens the compressed tier already
+    holds has no bearing on when the window's oldest block moves.  A 99-token
+    compressed tier takes the block on the step that fills the window, and the
+    moved tokens follow token 98 in order."""
+    rng = np.random.default_rng(5)
+    ek, ev = _tokens(rng, 191), _tokens(rng, 191)
+    qk, qv = _tokens(rng, 99), _tokens(rng, 99)
+    nk, nv = _tokens(rng, 3), _tokens(rng, 3)
+    fk, fv, gk, gv, lens = _run_steps(ek, ev, qk, qv, nk, nv, 128, 10 ** 6, 10 ** 6)
+    assert lens == [(128, 163), (129, 163), (130, 163)]
+    assert np.array_equal(gk, np.concatenate([qk, ek[:64]])) and np.array_equal(gv, np.concatenate([qv, ev[:64]]))
+    assert np.array_equal(fk, np.concatenate([ek[64:], nk])) and np.array_equal(fv, np.concatenate([ev[64:], nv]))
 
 
 def test_encoding_is_per_token():
