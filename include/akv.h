@@ -1,10 +1,11 @@
 /*
  * akv.h -- split-KV, two-tier decode attention for AMD Instinct MI355X (gfx950).
  *
- * A key/value history is held in two tiers (ActiveKV, "Context beyond VRAM",
- * section "What I built": recent context stays exact, older history is held in
- * a compact form the GPU reads directly, and the two are merged with exact
- * attention arithmetic):
+ * A key/value history is held in two tiers, after the two-precision cache of
+ * ActiveKV ("Context beyond VRAM", section "What I built"): a window of the
+ * newest tokens in full precision, the older tokens in a small encoded form
+ * that the attention kernels read in place, and one exact log-sum-exp merge
+ * joining the two:
  *
  *   exact tier       bfloat16 K and V, paged in 64-token blocks;
  *   compressed tier  K and V rotated by the normalized Walsh-Hadamard matrix
@@ -215,10 +216,13 @@ typedef akv_attn_desc akv_chunk_desc;
  * gets scale = fp16(sqrt(mean of squares)) and every element the index of
  * the nearest Lloyd-Max level to value/scale (exact ties to the lower index;
  * all-zero groups give index 7, or 2^(w-1) - 1 at code width w).  Codes and
- * scales are bit-exact functions of the input.  Source tokens [src_start, src_start+n_tokens) of the exact
- * tier's block table land at compressed positions [dst_start, dst_start +
- * n_tokens).  dst_start must be even (two tokens share a V byte); for odd
- * n_tokens the unused half of the last V byte is written as 0. */
+ * scales are bit-exact functions of the input.  Source tokens [src_start,
+ * src_start + n_tokens) of the exact tier's block table land at compressed
+ * positions [dst_start, dst_start + n_tokens); dst_start may be odd.  Two
+ * tokens share each value-code byte, so where the range begins or ends inside
+ * such a byte, the half of the neighbouring position is read and kept: no
+ * byte outside the range changes.  Each byte has one writer within a call,
+ * and calls that write the same compressed positions must not overlap. */
 typedef struct akv_compress_desc {
   uint32_t struct_size;        /* sizeof(akv_compress_desc) */
   int32_t Hkv, d;
@@ -284,7 +288,13 @@ typedef struct akv_staging_desc {
   void* const* events;         /* host array of 2*slots + 1 hipEvent_t */
 } akv_staging_desc;
 
-/* Split-KV decode attention, one query token per sequence.
+/* Split-KV decode attention, one query token per sequence (ActiveKV,
+ * "Context beyond VRAM", "What I built": each tier of the history gives its
+ * own partial result and the partials are joined by exact attention
+ * arithmetic; the compressed tier is read through a query rotated once,
+ * because the Hadamard rotation keeps dot products -- QuantForge walkthrough,
+ * section 1, "Triton Fused Kernels"; each partial carries the log-sum-exp
+ * statistic of "Bringing a serving stack up on new silicon", "What I built").
  * Enqueues two kernels: a split kernel in which every (split, kv head,
  * sequence) workgroup attends its split (the compressed tier with the
  * pre-rotated query and the value sum kept in rotated space) and writes a
@@ -298,10 +308,9 @@ typedef struct akv_staging_desc {
 akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
 /* akv_attend_decode with the compressed tier streamed from pinned host memory
- * (ActiveKV, "Context beyond VRAM", "What I built": the authoritative history
- * stays in host memory, the GPU keeps a budgeted staging region, and a
- * staging buffer is reused only after every kernel that read it has
- * finished).  The exact tier and the query are on the device as in
+ * (ActiveKV, "Context beyond VRAM", "What I built": host memory owns the
+ * history, device memory holds a bounded staging area, and no staged bytes
+ * are overwritten while a kernel may still read them).  The exact tier and the query are on the device as in
  * akv_attend_decode; desc->quant supplies lengths (device, for the merge) and
  * max_blocks (the split plan), and its pools and table may be NULL.  Per
  * sequence, runs of whole compressed splits (their records, one
@@ -330,7 +339,11 @@ akv_status akv_attend_decode_staged(const akv_attn_desc* desc, const akv_staging
  * akv_chunk_workspace_bytes(desc) bytes. */
 akv_status akv_attend_chunk(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
-/* Exact log-sum-exp merge of P normalized partials of R rows of width d:
+/* Exact log-sum-exp merge of P normalized partials of R rows of width d (the
+ * per-row log-sum-exp that "Bringing a serving stack up on new silicon",
+ * "What I built", adds to paged attention is what lets partial results over
+ * disjoint pieces of a history be joined exactly, as ActiveKV joins its two
+ * tiers -- "Context beyond VRAM", "What I built"):
  * o_parts [P][R][d], lse_parts [P][R] (natural log), outputs o_out [R][d],
  * lse_out [R].  Per row: M = max_p lse_p; if M = -inf the row is empty and
  * gets o = 0, lse = -inf; else w_p = exp(lse_p - M), W = sum_p w_p,
@@ -351,8 +364,8 @@ akv_status akv_compress_evicted(const akv_compress_desc* desc, void* stream);
  * read on the device:
  *   1. the new token's K and V (bf16 [B][Hkv][d]) are written at exact-tier
  *      position n (block exact_table[b][n / 64], layouts above);
- *   2. if n + 1 >= window + 64, m + 64 <= 64 * quant_max_blocks and m is even,
- *      the 64 oldest exact tokens (the first block of the row) are rotated
+ *   2. if n + 1 >= window + 64 and m + 64 <= 64 * quant_max_blocks (any m,
+ *      even or odd), the 64 oldest exact tokens (the first block of the row) are rotated
  *      and encoded into compressed positions [m, m + 64) exactly as
  *      akv_compress_evicted encodes them, the ceil((n + 1) / 64) entries in
  *      use of the exact table row rotate left by one (the freed block comes

@@ -451,7 +451,6 @@ akv_status akv_compress_evicted(const akv_compress_desc* d, void* stream) {
     return fail(AKV_ERR_SHAPE, "token range exceeds a block table");
   if (d->d != 64 && d->d != 128) return fail(AKV_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
   if (!width_ok(d->code_bits)) return fail(AKV_ERR_UNSUPPORTED, "code_bits %d (supported: 2, 3, 4)", d->code_bits);
-  if (d->dst_start & 1) return fail(AKV_ERR_UNSUPPORTED, "dst_start must be even");
   if (d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "Hkv must be <= 65535");
   if (!aligned(d->src_k, 2) || !aligned(d->src_v, 2) || !aligned(d->dst_k_scales, 2) ||
       !aligned(d->dst_v_scales, 2) || !aligned(d->src_block_table, 4) || !aligned(d->dst_block_table, 4))

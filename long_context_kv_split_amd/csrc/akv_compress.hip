@@ -23,9 +23,14 @@
 // compares a QR rotation with the Hadamard one), E2 is y = R x summed in
 // ascending k and E3 is dropped.
 //
-// One wavefront per (token pair, kv head, K|V) -- per 8 pairs with a given
-// rotation, which then share each load of R: lane l holds elements l + 64k;
-// butterflies with h < 64 exchange across lanes.
+// One wavefront per (destination token pair, kv head, K|V) -- per 8 pairs with
+// a given rotation, which then share each load of R: lane l holds elements
+// l + 64k; butterflies with h < 64 exchange across lanes.  Destination pairs
+// are aligned to the compressed tier's positions (2q, 2q + 1), because two
+// tokens share each value-code byte: when the range starts at an odd position
+// the first pair holds one token already there, and a pair's byte is read,
+// merged and written back by its one wavefront, so every byte has one writer
+// and the bits of positions outside the range keep their value.
 #include "akv_common.h"
 
 #pragma clang fp contract(off)
@@ -56,7 +61,7 @@ __device__ inline bool load_token(const CompressParams& p, int isv, int kv, int 
   constexpr int E = D / 64;
   const uint16_t* src = nullptr;
   const int dstride = isv ? kBlock / 2 : 1;
-  if (tok < p.n_tokens) {
+  if (tok >= 0 && tok < p.n_tokens) {
     const int s = p.src_start + tok;
     const int blk = p.src_table[s >> 6];
     if (blk >= 0 && blk < p.src_num_blocks) {
@@ -131,19 +136,19 @@ __device__ inline void dense_rows(const float* __restrict__ R, float (&x)[NT][D 
 // missing token), then each lane assembles whole output bytes.  K rows of
 // missing tokens are not written; a V byte always is.
 template <int D, int W>
-__device__ inline void store_narrow(const CompressParams& p, size_t slab, int r0, int ntok, int isv, int lane,
-                                    const int (&code)[2][D / 64], const bool (&ok)[2], unsigned char* cs) {
+__device__ inline void store_narrow(const CompressParams& p, size_t slab, int r0, const bool (&ours)[2], int isv,
+                                    int lane, const int (&code)[2][D / 64], const bool (&ok)[2], unsigned char* cs) {
   constexpr int E = D / 64, M = D / 32;
   __syncthreads();  // the previous pair's reads of cs are done
 #pragma unroll
   for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
-    for (int e = 0; e < E; ++e) cs[tk * D + lane + 64 * e] = (tk < ntok && ok[tk]) ? (unsigned char)code[tk][e] : 0;
+    for (int e = 0; e < E; ++e) cs[tk * D + lane + 64 * e] = (ours[tk] && ok[tk]) ? (unsigned char)code[tk][e] : 0;
   __syncthreads();
   if (!isv) {
     uint8_t* kslab = p.dst_kc + slab * (8 * W * D);
     for (int tk = 0; tk < 2; ++tk) {
-      if (!(tk < ntok && ok[tk])) continue;
+      if (!(ours[tk] && ok[tk])) continue;
       const unsigned char* ct = cs + tk * D;
       if (lane < D / 4) {  // pair plane: byte (d/16) a + 4 n + b of the row
         const int a = lane / (D / 16), r = lane % (D / 16), n = r >> 2, b = r & 3;
@@ -166,8 +171,13 @@ __device__ inline void store_narrow(const CompressParams& p, size_t slab, int r0
       }
     }
   } else {
+    // a byte holds bits of both tokens of the pair; those of a position
+    // outside the range are kept (pair plane: bits 2e, 2e + 1, 4 + 2e,
+    // 5 + 2e of token e; high plane: bits 2h + e)
     uint8_t* vslab = p.dst_vc + slab * (8 * W * D);
     const int c = r0 >> 5, a = (r0 >> 3) & 3, b = (r0 >> 1) & 3;
+    const int keep2 = (ours[0] ? 0 : 0x33) | (ours[1] ? 0 : 0xCC);
+    const int keep1 = (ours[0] ? 0 : 0x55) | (ours[1] ? 0 : 0xAA);
     for (int l = lane; l < D / 2; l += 64) {  // pair plane: dim 16(2n + h) + i
       const int i = l & 15, n = l >> 4;
       int byte = 0;
@@ -175,7 +185,9 @@ __device__ inline void store_narrow(const CompressParams& p, size_t slab, int r0
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 2; ++e) byte |= (cs[e * D + 16 * (2 * n + h) + i] & 3) << (4 * h + 2 * e);
-      vslab[((c * 4 + a) * 16 + i) * (D / 8) + 4 * n + b] = (uint8_t)byte;
+      uint8_t* dst = vslab + ((c * 4 + a) * 16 + i) * (D / 8) + 4 * n + b;
+      if (keep2) byte = (byte & ~keep2) | (*dst & keep2);
+      *dst = (uint8_t)byte;
     }
     if (W == 3) {
       for (int l = lane; l < D / 4; l += 64) {  // high plane: dim 16(4n + h) + i
@@ -185,21 +197,34 @@ __device__ inline void store_narrow(const CompressParams& p, size_t slab, int r0
         for (int h = 0; h < 4; ++h)
 #pragma unroll
           for (int e = 0; e < 2; ++e) byte |= ((cs[e * D + 16 * (4 * n + h) + i] >> 2) & 1) << (2 * h + e);
-        vslab[16 * D + ((c * 4 + a) * 16 + i) * (D / 16) + 4 * n + b] = (uint8_t)byte;
+        uint8_t* dst = vslab + 16 * D + ((c * 4 + a) * 16 + i) * (D / 16) + 4 * n + b;
+        if (keep1) byte = (byte & ~keep1) | (*dst & keep1);
+        *dst = (uint8_t)byte;
       }
     }
   }
 }
 
-// E4..E9 for token pair `pair` (tokens 2 pair, 2 pair + 1 of the range) of
-// one (kv head, K|V), given its rotated values y (lane l: elements l + 64k),
-// at code width W (cs: 2 * D bytes of LDS, this wavefront's own).
+// Source token (index in the range) of slot tk of destination pair `pair`:
+// the pair covers compressed positions (dst_start & ~1) + 2 pair + {0, 1}.
+__device__ inline int pair_token(const CompressParams& p, int pair, int tk) {
+  return 2 * pair + tk - (p.dst_start & 1);
+}
+
+// E4..E9 for destination pair `pair` of one (kv head, K|V), given its rotated
+// values y (lane l: elements l + 64k), at code width W (cs: 2 * D bytes of
+// LDS, this wavefront's own).  A slot whose position is outside the range is
+// not ours: nothing of it is written, and its half of the value byte is kept.
 template <int D, int W>
 __device__ inline void finish_pair(const CompressParams& p, int pair, int kv, int isv, int lane,
                                    const float (&y)[2][D / 64], const bool (&ok)[2], unsigned char* cs) {
   constexpr int E = D / 64;
-  const int first = 2 * pair;
-  const int ntok = min(2, p.n_tokens - first);
+  bool ours[2];
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk) {
+    const int t = pair_token(p, pair, tk);
+    ours[tk] = t >= 0 && t < p.n_tokens;
+  }
   int code[2][E];
   uint16_t s16[2][E];
 #pragma unroll
@@ -231,19 +256,19 @@ __device__ inline void finish_pair(const CompressParams& p, int pair, int kv, in
   }
 
   // E9: store
-  const int pos0 = p.dst_start + first;   // even
+  const int pos0 = (p.dst_start & ~1) + 2 * pair;   // even
   const int dblk = p.dst_table[pos0 >> 6];
   if (dblk < 0 || dblk >= p.dst_num_blocks) return;
   const int r0 = pos0 & 63;
   const size_t slab = (size_t)dblk * p.Hkv + kv;
   uint16_t* scales = (isv ? p.dst_vs : p.dst_ks) + slab * (2 * D);
   if constexpr (W < 4) {
-    store_narrow<D, W>(p, slab, r0, ntok, isv, lane, code, ok, cs);
+    store_narrow<D, W>(p, slab, r0, ours, isv, lane, code, ok, cs);
 #pragma unroll
     for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (tk < ntok && ok[tk] && (lane & 31) == 0) scales[((lane + 64 * e) >> 5) * kBlock + r0 + tk] = s16[tk][e];
+        if (ours[tk] && ok[tk] && (lane & 31) == 0) scales[((lane + 64 * e) >> 5) * kBlock + r0 + tk] = s16[tk][e];
     return;
   }
   if (!isv) {
@@ -254,28 +279,33 @@ __device__ inline void finish_pair(const CompressParams& p, int pair, int kv, in
       for (int e = 0; e < E; ++e) {
         int hi = __shfl_down(code[tk][e], 1);
         int dim = lane + 64 * e;
-        if (tk < ntok && ok[tk] && !(lane & 1))
+        if (ours[tk] && ok[tk] && !(lane & 1))
           codes[(r0 + tk) * (D / 2) + kcode_byte(D, dim)] = (uint8_t)(code[tk][e] | (hi << 4));
-        if (tk < ntok && ok[tk] && (lane & 31) == 0)
+        if (ours[tk] && ok[tk] && (lane & 31) == 0)
           scales[(dim >> 5) * kBlock + r0 + tk] = s16[tk][e];
       }
     }
   } else {
     uint8_t* codes = p.dst_vc + slab * (32 * D);
+    // the nibble of a position outside the range is kept
+    const int keep = (ours[0] ? 0 : 0x0F) | (ours[1] ? 0 : 0xF0);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       int dim = lane + 64 * e;
-      int c0 = ok[0] ? code[0][e] : 0;
-      int c1 = (ntok > 1 && ok[1]) ? code[1][e] : 0;
-      codes[vcode_byte(D, r0, dim)] = (uint8_t)(c0 | (c1 << 4));
+      int c0 = (ours[0] && ok[0]) ? code[0][e] : 0;
+      int c1 = (ours[1] && ok[1]) ? code[1][e] : 0;
+      uint8_t* dst = codes + vcode_byte(D, r0, dim);
+      int byte = c0 | (c1 << 4);
+      if (keep) byte = (byte & ~keep) | (*dst & keep);
+      *dst = (uint8_t)byte;
 #pragma unroll
       for (int tk = 0; tk < 2; ++tk)
-        if (tk < ntok && ok[tk] && (lane & 31) == 0) scales[(dim >> 5) * kBlock + r0 + tk] = s16[tk][e];
+        if (ours[tk] && ok[tk] && (lane & 31) == 0) scales[(dim >> 5) * kBlock + r0 + tk] = s16[tk][e];
     }
   }
 }
 
-// Encode token pairs pair0 .. pair0 + NP - 1 of one (kv head, K|V): one
+// Encode destination pairs pair0 .. pair0 + NP - 1 of one (kv head, K|V): one
 // wavefront, lane l holding elements l + 64k.  With a given rotation the NP
 // pairs share the loads of R (xs: 2 * NP * D floats of LDS).
 template <int D, int NP, int W>
@@ -286,7 +316,7 @@ __device__ inline void encode_pairs(const CompressParams& p, int pair0, int kv, 
   float x[2 * NP][E];
   bool ok[2 * NP];
 #pragma unroll
-  for (int i = 0; i < 2 * NP; ++i) ok[i] = load_token<D>(p, isv, kv, 2 * pair0 + i, lane, x[i]);   // E1
+  for (int i = 0; i < 2 * NP; ++i) ok[i] = load_token<D>(p, isv, kv, pair_token(p, pair0, i), lane, x[i]);  // E1
   if (p.rot) {
     dense_rows<D, 2 * NP>(p.rot, x, lane, xs);                                                       // E2
   } else {
@@ -295,7 +325,7 @@ __device__ inline void encode_pairs(const CompressParams& p, int pair0, int kv, 
   }
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
-    if (2 * (pair0 + j) >= p.n_tokens) break;
+    if (pair_token(p, pair0 + j, 0) >= p.n_tokens) break;
     float y[2][E];
     const bool okp[2] = {ok[2 * j], ok[2 * j + 1]};
 #pragma unroll
@@ -348,21 +378,22 @@ __device__ inline StepPlan step_plan(const StepParams& p, int b) {
   s.n = p.elen[b];
   s.m = p.qlen[b];
   s.append = s.n >= 0 && (s.n >> 6) < p.emax;
-  s.evict = s.append && s.n + 1 >= p.window + kBlock && s.m >= 0 && s.m + kBlock <= p.qmax * kBlock && !(s.m & 1);
+  s.evict = s.append && s.n + 1 >= p.window + kBlock && s.m >= 0 && s.m + kBlock <= p.qmax * kBlock;
   return s;
 }
 
-// grid (33, Hkv, 2B): x < 32 encodes token pair x of the evicted block (when
-// the sequence evicts), x == 32 writes the new token; z = 2 b + (K|V).  The
-// append writes block n / 64 >= 1 while the encode reads block 0, so the two
-// never touch the same bytes.
+// grid (34, Hkv, 2B): x < 33 encodes destination pair x of the evicted block
+// (when the sequence evicts; 64 tokens at compressed position m take 32 pairs
+// for an even m and 33 for an odd one), x == 33 writes the new token;
+// z = 2 b + (K|V).  The append writes block n / 64 >= 1 while the encode reads
+// block 0, so the two never touch the same bytes.
 template <int D, int W>
 __global__ __launch_bounds__(64) void append_evict_kernel(StepParams p) {
   __shared__ __attribute__((aligned(16))) float xs[2 * D];
   __shared__ unsigned char cs[2 * D];
   const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z >> 1, isv = blockIdx.z & 1, lane = threadIdx.x;
   const StepPlan s = step_plan(p, b);
-  if (x == kBlock / 2) {
+  if (x == kBlock / 2 + 1) {
     if (!s.append) return;
     const int pb = p.etab[(size_t)b * p.emax + (s.n >> 6)];
     if (pb < 0 || pb >= p.enb) return;  // the attention reports the bad id as NaN
@@ -379,7 +410,7 @@ __global__ __launch_bounds__(64) void append_evict_kernel(StepParams p) {
     }
     return;
   }
-  if (!s.evict) return;
+  if (!s.evict || x >= (kBlock + 1 + (s.m & 1)) / 2) return;
   CompressParams c;
   c.Hkv = p.Hkv;
   c.src_k = p.ek;
@@ -460,8 +491,9 @@ hipError_t launch_compress(const akv_compress_desc* d, hipStream_t stream) {
   p.dst_num_blocks = d->dst_num_blocks;
   p.dst_start = d->dst_start;
   p.rot = d->rotation;
-  // a given rotation: 8 pairs per wavefront share each load of R
-  const int pairs = (d->n_tokens + 1) / 2;
+  // destination pairs (aligned to even positions); a given rotation: 8 pairs
+  // per wavefront share each load of R
+  const int pairs = ((d->dst_start & 1) + d->n_tokens + 1) / 2;
   const int W = code_width(d->code_bits);
   if (p.rot) {
     dim3 grid((pairs + kDensePairs - 1) / kDensePairs, d->Hkv, 2);
@@ -501,7 +533,7 @@ hipError_t launch_append_evict(const akv_append_desc* d, hipStream_t stream) {
   p.qmax = d->quant_max_blocks;
   p.qnb = d->quant_num_blocks;
   p.rot = d->rotation;
-  dim3 grid(kBlock / 2 + 1, d->Hkv, 2 * d->B);
+  dim3 grid(kBlock / 2 + 2, d->Hkv, 2 * d->B);
   const int W = code_width(d->code_bits);
   if (d->d == 64)
     launch_append_w<64>(W, grid, stream, p);

@@ -18,7 +18,8 @@ The workloads are the five decode / prefill-chunk configurations of the
 hybrid-tier method (ActiveKV, "Context beyond VRAM", section "What I built";
 QuantForge walkthrough, section 1 for the rotated 4-bit tier):
 
-* ``tiny``       1 x (4 q heads / 1 kv head), d=64, 384 compressed + 128 exact
+* ``tiny``       1 x (4 q heads / 1 kv head), d=64, 384 compressed + 128 exact,
+                 one split per tier
 * ``exact32k``   1 x (32/4), d=128, 32,768 exact tokens, 16 fixed partitions
 * ``hybrid128k`` 1 x (32/4), d=128, 123,904 compressed + 4,096 exact, 1% outliers
 * ``ragged``     32 x (32/4), d=128, lengths U{4096..65536}, 2,048-token window
@@ -140,7 +141,9 @@ def _deal_tables(rng: np.random.Generator, lengths: List[int], reserve: List[int
 def make(name: str, seed: int = 0) -> Workload:
     """Build one of the five named workloads (seed 0 is the recipe's seed)."""
     if name == "tiny":
-        return _decode(name, seed, B=1, Hq=4, Hkv=1, d=64, quant=[384], exact=[128])
+        # two splits merged by log-sum-exp: one per tier
+        return _decode(name, seed, B=1, Hq=4, Hkv=1, d=64, quant=[384], exact=[128],
+                       split_quant=384, split_exact=128)
     if name == "exact32k":
         return _decode(name, seed, B=1, Hq=32, Hkv=4, d=128, quant=[0], exact=[32768],
                        split_exact=2048)
@@ -148,13 +151,17 @@ def make(name: str, seed: int = 0) -> Workload:
         return _decode(name, seed, B=1, Hq=32, Hkv=4, d=128, quant=[123904], exact=[4096],
                        outlier_frac=0.01)
     if name == "ragged":
-        lrng = stream(seed, "lengths")
-        lens = lrng.integers(4096, 65536, size=32, endpoint=True)
+        lens = ragged_lengths(seed)
         return _decode(name, seed, B=32, Hq=32, Hkv=4, d=128,
                        quant=[int(n) - 2048 for n in lens], exact=[2048] * 32)
     if name == "chunk":
         return _chunk(name, seed)
     raise KeyError(name)
+
+
+def ragged_lengths(seed: int = 0) -> np.ndarray:
+    """History lengths of the ragged batch: 32 draws uniform on [4096, 65536]."""
+    return stream(seed, "lengths").integers(4096, 65536, size=32, endpoint=True)
 
 
 def make_small(name: str, seed: int = 0, **kw) -> Workload:

@@ -217,7 +217,9 @@ def test_compress_validation():
     assert f(compress_desc(src_start=72 * 64 - 511)) == akv.AKV_ERR_SHAPE
     assert f(compress_desc(dst_start=456 * 64 - 510)) == akv.AKV_ERR_SHAPE
     assert f(compress_desc(d=32)) == akv.AKV_ERR_UNSUPPORTED
-    assert f(compress_desc(dst_start=28671)) == akv.AKV_ERR_UNSUPPORTED
+    # an odd destination start is served (the shared value bytes are merged)
+    assert f(compress_desc(dst_start=28671, dst_k_scales=FAKE + 0x500001)) == akv.AKV_ERR_ALIGN
+    assert f(compress_desc(dst_start=28671, n_tokens=0)) == akv.AKV_OK
     assert f(compress_desc(dst_k_scales=FAKE + 0x500001)) == akv.AKV_ERR_ALIGN
     assert f(compress_desc(n_tokens=0)) == akv.AKV_OK
 
@@ -237,8 +239,11 @@ def test_frozen_device_constants_match_oracle():
         body = re.search(name + r"\[\d+\] = \{(.*?)\};", src, re.S).group(1)
         return np.array([int(x, 16) for x in re.findall(r"0x([0-9A-Fa-f]+)u", body)], dtype=np.uint32)
 
-    assert np.array_equal(table("kLevelBits"), O.centroids_f32().view(np.uint32))
-    assert np.array_equal(table("kThreshBits"), O.thresholds_f32().view(np.uint32))
+    for suffix, width in (("", 4), ("2", 2), ("3", 3)):
+        levels, thresh = table("kLevelBits" + suffix), table("kThreshBits" + suffix)
+        assert levels.size == 2 ** width and thresh.size == 2 ** width - 1
+        assert np.array_equal(levels, O.centroids_f32(width).view(np.uint32)), f"levels, width {width}"
+        assert np.array_equal(thresh, O.thresholds_f32(width=width).view(np.uint32)), f"thresholds, width {width}"
     assert "0x3DB504F3u" in src and O.inv_sqrt_f32(128).view(np.uint32) == 0x3DB504F3
 
 

@@ -109,6 +109,31 @@ def test_append_evict_steps_match_oracle(d):
     _check_attention(dw, w, ref, f"d={d} attention after {S} steps")
 
 
+def test_append_evict_odd_compressed_lengths_of_the_ragged_batch():
+    """Three sequences with compressed lengths that the ragged batch draws
+    (history length - 2048, odd for 14 of its 32 sequences) and its 2,048-token
+    window.  Sequences 0 and 2 start one token short of a move, so the first
+    step moves a block onto an odd compressed length (and sequence 0 moves a
+    second one, again onto an odd length, 64 steps later); sequence 1 moves
+    after 24 steps."""
+    akv, harness = _mods()
+    W, S = 2048, 70
+    odd = [int(n) - W for n in synth.ragged_lengths(0) if (int(n) - W) % 2]
+    quant = [odd[0], odd[5], odd[12]]
+    assert all(m % 2 for m in quant)
+    w = synth.make_small("step_odd", B=3, Hq=8, Hkv=2, d=128, quant=quant, exact=[W + 63, W + 40, W + 63],
+                         reserve_exact=[1, 1, 1], reserve_quant=[3, 3, 3])
+    _say(f"append/evict odd lengths: compressed {quant}, exact {list(w.exact_len)}, window {W}")
+    dw = harness.DeviceWorkload(w)
+    nk, nv = synth.step_tokens(2, S, w.B, w.Hkv, w.d)
+    _run_steps(dw, nk, nv, W, 1)
+    _check_state(dw, w, nk, nv, W, 1, "odd lengths after 1 step")
+    _run_steps_from(dw, nk, nv, W, 1, S)
+    ref = _check_state(dw, w, nk, nv, W, S, f"odd lengths after {S} steps")
+    assert [int(x) for x in dw.quant_len.tolist()] == [quant[0] + 128, quant[1] + 64, quant[2] + 128]
+    _check_attention(dw, w, ref, f"odd lengths attention after {S} steps")
+
+
 def _run_steps_from(dw, nk, nv, window, t0, t1):
     _run_steps(dw, nk[t0:t1], nv[t0:t1], window, t1 - t0)
 
