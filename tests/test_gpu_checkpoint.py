@@ -1,10 +1,12 @@
 """GPU tests of the context checkpoint (akv_checkpoint_save / _restore).
 
 The image depends only on the tokens, so a context saved from one block
-placement and restored into another (zeroed) placement must attend bit for
-bit like the original, save back to the same bytes, and keep doing so
-through further append / evict steps.  A damaged header or a bad table entry
-turns the affected sequences' attention into NaN.
+placement and restored into another (zeroed) placement must hold the saved
+tokens (codes and scales bit-exact against the oracle's encoding), attend
+within the decode tolerances of the float64 oracle over them and bit for bit
+like the original, save back to the same bytes, and keep doing so through
+further append / evict steps (replayed by the oracle).  A damaged header or a
+bad table entry turns the affected sequences' attention into NaN.
 """
 import copy
 
@@ -15,7 +17,9 @@ torch = pytest.importorskip("torch")
 
 from long_context_kv_split_amd import synth
 
-from test_gpu_parity import _mods, _say
+from oracle import akv_oracle as O
+from test_gpu_parity import _mods, _say, assert_attention, assert_codes, oracle_case
+from test_gpu_step import _replay
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +97,10 @@ def test_restore_into_another_placement_is_bit_identical(d):
     img2 = _save(dw2)
     assert torch.equal(img, img2), "image depends on the block placement"
     _say(f"checkpoint d={d}: {img.numel()} bytes, restore bit-identical, image placement-free")
+    o_ref, lse_ref, ek, ev = oracle_case(w)
+    assert_codes(dw2, w2, {b: ek[b] for b in range(w.B) if w.quant_len[b]},
+                 {b: ev[b] for b in range(w.B) if w.quant_len[b]}, f"restored d={d}")
+    assert_attention(o2.cpu().numpy(), l2.cpu().numpy(), o_ref, lse_ref, f"restored d={d} vs oracle")
 
 
 def test_restore_then_steps_stay_identical():
@@ -114,6 +122,21 @@ def test_restore_then_steps_stay_identical():
     o2, l2 = _attend(dw2)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     _say(f"checkpoint mid-stream: lengths {dw.exact_len.tolist()} / {dw.quant_len.tolist()}, identical after 10 more steps")
+    # the restored-and-stepped context against the oracle's replay of all 20 steps
+    o, lse = o2.cpu().numpy(), l2.cpu().numpy()
+    for b in range(w.B):
+        ek, ev, qk, qv = _replay(w, nk, nv, W, b, 20)
+        assert (int(dw2.exact_len[b].item()), int(dw2.quant_len[b].item())) == (ek.shape[0], qk.shape[0])
+        gk, gv = dw2.read_exact(b)
+        assert np.array_equal(gk, ek) and np.array_equal(gv, ev), f"seq {b}: exact tier bytes"
+        kc, ks = O.encode(qk)
+        vc, vs = O.encode(qv)
+        if qk.shape[0]:
+            ck, cks, cv, cvs = dw2.read_codes(b, 0, qk.shape[0])
+            assert np.array_equal(ck, kc) and np.array_equal(cks, ks), f"seq {b}: K codes / scales"
+            assert np.array_equal(cv, vc) and np.array_equal(cvs, vs), f"seq {b}: V codes / scales"
+        o_ref, lse_ref = O.decode_sequence(w.q[b], ek, ev, kc, ks, vc, vs)
+        assert_attention(o[b], lse[b], o_ref, lse_ref, f"restored + stepped seq {b} vs oracle")
 
 
 def test_damaged_image_or_table_gives_nan():

@@ -127,6 +127,9 @@ def test_qr_staged_equals_resident():
     torch.cuda.synchronize()
     assert torch.equal(dw.o, o_res) and torch.equal(dw.lse, l_res)
     _say("QR staged: bit-identical to resident")
+    ek, ev = _encoded(w, R, range(w.B))
+    o_ref, lse_ref = O.reference_outputs(w, [ek[b] for b in range(w.B)], [ev[b] for b in range(w.B)], rotation=R)
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "QR staged vs oracle")
 
 
 def test_qr_chunk_refused():

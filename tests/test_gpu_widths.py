@@ -147,6 +147,9 @@ def test_narrow_staged_equals_resident():
         torch.cuda.synchronize()
         assert torch.equal(dw.o, o_res) and torch.equal(dw.lse, l_res), f"staged call {rep}"
     _say("width 3 staged: bit-identical to resident, twice")
+    ek, ev = _enc(w, width)
+    o_ref, lse_ref = _ref(w, width, ek, ev)
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "width 3 staged vs oracle")
 
 
 def test_narrow_checkpoint_round_trip():
@@ -175,6 +178,11 @@ def test_narrow_checkpoint_round_trip():
         akv.check(x.attend())
     torch.cuda.synchronize()
     assert torch.equal(dw.o, dw2.o) and torch.equal(dw.lse, dw2.lse)
+    # the restored context against the oracle over the saved tokens
+    ek, ev = _enc(w, 2)
+    assert_codes(dw2, w2, ek, ev, "width 2 restored")
+    o_ref, lse_ref = _ref(w, 2, ek, ev)
+    assert_attention(dw2.o.cpu().numpy(), dw2.lse.cpu().numpy(), o_ref, lse_ref, "width 2 restored vs oracle")
     img2 = torch.zeros_like(img)
     akv.check(akv.akv_checkpoint_save(dw2.context_desc(), img2.data_ptr(), harness.stream_handle()))
     torch.cuda.synchronize()
