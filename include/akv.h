@@ -307,6 +307,21 @@ typedef struct akv_staging_desc {
  * workspace race. */
 akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
+/* akv_attend_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * hipMalloc): no workspace argument; the partials live in the library's own
+ * device array of AKV_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until
+ * the process ends.  Same validation, kernels and results as
+ * akv_attend_decode (bit for bit); a shape whose workspace
+ * (akv_decode_workspace_bytes) exceeds the array returns AKV_ERR_WORKSPACE.
+ * The call allocates nothing.  Its first call on a GPU looks up that GPU's
+ * array (a HIP symbol query, AKV_ERR_HIP if it fails).  Every call on one GPU
+ * shares that GPU's array, and nothing in it must start at zero (each call
+ * writes every value it reads): calls that overlap in time on one GPU race,
+ * so serialize them (one stream, or events). */
+#define AKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+akv_status akv_attend_decode_noalloc(const akv_attn_desc* desc, void* stream);
+
 /* akv_attend_decode with the compressed tier streamed from pinned host memory
  * (ActiveKV, "Context beyond VRAM", "What I built": host memory owns the
  * history, device memory holds a bounded staging area, and no staged bytes

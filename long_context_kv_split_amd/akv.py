@@ -36,6 +36,7 @@ MIN_SPLIT_TOKENS = 256
 DECODE_TARGET_WORKGROUPS = 512
 MAX_SPLITS = 2048
 MAX_CHUNK = 512
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class ExactTier(ctypes.Structure):
@@ -141,6 +142,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P(AttnDesc), c_void_p, c_size_t, c_void_p]
+    lib.akv_attend_decode_noalloc.restype = ctypes.c_int
+    lib.akv_attend_decode_noalloc.argtypes = [P(AttnDesc), c_void_p]
     lib.akv_split_plan.restype = ctypes.c_int
     lib.akv_split_plan.argtypes = [P(AttnDesc), c_int32, P(c_int32)]
     lib.akv_attend_decode_staged.restype = ctypes.c_int
@@ -195,6 +198,10 @@ def akv_split_plan(desc: AttnDesc, chunk: bool = False) -> dict:
 
 def akv_attend_decode(desc: AttnDesc, ws: int, ws_bytes: int, stream: int = 0) -> int:
     return LIB.akv_attend_decode(ctypes.byref(desc), ws, ws_bytes, stream)
+
+
+def akv_attend_decode_noalloc(desc: AttnDesc, stream: int = 0) -> int:
+    return LIB.akv_attend_decode_noalloc(ctypes.byref(desc), stream)
 
 
 def akv_attend_chunk(desc: AttnDesc, ws: int, ws_bytes: int, stream: int = 0) -> int:

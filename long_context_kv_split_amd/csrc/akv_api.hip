@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "akv_common.h"
@@ -266,6 +267,56 @@ akv_status akv_attend_decode(const akv_attn_desc* desc, void* ws, size_t ws_byte
   if ((s = check_ws(plan, ws, ws_bytes)) != AKV_OK) return s;
   akv::AttnParams p = make_params(desc, plan, ws);
   return hip_status(akv::launch_decode(p, desc->d, static_cast<hipStream_t>(stream)), "akv_attend_decode");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free decode
+// The library's own scratch for akv_attend_decode_noalloc: one array per GPU,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory, so the kernels only ever get the device
+// address that hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) unsigned char scratch[AKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per GPU, once looked up
+
+// The current GPU's scratch address, looked up on its first call there.
+akv_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(AKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(AKV_ERR_UNSUPPORTED, "device %d (at most %d served)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(AKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return AKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+akv_status akv_attend_decode_noalloc(const akv_attn_desc* desc, void* stream) {
+  Plan plan;
+  akv_status s = check_attn(desc, false, &plan);
+  if (s != AKV_OK) return s;
+  if (plan.ws_bytes > AKV_NOALLOC_SCRATCH_BYTES)
+    return fail(AKV_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the library's own holds %zu "
+                "(use akv_attend_decode with a workspace)", plan.ws_bytes, (size_t)AKV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != AKV_OK) return s;
+  akv::AttnParams p = make_params(desc, plan, ws);
+  return hip_status(akv::launch_decode(p, desc->d, static_cast<hipStream_t>(stream)), "akv_attend_decode_noalloc");
 }
 
 // Validation of the staging descriptor, one category at a time (the caller

@@ -43,7 +43,7 @@ def test_abi_version_and_exports():
                           "akv_chunk_workspace_bytes", "akv_attend_decode", "akv_attend_chunk",
                           "akv_split_plan", "akv_lse_merge", "akv_compress_evicted", "akv_append_evict",
                           "akv_checkpoint_bytes", "akv_checkpoint_save", "akv_checkpoint_restore",
-                          "akv_attend_decode_staged"}
+                          "akv_attend_decode_staged", "akv_attend_decode_noalloc"}
     for n in names:
         assert hasattr(akv.LIB, n), n
 
@@ -136,6 +136,25 @@ def test_null_checks_first():
     assert call(good_desc(q=0, Hq=33, d=96)) == akv.AKV_ERR_NULL
     assert call(good_desc(Hq=33, d=96)) == akv.AKV_ERR_SHAPE
     assert call(good_desc(d=96, q=FAKE + 2)) == akv.AKV_ERR_UNSUPPORTED
+
+
+def test_noalloc_validation_and_size_limit():
+    """The allocation-free decode validates like akv_attend_decode, then refuses
+    a shape whose partials exceed the library's fixed scratch (nothing is
+    enqueued, so no GPU is needed)."""
+    f = lambda d: akv.akv_attend_decode_noalloc(d, 0)
+    assert akv.LIB.akv_attend_decode_noalloc(None, None) == akv.AKV_ERR_NULL
+    assert f(good_desc(q=0)) == akv.AKV_ERR_NULL
+    assert f(good_desc(Hq=33)) == akv.AKV_ERR_SHAPE
+    assert f(good_desc(d=96)) == akv.AKV_ERR_UNSUPPORTED
+    assert f(good_desc(q=FAKE + 2)) == akv.AKV_ERR_ALIGN
+    tiers = dict(quant=good_desc().quant, exact=good_desc().exact)
+    tiers["quant"].max_blocks = tiers["quant"].num_blocks = 1024
+    tiers["exact"].max_blocks = tiers["exact"].num_blocks = 32
+    big = good_desc(B=64, **tiers)
+    assert akv.akv_decode_workspace_bytes(big) > akv.NOALLOC_SCRATCH_BYTES
+    assert f(big) == akv.AKV_ERR_WORKSPACE
+    assert "scratch" in akv.akv_last_error()
 
 
 def test_absent_tier_may_be_null():
