@@ -141,6 +141,18 @@ extern "C" {
 #define AKV_SPLIT_TOKENS_QUANT_DEFAULT 1024
 #define AKV_MIN_SPLIT_TOKENS 256
 #define AKV_DECODE_TARGET_WORKGROUPS 512   /* two per compute unit on 256 CUs */
+/* A decode grid whose splits give fewer workgroups than compute units attends
+ * every split with `sub` workgroups (equal runs of whole blocks, each at least
+ * AKV_MIN_SUBSPLIT_BLOCKS blocks; sub the largest of AKV_DECODE_MAX_SUBSPLITS,
+ * ..., 4, 2 with B * Hkv * splits * sub <= AKV_DECODE_TARGET_WORKGROUPS / 2
+ * that divides every present tier's split blocks by AKV_MIN_SUBSPLIT_BLOCKS
+ * runs), because one compute unit streams only part of what HBM delivers.
+ * Their partials are merged in ascending token order inside the call, so a
+ * split stays the unit of the caller's partition; the choice depends on the
+ * shape only.  E.g. 32,768 exact tokens in 16 splits of 2,048 on 4 kv heads:
+ * 4 workgroups of 512 tokens per split. */
+#define AKV_DECODE_MAX_SUBSPLITS 8
+#define AKV_MIN_SUBSPLIT_BLOCKS 4
 /* akv_attend_chunk's default instead: with Tq*G rows per kv head taken in
  * row groups of AKV_CHUNK_ROWS, a tier of max_blocks blocks is cut into
  * want = ceil(AKV_CHUNK_TARGET_WORKGROUPS / (B * Hkv * row groups)) runs of
@@ -259,6 +271,11 @@ size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc);
  * and kv head.  Validates desc like the call itself and returns its status;
  * out (host memory, 4 int32) is written only on AKV_OK. */
 akv_status akv_split_plan(const akv_attn_desc* desc, int32_t chunk, int32_t* out);
+
+/* Workgroups that attend each split of an akv_attend_decode call with `desc`
+ * (1, or the sub-split count of AKV_DECODE_MAX_SUBSPLITS above); 0 if desc is
+ * invalid. */
+int32_t akv_decode_split_workgroups(const akv_attn_desc* desc);
 
 /* One sequence's compressed tier held in pinned host memory (hipHostMalloc):
  * ceil(length / 64) block records in token order (record i holds tokens

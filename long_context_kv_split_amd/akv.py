@@ -36,6 +36,8 @@ MIN_SPLIT_TOKENS = 256
 DECODE_TARGET_WORKGROUPS = 512
 MAX_SPLITS = 2048
 MAX_CHUNK = 512
+DECODE_MAX_SUBSPLITS = 8
+MIN_SUBSPLIT_BLOCKS = 4
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -144,6 +146,8 @@ def _load() -> ctypes.CDLL:
         fn.argtypes = [P(AttnDesc), c_void_p, c_size_t, c_void_p]
     lib.akv_attend_decode_noalloc.restype = ctypes.c_int
     lib.akv_attend_decode_noalloc.argtypes = [P(AttnDesc), c_void_p]
+    lib.akv_decode_split_workgroups.restype = c_int32
+    lib.akv_decode_split_workgroups.argtypes = [P(AttnDesc)]
     lib.akv_split_plan.restype = ctypes.c_int
     lib.akv_split_plan.argtypes = [P(AttnDesc), c_int32, P(c_int32)]
     lib.akv_attend_decode_staged.restype = ctypes.c_int
@@ -169,7 +173,7 @@ LIB = _load()
 def header_functions() -> list:
     """Names of the functions include/akv.h declares."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:akv_status|size_t|int|const char\*)\s+(akv_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:akv_status|size_t|int32_t|int|const char\*)\s+(akv_\w+)\s*\(", text, re.M)))
 
 
 def akv_abi_version() -> int:
@@ -194,6 +198,10 @@ def akv_split_plan(desc: AttnDesc, chunk: bool = False) -> dict:
     check(LIB.akv_split_plan(ctypes.byref(desc), int(bool(chunk)), out))
     return {"split_tokens_quant": out[0], "split_tokens_exact": out[1], "splits_quant": out[2],
             "splits_exact": out[3]}
+
+
+def akv_decode_split_workgroups(desc: AttnDesc) -> int:
+    return LIB.akv_decode_split_workgroups(ctypes.byref(desc))
 
 
 def akv_attend_decode(desc: AttnDesc, ws: int, ws_bytes: int, stream: int = 0) -> int:

@@ -52,7 +52,9 @@ bool width_ok(int code_bits) { return code_bits == 0 || code_bits == 2 || code_b
 int split_tokens(int v, int dflt) { return v ? v : dflt; }
 
 struct Plan {
-  int G, Pe, Pq, Se, Sq;
+  int G, Pe, Pq, Se, Sq;  // workgroup split sizes and counts per tier (what the kernels run)
+  int part_q, part_e;     // the caller-facing split (partition) sizes
+  int sub;                // workgroups per partition (Pq = part_q / sub, Pe = part_e / sub)
   size_t part_rows;  // partial rows = B * Hkv * (Sq+Se) * Tq * G
   size_t qrot_off;   // rotated queries (given rotation only), after the partials
   size_t ws_bytes;
@@ -140,6 +142,28 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   }
   if (Pe > AKV_MAX_SPLIT_TOKENS || Pq > AKV_MAX_SPLIT_TOKENS)
     return fail(AKV_ERR_UNSUPPORTED, "split size above %d tokens", AKV_MAX_SPLIT_TOKENS);
+  const int part_q = Pq, part_e = Pe;
+  // decode grids with fewer workgroups than compute units: each split is
+  // attended by `sub` workgroups of equal runs of whole blocks (a compute
+  // unit streams at most ~40 GB/s, so a partition must span several), and
+  // the merge takes their partials in ascending token order
+  int sub = 1;
+  if (!chunk) {
+    const long long units = (long long)d->B * d->Hkv;
+    const long long wgs = units * (((long long)q.max_blocks * AKV_BLOCK_TOKENS + Pq - 1) / Pq +
+                                   ((long long)e.max_blocks * AKV_BLOCK_TOKENS + Pe - 1) / Pe);
+    for (int c = AKV_DECODE_MAX_SUBSPLITS; c > 1; c >>= 1) {
+      const bool fits = wgs * c <= AKV_DECODE_TARGET_WORKGROUPS / 2 &&
+                        (q.max_blocks == 0 || (Pq / AKV_BLOCK_TOKENS) % (c * AKV_MIN_SUBSPLIT_BLOCKS) == 0) &&
+                        (e.max_blocks == 0 || (Pe / AKV_BLOCK_TOKENS) % (c * AKV_MIN_SUBSPLIT_BLOCKS) == 0);
+      if (fits) {
+        sub = c;
+        break;
+      }
+    }
+    Pq /= sub;
+    Pe /= sub;
+  }
   const long long Se = ((long long)e.max_blocks * AKV_BLOCK_TOKENS + Pe - 1) / Pe;
   const long long Sq = ((long long)q.max_blocks * AKV_BLOCK_TOKENS + Pq - 1) / Pq;
   if (Se + Sq > AKV_MAX_SPLITS)
@@ -159,6 +183,9 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   plan->G = G;
   plan->Pe = Pe;
   plan->Pq = Pq;
+  plan->part_q = part_q;
+  plan->part_e = part_e;
+  plan->sub = sub;
   plan->Se = (int)Se;
   plan->Sq = (int)Sq;
   plan->part_rows = (size_t)d->B * d->Hkv * (size_t)(Se + Sq) * d->Tq * G;
@@ -243,6 +270,11 @@ size_t akv_decode_workspace_bytes(const akv_attn_desc* desc) {
   return check_attn(desc, false, &plan) == AKV_OK ? plan.ws_bytes : 0;
 }
 
+int32_t akv_decode_split_workgroups(const akv_attn_desc* desc) {
+  Plan plan;
+  return check_attn(desc, false, &plan) == AKV_OK ? plan.sub : 0;
+}
+
 size_t akv_chunk_workspace_bytes(const akv_attn_desc* desc) {
   Plan plan;
   return check_attn(desc, true, &plan) == AKV_OK ? plan.ws_bytes : 0;
@@ -253,10 +285,10 @@ akv_status akv_split_plan(const akv_attn_desc* desc, int32_t chunk, int32_t* out
   akv_status s = check_attn(desc, chunk != 0, &plan);
   if (s != AKV_OK) return s;
   if (!out) return fail(AKV_ERR_NULL, "out is NULL");
-  out[0] = plan.Pq;
-  out[1] = plan.Pe;
-  out[2] = plan.Sq;
-  out[3] = plan.Se;
+  out[0] = plan.part_q;
+  out[1] = plan.part_e;
+  out[2] = (plan.Sq + plan.sub - 1) / plan.sub;
+  out[3] = (plan.Se + plan.sub - 1) / plan.sub;
   return AKV_OK;
 }
 

@@ -43,7 +43,8 @@ def test_abi_version_and_exports():
                           "akv_chunk_workspace_bytes", "akv_attend_decode", "akv_attend_chunk",
                           "akv_split_plan", "akv_lse_merge", "akv_compress_evicted", "akv_append_evict",
                           "akv_checkpoint_bytes", "akv_checkpoint_save", "akv_checkpoint_restore",
-                          "akv_attend_decode_staged", "akv_attend_decode_noalloc"}
+                          "akv_attend_decode_staged", "akv_attend_decode_noalloc",
+                          "akv_decode_split_workgroups"}
     for n in names:
         assert hasattr(akv.LIB, n), n
 
@@ -123,6 +124,28 @@ def test_decode_split_planner():
         assert 4 * (p["splits_quant"] + p["splits_exact"]) <= 512
     with pytest.raises(akv.AKVError):
         akv.akv_split_plan(good_desc(d=96))
+
+
+def test_decode_sub_splits_for_small_grids():
+    """A grid with fewer workgroups than compute units attends each split with
+    several workgroups; the caller's partition (the split plan) is unchanged."""
+    ex = _tiers(0, 512)   # 32,768 exact tokens on 4 kv heads
+    d = good_desc(split_tokens_exact=2048, **ex)
+    assert _plan(split_tokens_exact=2048, **ex) == (256, 2048, 0, 16)
+    assert akv.akv_decode_split_workgroups(d) == 4          # 4 x 16 x 4 = 256 workgroups of 512 tokens
+    rows = 4 * 64 * 8
+    assert akv.akv_decode_workspace_bytes(d) == rows * 128 * 4 + rows * 4
+    # 8 splits of 4,096: 8 workgroups each (256 workgroups of 512 tokens)
+    assert akv.akv_decode_split_workgroups(good_desc(split_tokens_exact=4096, **ex)) == 8
+    # the default plans already fill the GPU, and small splits are never cut
+    assert akv.akv_decode_split_workgroups(good_desc()) == 1
+    assert akv.akv_decode_split_workgroups(good_desc(**ex)) == 1
+    tiny = dict(Hq=4, Hkv=1, d=64, split_tokens_quant=384, split_tokens_exact=128, **_tiers(6, 2))
+    assert akv.akv_decode_split_workgroups(good_desc(**tiny)) == 1
+    assert _plan(**tiny) == (384, 128, 1, 1)
+    # a split whose blocks do not cut into equal runs of >= 4 blocks stays whole
+    assert akv.akv_decode_split_workgroups(good_desc(split_tokens_exact=1920, **ex)) == 1
+    assert akv.akv_decode_split_workgroups(good_desc(d=96)) == 0
 
 
 def test_null_checks_first():

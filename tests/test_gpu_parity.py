@@ -273,6 +273,18 @@ def test_exact32k_paged_equals_contiguous(exact32k):
     assert torch.equal(dc.o, o0) and torch.equal(dc.lse, l0)
 
 
+def test_exact32k_sub_splits_are_the_finer_plan(exact32k):
+    """Each of the 16 partitions is attended by 4 workgroups of 512 tokens whose
+    partials are merged in token order: the same bytes as 64 splits of 512."""
+    akv, harness = _mods()
+    w, dw, _, _ = exact32k
+    assert akv.akv_decode_split_workgroups(dw.desc(split_exact=2048)) == 4
+    o0, l0 = dw.o.clone(), dw.lse.clone()
+    akv.check(dw.attend(split_exact=512))
+    torch.cuda.synchronize()
+    assert torch.equal(dw.o, o0) and torch.equal(dw.lse, l0)
+
+
 def test_exact32k_single_split_within_tolerance(exact32k):
     akv, harness = _mods()
     w, dw, o_ref, lse_ref = exact32k
