@@ -1,14 +1,19 @@
 #!/usr/bin/env python3
-"""Benchmark: hybrid two-tier split-KV decode at a 128,000-token history on one MI355X.
+"""Benchmark: two-tier split-KV attention on one MI355X, every configuration.
 
-One step = one akv_attend_decode call (query pre-rotation, fixed split plan,
-exact-tier and compressed-tier split attention, merge with the inverse
-rotation) for batch 1, 32 query heads over 4 kv heads, head dim 128, with
-123,904 compressed (4-bit) + 4,096 exact (bf16) tokens resident in HBM.
+The headline step is one akv_attend_decode call (query pre-rotation, fixed
+split plan, exact-tier and compressed-tier split attention, merge with the
+inverse rotation) for batch 1, 32 query heads over 4 kv heads, head dim 128,
+with 123,904 compressed (4-bit) + 4,096 exact (bf16) tokens resident in HBM.
+The same JSON line carries the other configurations (tiny: one split per
+tier; exact32k: 16 partitions of 2,048 tokens; ragged: 32 sequences; the
+512-query chunk and its eviction), the extra legs (host-staged decode,
+checkpoint, per-step append/evict, QR rotation, 2- and 3-bit codes) and the
+float64 CPU oracle timed on the host's cores for every configuration.
 Inputs rotate through replicas totalling >= 512 MB so the 256 MB Infinity
-Cache cannot hold them.  Prints one JSON line.
+Cache cannot hold them.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--aux]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -83,33 +88,106 @@ def traffic_from_profile(name: str, current_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The float64 oracle (as it stands) on a bounded sample: kv head 0 of 4
-    (query heads 0..7) over the whole history, scaled to one full call."""
-    import numpy as np
-    from oracle import akv_oracle as O
+def cpu_info():
+    """CPU model and the cores this process may run on."""
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
         cores = os.cpu_count() or 1
-    kc, ks = O.encode(w.quant_k_src[0][:, :1])
-    vc, vs = O.encode(w.quant_v_src[0][:, :1])
+    return model, cores
+
+
+def _oracle_jobs(w, seqs, encoded):
+    """One float64 oracle call per (sequence, kv head): dequantize that head's
+    history and attend with its query heads (the oracle as it stands)."""
+    from oracle import akv_oracle as O
     G = w.Hq // w.Hkv
-    q = w.q[0][:, :G]
-    n, t0 = 0, time.perf_counter()
-    while True:
-        O.decode_sequence(q, w.exact_k[0][:, :1], w.exact_v[0][:, :1], kc, ks, vc, vs)
-        n += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    per_head = (time.perf_counter() - t0) / n
-    per_call = per_head * w.Hkv
-    return {"value": w.B / per_call, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"float64 oracle, kv head 0 of {w.Hkv} ({G} query heads) over the full "
-                      f"{int(w.quant_len[0] + w.exact_len[0])}-token history (dequantize + softmax), "
-                      f"{n} repetitions in {per_head * n:.1f} s; per-call time scaled x{w.Hkv}",
-            "seconds_per_call": per_call}
+    jobs = []
+    for b in seqs:
+        (kc, ks), (vc, vs) = encoded[b] if encoded.get(b) else ((None, None), (None, None))
+        for kv in range(w.Hkv):
+            hs = list(range(kv * G, (kv + 1) * G))
+            jobs.append(lambda b=b, kc=kc, ks=ks, vc=vc, vs=vs, hs=hs: O.decode_sequence(
+                w.q[b], w.exact_k[b], w.exact_v[b], kc, ks, vc, vs, causal_tail=w.causal_tail, heads=hs))
+    return jobs
+
+
+def _run_jobs(jobs, threads):
+    """Run the calls on `threads` workers with BLAS at one thread per call;
+    returns the wall time in seconds."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        if threads == 1:
+            for j in jobs:
+                j()
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(lambda j: j(), jobs))
+        return time.perf_counter() - t0
+
+
+def _encode_for_oracle(w, seqs, threads):
+    """The oracle's own encoding of the compressed tier (not timed: the attention
+    call reads codes that already exist, as the GPU call does)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import akv_oracle as O
+    def enc(b):
+        if not w.quant_len[b]:
+            return b, None
+        return b, (O.encode(w.quant_k_src[b]), O.encode(w.quant_v_src[b]))
+    with ThreadPoolExecutor(threads) as ex:
+        return dict(ex.map(enc, seqs))
+
+
+def cpu_baselines(workloads):
+    """The float64 oracle (untuned) on the host's cores, per config, on the same
+    synthetic inputs the GPU timed.  For each config: one timing with a worker
+    per core (each oracle call one (sequence, kv head), BLAS single-threaded)
+    and one single-threaded, the best of 5 when a call is short.  hybrid128k,
+    exact32k, tiny and chunk are timed on the whole call; ragged on a fixed
+    sample of its sequences, scaled by history tokens.  Encoding the
+    compressed tier is not timed (the attention call reads existing codes)."""
+    model, cores = cpu_info()
+    threads = max(1, min(16, cores))
+    out = {}
+    for name, w in workloads.items():
+        B = w.B
+        seqs = list(range(B)) if name != "ragged" else [0, 1, 2, 3]
+        encoded = _encode_for_oracle(w, seqs, threads)
+        jobs = _oracle_jobs(w, seqs, encoded)
+        t_multi = _run_jobs(jobs, threads)
+        t_single = _run_jobs(jobs, 1)
+        if t_single < 0.5:   # short calls: the best of 5
+            t_multi = min([t_multi] + [_run_jobs(jobs, threads) for _ in range(4)])
+            t_single = min([t_single] + [_run_jobs(jobs, 1) for _ in range(4)])
+        hist = float((w.quant_len + w.exact_len).sum())
+        hist_s = float(sum(int(w.quant_len[b] + w.exact_len[b]) for b in seqs))
+        scale = hist / hist_s
+        per_call_multi, per_call_single = t_multi * scale, t_single * scale
+        unit_tokens = B * w.Tq
+        out[name] = {
+            "value": unit_tokens / per_call_multi, "unit": "query tokens/s" if w.Tq > 1 else "tokens/s",
+            "cores": threads, "kind": "oracle",
+            "seconds_per_call": per_call_multi,
+            "single_thread": {"value": unit_tokens / per_call_single, "cores": 1, "seconds_per_call": per_call_single},
+            "sample": (f"float64 oracle, whole call ({B} sequence(s), {w.Hkv} kv heads, {int(hist)} history tokens), "
+                       f"one oracle call per (sequence, kv head) on {threads} worker(s), BLAS 1 thread each"
+                       if seqs == list(range(B)) else
+                       f"float64 oracle on sequences {seqs} of {B} ({int(hist_s)} of {int(hist)} history tokens), "
+                       f"one oracle call per (sequence, kv head), per-call time scaled x{scale:.2f} by history tokens"),
+        }
+        log(f"bench: cpu oracle {name}: {per_call_multi:.3f} s/call on {threads} cores, {per_call_single:.3f} s single")
+    return out, model, threads
 
 
 def bench_decode(name, steps, warmup, stream, min_bytes=2 * MALL_BYTES, w=None, split_quant=None, split_exact=None,
@@ -339,7 +417,8 @@ def bench_chunk(steps, warmup, stream, min_bytes=2 * MALL_BYTES):
     evict_bytes = w.Hkv * w.evict * (2 * 2 * w.d + 2 * (w.d // 2 + 2 * (w.d // 32)))
     flops = chunk_flops(w)
     tflops = flops / (ev_ms * 1e-3) / 1e12
-    return {"workload": "chunk512 over 28,672 compressed + 4,096 exact + 512 chunk tokens, "
+    return {"_workload": w,
+            "workload": "chunk512 over 28,672 compressed + 4,096 exact + 512 chunk tokens, "
                         "Hq 32 / Hkv 4, d 128",
             "us_per_call": ev_ms * 1e3, "wall_us_per_call": wall_ms * 1e3, "steps": steps,
             "query_tokens_per_s": w.B * w.Tq / (ev_ms * 1e-3), "kv_bytes": kv_bytes,
@@ -352,16 +431,42 @@ def bench_chunk(steps, warmup, stream, min_bytes=2 * MALL_BYTES):
                          "algorithmic_flops_per_launch": flops}}
 
 
+def decode_line(name, w, dw, kv_bytes, n_rep, ev_ms, wall_ms, steps):
+    """One decode config's numbers: time per call, KV GB/s against the HBM peak."""
+    from long_context_kv_split_amd import akv
+    gbps = kv_bytes / (ev_ms * 1e-3) / 1e9
+    hist = int((w.quant_len + w.exact_len).sum())
+    return {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "history_tokens": hist,
+            "compressed_tokens": int(w.quant_len.sum()), "exact_tokens": int(w.exact_len.sum()), **dw.plan,
+            "workgroups_per_split": akv.akv_decode_split_workgroups(dw.desc()),
+            "us_per_call": ev_ms * 1e3, "wall_us_per_call": wall_ms * 1e3, "steps": steps,
+            "decode_tokens_per_s": w.B / (ev_ms * 1e-3), "history_tokens_per_s": hist / (ev_ms * 1e-3),
+            "kv_bytes": kv_bytes, "kv_gbps": gbps, "input_replicas": n_rep,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": traffic_from_profile(f"split_decode_{name}_counters.json",
+                                                         source_hash(KERNEL_SOURCES)),
+                         "kernel": "akv_attend_decode (split + merge kernels, one call)",
+                         "algorithmic_bytes_per_launch": kv_bytes}}
+
+
+# The decode configs besides the headline one: (name, split overrides).
+# exact32k runs its 16 partitions of 2,048 tokens; tiny one split per tier.
+OTHER_DECODE = (("tiny", {}), ("exact32k", {"split_exact": 2048}), ("ragged", {}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--aux", action="store_true", help="also time the other workloads")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=("hybrid128k", "tiny", "exact32k", "ragged", "chunk"),
+                    help="time this one workload only (for profiler runs) and print its line")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--no-chunk", action="store_true", help="skip the prefill-chunk line")
+    ap.add_argument("--no-configs", action="store_true", help="skip the tiny, exact32k and ragged lines")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the host-staged, checkpoint and per-step legs (decode and chunk only)")
+                    help="skip the host-staged, checkpoint, per-step, rotation and code-width legs")
     ap.add_argument("--split-quant", type=int, default=0, help="compressed-tier split tokens (0 = library default)")
     ap.add_argument("--split-exact", type=int, default=0, help="exact-tier split tokens (0 = library default)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -376,20 +481,54 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
+
+    def copy_calibration():
+        if args.copy_mb:
+            src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"bench: copied {args.copy_mb} MiB x3 (counter calibration)")
+
+    if args.only:
+        with torch.cuda.stream(stream):
+            if args.only == "chunk":
+                line = bench_chunk(args.steps, args.warmup, stream)
+                line.pop("_workload")
+            else:
+                over = dict(OTHER_DECODE).get(args.only, {})
+                if args.split_exact:
+                    over["split_exact"] = args.split_exact
+                if args.split_quant:
+                    over["split_quant"] = args.split_quant
+                w, dw, kvb, n_rep, ev_ms, wall_ms = bench_decode(args.only, args.steps, args.warmup, stream, **over)
+                line = decode_line(args.only, w, dw, kvb, n_rep, ev_ms, wall_ms, args.steps)
+            copy_calibration()
+        log(f"bench: {args.only} {line['us_per_call']:.2f} us/call")
+        print(json.dumps({"only": args.only, **line}), flush=True)
+        return
+
+    workloads = {}
     with torch.cuda.stream(stream):
         log("bench: building hybrid128k workload")
         w, dw, kv_bytes, n_rep, ev_ms, wall_ms = bench_decode("hybrid128k", args.steps, args.warmup, stream,
                                                               split_quant=args.split_quant or None,
                                                               split_exact=args.split_exact or None)
+        workloads["hybrid128k"] = w
         log(f"bench: hybrid128k {ev_ms * 1e3:.2f} us/call (events), {wall_ms * 1e3:.2f} us/call (wall)")
-        aux = {}
-        if args.aux:
-            for name in ("exact32k", "ragged"):
-                w2, _, b2, r2, e2, wl2 = bench_decode(name, max(50, args.steps // 10), 10, stream)
-                aux[name] = {"us_per_call": e2 * 1e3, "wall_us_per_call": wl2 * 1e3, "kv_bytes": b2,
-                             "kv_gbps": b2 / (e2 * 1e-3) / 1e9, "replicas": r2,
-                             "decode_tokens_per_s": w2.B / (e2 * 1e-3)}
-                log(f"bench: {name} {e2 * 1e3:.2f} us/call")
+        configs = {}
+        if not args.no_configs:
+            for name, over in OTHER_DECODE:
+                log(f"bench: building {name} workload")
+                k = max(200, args.steps) if name != "ragged" else max(50, args.steps)
+                w2, dw2, b2, r2, e2, wl2 = bench_decode(name, k, 10, stream, **over)
+                configs[name] = decode_line(name, w2, dw2, b2, r2, e2, wl2, k)
+                if name == "tiny":
+                    configs[name]["roofline"] = None   # a latency-only case: no roofline claim
+                workloads[name] = w2
+                log(f"bench: {name} {e2 * 1e3:.2f} us/call, {b2 / (e2 * 1e-3) / 1e9:.0f} GB/s")
+                del dw2
         staged = ckpt = step = rot = widths = None
         if not args.no_extra:
             log("bench: host-staged decode")
@@ -414,14 +553,9 @@ def main():
         if not args.no_chunk:
             log("bench: building chunk workload")
             chunk = bench_chunk(max(20, args.steps // 20), 5, stream)
+            workloads["chunk"] = chunk.pop("_workload")
             log(f"bench: chunk {chunk['us_per_call']:.1f} us/call, {chunk['roofline']['achieved']:.1f} TFLOP/s")
-        if args.copy_mb:
-            src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")
-            dst = torch.empty_like(src)
-            for _ in range(3):
-                dst.copy_(src)
-            torch.cuda.synchronize()
-            log(f"bench: copied {args.copy_mb} MiB x3 (counter calibration)")
+        copy_calibration()
     t_s = ev_ms * 1e-3
     gbps = kv_bytes / t_s / 1e9
     hist = int(w.quant_len.sum() + w.exact_len.sum())
@@ -432,9 +566,16 @@ def main():
                 "kernel": "akv_attend_decode (split + merge kernels, one call)",
                 "algorithmic_bytes_per_launch": kv_bytes}
     cpu = None
+    cpu_all = None
     if not args.no_cpu:
-        log("bench: CPU oracle baseline")
-        cpu = cpu_baseline(w)
+        log("bench: CPU oracle baselines")
+        cpu_all, model, threads = cpu_baselines(workloads)
+        cpu = dict(cpu_all["hybrid128k"])
+        cpu["cpu_model"] = model
+        for name, line in configs.items():
+            line["cpu_baseline"] = cpu_all.get(name)
+        if chunk is not None:
+            chunk["cpu_baseline"] = cpu_all.get("chunk")
     out = {
         "metric": METRIC,
         "value": w.B / t_s,
@@ -460,6 +601,10 @@ def main():
         "cpu_baseline": cpu,
         "kernel_source_hash": khash,
     }
+    if configs:
+        out["configs"] = configs
+    if chunk:
+        out["chunk"] = chunk
     if staged:
         out["staged"] = staged
         out["checkpoint"] = ckpt
@@ -467,10 +612,6 @@ def main():
         out["code_widths"] = widths
         out["step"] = {"workload": "akv_append_evict per decode step, Hkv 4, d 128 (B1: window 4096; "
                                "B32: window 2048); one block move per sequence every 64 steps", **step}
-    if chunk:
-        out["chunk"] = chunk
-    if aux:
-        out["aux"] = aux
     print(json.dumps(out), flush=True)
 
 
