@@ -521,8 +521,8 @@ def main():
         if not args.no_configs:
             for name, over in OTHER_DECODE:
                 log(f"bench: building {name} workload")
-                k = max(200, args.steps) if name != "ragged" else max(50, args.steps)
-                w2, dw2, b2, r2, e2, wl2 = bench_decode(name, k, 10, stream, **over)
+                k = max(200, args.steps)
+                w2, dw2, b2, r2, e2, wl2 = bench_decode(name, k, 20, stream, **over)
                 configs[name] = decode_line(name, w2, dw2, b2, r2, e2, wl2, k)
                 if name == "tiny":
                     configs[name]["roofline"] = None   # a latency-only case: no roofline claim
