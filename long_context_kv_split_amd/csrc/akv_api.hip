@@ -245,6 +245,7 @@ akv::AttnParams make_params(const akv_attn_desc* d, const Plan& plan, void* ws) 
   p.part_stride = plan.Sq + plan.Se;
   p.qlen_fixed = -1;
   p.qw = akv::code_width(d->code_bits);
+  p.exact_nt = d->quant.max_blocks == 0;
   p.q_code_stride = (size_t)d->Hkv * 8 * p.qw * d->d;
   p.q_scale_stride = (size_t)d->Hkv * 2 * d->d;
   p.rot = d->rotation;

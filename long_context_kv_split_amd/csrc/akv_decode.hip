@@ -765,8 +765,10 @@ struct EUnit {
 // rows (the query operand uses the same dim order).  V is dim-major inside
 // each half block, so the same lane reads tokens 32c + 8qq .. + 7 of dim
 // 16t + j, 1 KB of consecutive bytes per load instruction.  Both operands
-// come straight from HBM, with no transposition.
-template <int D>
+// come straight from HBM, with no transposition.  NTV: the V loads are
+// non-temporal (each V load instruction reads 1 KB of whole lines; K rows are
+// read in 64-byte pieces by four instructions, so they keep normal loads).
+template <int D, bool NTV>
 __device__ inline void exact_load(EUnit<D>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq, int lane) {
   constexpr int MK = D / 32, NT = D / 16;
   const uint16_t* kslab = p.ek + ((size_t)pb * p.Hkv + kv) * kBlock * D;
@@ -779,8 +781,10 @@ __device__ inline void exact_load(EUnit<D>& u, const AttnParams& p, int pb, int 
     for (int m = 0; m < MK; ++m) u.kx[tp][m] = src[4 * m];
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    u.vx[t] = *reinterpret_cast<const u32x4*>(vslab + (c * D + 16 * t + j) * (kBlock / 2) + 8 * qq);
+  for (int t = 0; t < D / 16; ++t) {
+    const void* src = vslab + (c * D + 16 * t + j) * (kBlock / 2) + 8 * qq;
+    u.vx[t] = NTV ? stream_load<u32x4>(src) : *reinterpret_cast<const u32x4*>(src);
+  }
 }
 
 template <int D, bool PARTIAL>
@@ -824,7 +828,7 @@ __device__ inline void exact_compute(const EUnit<D>& u, int nvalid, const bf16x8
   }
 }
 
-template <int D>
+template <int D, bool NTV>
 __device__ void exact_split(const AttnParams& p, const Lds& L, int b, int kv, int sx, int s) {
   constexpr int MK = D / 32;  // score tiles per token tile
   constexpr int NT = D / 16;
@@ -872,15 +876,15 @@ __device__ void exact_split(const AttnParams& p, const Lds& L, int b, int kv, in
   };
   EUnit<D> ua, ub;
   bool oka, okb;
-  exact_load<D>(ua, p, block_of(0, oka), kv, 0, j, qq, lane);
+  exact_load<D, NTV>(ua, p, block_of(0, oka), kv, 0, j, qq, lane);
   for (int i = 0; i < nblk_w; ++i) {
     const int pb = block_of(i, okb);
-    exact_load<D>(ub, p, pb, kv, 1, j, qq, lane);
+    exact_load<D, NTV>(ub, p, pb, kv, 1, j, qq, lane);
     const int tb = (blk0 + w + kWaves * i) * 64;
     poison |= !oka;
     if (end - tb >= 32) exact_compute<D, false>(ua, 32, Q, p.qscale2, qq, st, O);
     else exact_compute<D, true>(ua, end - tb, Q, p.qscale2, qq, st, O);
-    exact_load<D>(ua, p, block_of(i + 1, oka), kv, 0, j, qq, lane);
+    exact_load<D, NTV>(ua, p, block_of(i + 1, oka), kv, 0, j, qq, lane);
     if (end - tb >= 64) exact_compute<D, false>(ub, 32, Q, p.qscale2, qq, st, O);
     else if (end - tb > 32) exact_compute<D, true>(ub, end - tb - 32, Q, p.qscale2, qq, st, O);
   }
@@ -916,7 +920,18 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(AttnParams p)
   if (sx < p.Sq)
     quant_split<D, W>(p, L, b, kv, p.part_base + sx, sx);
   else
-    exact_split<D>(p, L, b, kv, p.part_base + sx, sx - p.Sq);
+    exact_split<D, false>(p, L, b, kv, p.part_base + sx, sx - p.Sq);
+}
+
+// A call without a compressed tier: exact-tier splits only, with
+// non-temporal V loads (a kernel of its own, so the two-tier kernel's code
+// and registers stay as they are).
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void exact_decode_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  const Lds L = lds_layout(smem);
+  const int sx = blockIdx.x, kv = blockIdx.y, b = p.b0 + blockIdx.z;
+  exact_split<D, true>(p, L, b, kv, p.part_base + sx, sx - p.Sq);
 }
 
 constexpr int kMergeThreads = 512;
@@ -1177,7 +1192,9 @@ hipError_t launch_decode_qrot(const AttnParams& p, int D, hipStream_t stream) {
 
 template <int D>
 static void launch_split_w(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  if (p.qw == 2)
+  if (p.exact_nt)
+    hipLaunchKernelGGL(exact_decode_kernel<D>, grid, dim3(kThreads), 0, stream, p);
+  else if (p.qw == 2)
     hipLaunchKernelGGL((split_decode_kernel<D, 2>), grid, dim3(kThreads), 0, stream, p);
   else if (p.qw == 3)
     hipLaunchKernelGGL((split_decode_kernel<D, 3>), grid, dim3(kThreads), 0, stream, p);

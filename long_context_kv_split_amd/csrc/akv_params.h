@@ -42,6 +42,11 @@ struct AttnParams {
   // qrot: [B][Hq][d] float32 workspace for the queries rotated by R.
   const float* rot;
   int qw;  // compressed-tier code width (2, 3 or 4)
+  // The call has no compressed tier: the split kernel is the exact-only one,
+  // with non-temporal exact-tier V loads (every workgroup streams bf16
+  // blocks; measured faster there, and slower beside compressed-tier
+  // workgroups).
+  int exact_nt;
   float* qrot;
 };
 
