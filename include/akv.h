@@ -434,8 +434,9 @@ typedef struct akv_append_desc {
 
 akv_status akv_append_evict(const akv_append_desc* desc, void* stream);
 
-/* Context checkpoint (ActiveKV, "Context beyond VRAM", "What I built": a long
- * context is suspended and resumed without recomputing it).  The image of a
+/* Context checkpoint (ActiveKV, "Context beyond VRAM", "What I built": a
+ * context can be parked and brought back later without being rebuilt from its
+ * tokens).  The image of a
  * batch is a fixed-size byte string, every field little-endian:
  *   [0, 256)   header: "AKVCTX01" (8 bytes), then int32 B, Hkv, d,
  *              exact_max_blocks, quant_max_blocks, code width w (2, 3

@@ -1,8 +1,8 @@
 // Prefill-chunk attention: Tq causal queries per sequence over the two-tier
 // history, on 16x16x32 matrix-core tiles (ActiveKV, "Context beyond VRAM",
-// "What I built": exact recent tier + compact older tier, merged with exact
-// attention arithmetic; the compact tier is read through the pre-rotated query
-// of the QuantForge walkthrough, section 1).
+// "What I built": a full-precision recent window and an encoded older tier,
+// combined without approximation; the encoded tier is read through the
+// pre-rotated query of the QuantForge walkthrough, section 1).
 //
 // Rows of one kv head are (query, head) pairs r = tau * G + g.  A workgroup
 // (4 waves x 32 rows; two workgroups per CU) takes

@@ -1,9 +1,9 @@
 // Compress evicted exact-tier tokens into the 4-bit tier.
 //
 // For every (token, kv head, K|V) vector of d bf16 values (ActiveKV, "Context
-// beyond VRAM", "What I built": older history held in a compact form; the
-// rotation is the Walsh-Hadamard rotation of the QuantForge walkthrough,
-// section 1):
+// beyond VRAM", "What I built": tokens leaving the recent window are encoded
+// into the small tier; the rotation is the Walsh-Hadamard rotation of the
+// QuantForge walkthrough, section 1):
 //   E1 x = float(bf16)                                   exact
 //   E2 unnormalized Sylvester butterflies, h = 1, 2, ..., d/2 ascending:
 //      (x[i], x[i+h]) <- (x[i] + x[i+h], x[i] - x[i+h])  for i & h == 0

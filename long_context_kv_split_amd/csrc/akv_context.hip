@@ -1,6 +1,6 @@
 // Context checkpoint: a fixed-format image of a batch's two-tier history
-// (ActiveKV, "Context beyond VRAM", "What I built": a long context is
-// suspended and resumed without recomputing it).  The image holds the
+// (ActiveKV, "Context beyond VRAM", "What I built": a context can be parked
+// and brought back later without being rebuilt from its tokens).  The image holds the
 // lengths and, slot by slot in token order, the bytes of every block below
 // each length; restore writes those bytes into whatever pool blocks the
 // caller's tables name.  Pure data movement: one workgroup of 256 threads per

@@ -1,6 +1,7 @@
 // Split-KV decode attention over a two-tier history, and the exact
-// log-sum-exp merge (ActiveKV, "Context beyond VRAM", "What I built": exact and compact tiers merged with exact attention
-// arithmetic; each partial carries the log-sum-exp statistic that "Bringing a
+// log-sum-exp merge (ActiveKV, "Context beyond VRAM", "What I built": a
+// full-precision recent window and an encoded older tier, attended apart and
+// combined without approximation; each partial carries the log-sum-exp statistic that "Bringing a
 // serving stack up on new silicon", "What I built", adds to the
 // paged-attention path).
 //

@@ -9,11 +9,11 @@ What it computes (plain definitions, float64 unless a step fixes another
 precision):
 
 * attention over a two-tier history (ActiveKV, "Context beyond VRAM",
-  section "What I built": recent tokens exact BF16, older history in a compact
-  form, the two merged with exact attention arithmetic).  The oracle does not
+  section "What I built": recent tokens kept in bf16, older ones encoded, both
+  attended through one exact softmax).  The oracle does not
   split or merge at all: it takes one softmax over the whole dequantized
   history, which is what an exact merge of per-tier partials equals;
-* the compact form: a normalized Walsh-Hadamard rotation (QuantForge
+* the encoded form: a normalized Walsh-Hadamard rotation (QuantForge
   walkthrough, section 1 "Triton Fused Kernels": a Hadamard rotation keeps dot
   products, so the query can be rotated instead of the compressed blocks),
   32-element group RMS scales stored as fp16 and 4-bit indices into the
@@ -21,7 +21,7 @@ precision):
   bit for bit, the encoder emulates the float32 operation sequence of the
   encode steps E1-E9 exactly (each numpy float32 operation is one IEEE
   round-to-nearest-even operation, with no fused multiply-add);
-* the same compact form at 2 and 3 bits (``width``): the 4- and 8-level
+* the same encoded form at 2 and 3 bits (``width``): the 4- and 8-level
   Lloyd-Max tables for N(0,1) in place of the 16-level one, every other step
   unchanged;
 * the log-sum-exp merge of normalized partials (the attention statistic added
