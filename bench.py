@@ -482,6 +482,29 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
 
+    def device_copy_gbps(mib=1024, reps=10):
+        """A plain device-to-device copy of `mib` MiB on the bench stream:
+        (read + write) bytes per second, median of `reps` event-timed copies
+        (the measured second denominator next to the vendor HBM peak)."""
+        src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        times = []
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+            for _ in range(reps):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                dst.copy_(src)
+                b.record(stream)
+                b.synchronize()
+                times.append(a.elapsed_time(b) * 1e-3)
+        t = sorted(times)[len(times) // 2]
+        del src, dst
+        return {"gbps": 2 * (mib << 20) / t / 1e9, "bytes_moved": 2 * (mib << 20),
+                "method": f"torch device-to-device copy of {mib} MiB, (read + write) bytes / median time of {reps}"}
+
     def copy_calibration():
         if args.copy_mb:
             src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")
@@ -556,6 +579,8 @@ def main():
             workloads["chunk"] = chunk.pop("_workload")
             log(f"bench: chunk {chunk['us_per_call']:.1f} us/call, {chunk['roofline']['achieved']:.1f} TFLOP/s")
         copy_calibration()
+    copy_meas = device_copy_gbps()
+    log(f"bench: device copy {copy_meas['gbps']:.0f} GB/s (read + write)")
     t_s = ev_ms * 1e-3
     gbps = kv_bytes / t_s / 1e9
     hist = int(w.quant_len.sum() + w.exact_len.sum())
@@ -595,6 +620,8 @@ def main():
                    "input_replicas": n_rep, "replica_bytes": kv_bytes * n_rep},
         "kv_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "device_copy": copy_meas,
+        "frac_of_device_copy": gbps / copy_meas["gbps"],
         "history_tokens_per_s": hist / t_s,
         "wall_ms_per_step": wall_ms,
         "roofline": roofline,
