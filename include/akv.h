@@ -162,6 +162,9 @@ extern "C" {
 #define AKV_MAX_SPLIT_TOKENS 32768   /* largest split size served */
 #define AKV_MAX_SPLITS 2048          /* largest (compressed + exact) splits per sequence */
 #define AKV_MAX_CHUNK 512
+/* Also AKV_ERR_UNSUPPORTED: B or Hkv above 65535, Tq * Hq above 2^30, and any
+ * shape whose partials (B * Hkv * splits * Tq * G rows of d + 1 floats) would
+ * need more than 2^50 workspace bytes. */
 
 typedef enum akv_status {
   AKV_OK = 0,

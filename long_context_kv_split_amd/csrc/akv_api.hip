@@ -170,6 +170,13 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
     return fail(AKV_ERR_UNSUPPORTED, "%lld splits per sequence (max %d): use larger splits", Se + Sq,
                 AKV_MAX_SPLITS);
   if ((long long)d->Tq * d->Hq > (1LL << 30)) return fail(AKV_ERR_UNSUPPORTED, "Tq * Hq too large");
+  {
+    // the partials' workspace, B * Hkv * splits * Tq * G rows of d + 1 floats,
+    // must stay far below the size_t range
+    const double rows = (double)d->B * d->Hkv * (double)(Se + Sq) * d->Tq * G;
+    if (rows * (d->d + 1) * 4.0 > (double)(1ULL << 50))
+      return fail(AKV_ERR_UNSUPPORTED, "%.3g partial rows need more than 2^50 workspace bytes", rows);
+  }
   // ---- ALIGN
   if (!aligned(d->q, 16)) return fail(AKV_ERR_ALIGN, "q must be 16-byte aligned");
   if (!aligned(d->rotation, 16)) return fail(AKV_ERR_ALIGN, "rotation must be 16-byte aligned");

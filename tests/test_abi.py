@@ -209,6 +209,11 @@ def test_unsupported():
     assert call(good_desc(Tq=2)) == akv.AKV_ERR_UNSUPPORTED          # decode is one query
     assert call(good_desc(Tq=513), chunk=True) == akv.AKV_ERR_UNSUPPORTED
     assert call(good_desc(Tq=4, exact=akv.ExactTier()), chunk=True) == akv.AKV_ERR_UNSUPPORTED
+    # workspace sizes that would approach the size_t range are refused, not wrapped
+    huge = good_desc(B=65535, Hkv=65535, Hq=8 * 65535)
+    assert call(huge) == akv.AKV_ERR_UNSUPPORTED
+    assert akv.akv_decode_workspace_bytes(huge) == 0
+    assert call(good_desc(B=65535, Hkv=8000, Hq=8 * 8000, Tq=512), chunk=True) == akv.AKV_ERR_UNSUPPORTED
 
 
 def test_alignment():
