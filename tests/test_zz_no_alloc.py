@@ -50,3 +50,39 @@ def test_noalloc_decode_equals_workspace_decode_twice():
         assert torch.equal(dw.o, o_ws) and torch.equal(dw.lse, l_ws), f"{w.name}: differs from akv_attend_decode"
         o_ref, lse_ref, _, _ = oracle_case(w)
         assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, f"noalloc {w.name} vs oracle")
+
+
+def test_noalloc_decode_in_a_captured_graph():
+    """The entry point's purpose: a decode that a HIP graph can capture.  The
+    first call on the device (the array's address lookup) runs eagerly, one
+    call is captured, and every replay, with eager decodes and
+    synchronizations between the replays, must equal the workspace decode."""
+    akv, harness = _mods()
+    w = synth.make_small("noalloc_graph", B=2, Hq=32, Hkv=4, d=128, quant=[3000, 700], exact=[300, 64])
+    _say(f"noalloc graph: B={w.B} quant={list(w.quant_len)} exact={list(w.exact_len)}")
+    dw = harness.DeviceWorkload(w)
+    akv.check(dw.attend())
+    torch.cuda.synchronize()
+    o_ref, l_ref = dw.o.clone(), dw.lse.clone()
+    desc = dw.desc()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        akv.check(akv.akv_attend_decode_noalloc(desc, side.cuda_stream))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = akv.akv_attend_decode_noalloc(desc, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, akv.akv_last_error()
+    for r in range(4):
+        dw.o.fill_(float("nan"))
+        dw.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.o, o_ref) and torch.equal(dw.lse, l_ref), f"replay {r} differs from the workspace decode"
+        akv.check(dw.attend())  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(dw.o, o_ref) and torch.equal(dw.lse, l_ref)
+    _say("noalloc graph: 4 replays equal to the workspace decode")
