@@ -64,9 +64,11 @@ __device__ inline float half_bits(uint32_t h) { return (float)__builtin_bit_cast
 // optimizer.  An fp16 hi + lo split must convert hi, and subtract it, from
 // one fp32 value: left to itself the backend folds (_Float16)(a * b) into a
 // single-rounding mixed multiply for some uses only, so on fp16 ties hi and
-// the hi that lo was taken from differ by one ulp.
+// the hi that lo was taken from differ by one ulp.  The empty asm is not
+// volatile: it hides the value without ordering the conversions of one
+// staged block against each other.
 __device__ inline float fp32_pinned(float x) {
-  asm volatile("" : "+v"(x));
+  asm("" : "+v"(x));
   return x;
 }
 
