@@ -197,6 +197,15 @@ template <int D>
 __device__ inline void quant_stage_k(const QRegs<D>& r, unsigned char* smem, unsigned char* buf, int nvalid) {
   constexpr int M = D / 32;
   const float2* klut = reinterpret_cast<const float2*>(smem + ChunkLds<D>::KLUT);
+  // every table read of this thread's share first, so they are in flight
+  // together, then the products and conversions
+  float2 lvs[kVT][QRegs<D>::KDW][4];
+#pragma unroll
+  for (int u = 0; u < kVT; ++u)
+#pragma unroll
+    for (int k = 0; k < QRegs<D>::KDW; ++k)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) lvs[u][k][b] = klut[(r.kc[u][k] >> (8 * b)) & 0xFFu];
 #pragma unroll
   for (int u = 0; u < kVT; ++u)
 #pragma unroll
@@ -207,7 +216,7 @@ __device__ inline void quant_stage_k(const QRegs<D>& r, unsigned char* smem, uns
     half8 hi, lo;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float2 lv = klut[(r.kc[u][k] >> (8 * b)) & 0xFFu];
+      const float2 lv = lvs[u][k][b];
       const float v0 = fp32_pinned(lv.x * s), v1 = fp32_pinned(lv.y * s);
       hi[2 * b] = (_Float16)v0;
       hi[2 * b + 1] = (_Float16)v1;
@@ -228,7 +237,7 @@ __device__ inline void quant_stage_v(const QRegs<D>& r, unsigned char* smem, uns
   for (int u = 0; u < kVT; ++u) {
     const int v = threadIdx.x + kCThreads * u, i = v & 15, tq = (v >> 4) & 3, ca = v >> 6, tok0 = 8 * ca;
     u32x4 sc = r.vs[u];
-    if (tok0 + 8 > nvalid) {
+    if (nvalid < 64 && tok0 + 8 > nvalid) {  // nvalid is the block's: only its last block masks
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (tok0 + 2 * b >= nvalid) sc[b] = 0u;
