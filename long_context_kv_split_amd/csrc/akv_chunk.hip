@@ -418,17 +418,18 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
   const int* table = QUANT ? p.qtab + (size_t)b * p.qmax : p.etab + (size_t)b * p.emax;
   const int nbpool = QUANT ? p.qnb : p.enb;
   bool poison = false;
-  auto block_id = [&](int n) {
-    const int pb = table[(start >> 6) + n];
+  // pool block of raw table entry pb (a bad id poisons the split and reads block 0)
+  auto checked = [&](int pb) {
     const bool ok = pb >= 0 && pb < nbpool;
     poison |= !ok;
     return ok ? pb : 0;
   };
-  auto fetch = [&](Regs& r, int n) {
+  auto raw_id = [&](int n) { return n < nb ? table[(start >> 6) + n] : 0; };
+  auto fetch = [&](Regs& r, int pb) {
     if constexpr (QUANT)
-      quant_fetch<D>(r, p, block_id(n), kv);
+      quant_fetch<D>(r, p, checked(pb), kv);
     else
-      exact_fetch<D>(r, p, block_id(n), kv);
+      exact_fetch<D>(r, p, checked(pb), kv);
   };
 
   // ---- byte tables (compressed tier)
@@ -525,7 +526,10 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
   auto nvalid_of = [&](int n) { return min(64, end - (start + 64 * n)); };
   const int causal_from = el - p.Tq;  // blocks reaching past this token need the causal mask
   Regs regs;
-  if (nb > 0) fetch(regs, 0);
+  // block ids are read one block ahead of their fetch, so a fetch does not
+  // wait for its table entry
+  if (nb > 0) fetch(regs, raw_id(0));
+  int id_next = raw_id(1);
   __syncthreads();  // byte tables visible
   for (int n = 0; n < nb; ++n) {
     if (n) __syncthreads();  // every wave is done with the previous block
@@ -537,7 +541,11 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
       exact_stage_v<D>(regs, buf, nvalid_of(n));
     }
     __syncthreads();
-    if (n + 1 < nb) fetch(regs, n + 1);  // in flight while this block is computed
+    if (n + 1 < nb) {  // in flight while this block is computed
+      const int id2 = raw_id(n + 2);
+      fetch(regs, id_next);
+      id_next = id2;
+    }
     const int tb = start + 64 * n;
     const bool mask = (tb + 64 > end) || (!QUANT && tb + 63 > causal_from);
     compute_half<D, QUANT>(buf, 0, mask, tb, end, climit, Qh, Ql, Qe, p.qscale2, rs);
