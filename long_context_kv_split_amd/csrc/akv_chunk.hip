@@ -212,16 +212,17 @@ __device__ inline void quant_stage_k(const QRegs<D>& r, unsigned char* smem, uns
   for (int k = 0; k < QRegs<D>::KDW; ++k) {
     const int v = threadIdx.x + kCThreads * u, tok = v >> 3;
     const int wi = qk_dword<D>(v, k), m = wi % M, a = wi / M;
-    const float s = tok < nvalid ? half_bits(r.ks[u][k] & 0xFFFFu) : 0.0f;
+    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(tok < nvalid ? r.ks[u][k] & 0xFFFFu : 0u));
     half8 hi, lo;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const float2 lv = lvs[u][k][b];
-      const float v0 = fp32_pinned(lv.x * s), v1 = fp32_pinned(lv.y * s);
-      hi[2 * b] = (_Float16)v0;
-      hi[2 * b + 1] = (_Float16)v1;
-      lo[2 * b] = (_Float16)(v0 - (float)hi[2 * b]);
-      lo[2 * b + 1] = (_Float16)(v1 - (float)hi[2 * b + 1]);
+      // hi = fp16(c s) and lo = fp16(c s - hi), each one rounding of an exact
+      // fused product (mixed-precision FMAs)
+      hi[2 * b] = (_Float16)__builtin_fmaf(lv.x, s, 0.0f);
+      hi[2 * b + 1] = (_Float16)__builtin_fmaf(lv.y, s, 0.0f);
+      lo[2 * b] = (_Float16)__builtin_fmaf(lv.x, s, -(float)hi[2 * b]);
+      lo[2 * b + 1] = (_Float16)__builtin_fmaf(lv.y, s, -(float)hi[2 * b + 1]);
     }
     const int off = kchunk_off<D>(tok, 4 * m + a);
     *reinterpret_cast<half8*>(buf + off) = hi;
@@ -296,9 +297,19 @@ __device__ inline void exact_stage_v(const ERegs<D>& r, unsigned char* buf, int 
 }
 
 // ---------------------------------------------------------------- compute
+// Online softmax in base 2 against a reference m per row: l and O hold sums
+// of 2^(s - m), and moving m rescales them; the log-sum-exp m + log2 l and
+// O / l do not depend on where m sits.  The compressed tier moves m up to the
+// row maximum only when a score exceeds it by more than kLazyShift (an fp16
+// probability is then at most 2^8).  The exact tier's probabilities are
+// rounded to bf16 (8 significant bits) before the product with V while l sums
+// them unrounded, so it moves m whenever a score exceeds it: the row
+// maximum's probability stays exactly 1 and the dominant term is not rounded.
+constexpr float kLazyShift = 8.0f;
+
 template <int D>
 struct RowState {
-  float m[kRT], l[kRT];
+  float m[kRT], l[kRT];  // m = -inf until the row has seen a score
   float4v O[D / 16][kRT];
 };
 
@@ -310,6 +321,10 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
                                     const bf16x8 (&Qe)[kRT][D / 32], float qs, RowState<D>& rs) {
   constexpr int M = D / 32, NT = D / 16;
   const int lane = threadIdx.x & 63, j = lane & 15, qq = lane >> 4;
+  // scores relative to the reference: s - base, base = m (0 before any score)
+  float base[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) base[rt] = rs.m[rt] == neg_inf() ? 0.0f : rs.m[rt];
   // scores: row i of tile tp is token 32c + 8(i/4) + 4tp + i%4, so lane
   // (j, qq) ends up with tokens 32c + 8qq + 0..7 of row j
   float s[kRT][8];
@@ -331,7 +346,10 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
     }
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      float4v acc = float4v{0, 0, 0, 0};
+      // the compressed tier's query carries the score scale, so the tile
+      // starts from -base; the exact tier scales afterwards
+      const float a0 = QUANT ? -base[rt] : 0.0f;
+      float4v acc = float4v{a0, a0, a0, a0};
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         if (QUANT) {
@@ -343,7 +361,7 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[rt][4 * tp + r] = QUANT ? acc[r] : acc[r] * qs;
+      for (int r = 0; r < 4; ++r) s[rt][4 * tp + r] = QUANT ? acc[r] : __builtin_fmaf(acc[r], qs, -base[rt]);
     }
   }
   if (mask) {
@@ -355,35 +373,56 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
         if (tok >= end || tok > climit[rt]) s[rt][e] = neg_inf();
       }
   }
-  // online softmax (base 2); lanes j, j+16, j+32, j+48 share a row
-  half8 ph[kRT];
-  bf16x8 pbf[kRT];
+  // online softmax; lanes j, j+16, j+32, j+48 share a row.  The reference
+  // moves (for the whole wave at once) when a row has no reference yet or a
+  // score exceeds it by more than the tier's allowance; a NaN score also
+  // takes that path and ends as a NaN output.
+  constexpr float lazy = QUANT ? kLazyShift : 0.0f;
+  bool move = false;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     float mx = s[rt][0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[rt][e]);
-    mx = fmaxf(mx, cxor16(mx));
-    mx = fmaxf(mx, cxor32(mx));
-    const float mnew = fmaxf(rs.m[rt], mx);
-    const float muse = (mnew == neg_inf()) ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(rs.m[rt] - muse);
+    move |= !(mx <= lazy) || rs.m[rt] == neg_inf();
+  }
+  if (__ballot(move)) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      float mx = s[rt][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[rt][e]);
+      mx = fmaxf(mx, cxor16(mx));
+      mx = fmaxf(mx, cxor32(mx));
+      // shift d of the reference: to the row maximum, never down once set
+      const bool fresh = rs.m[rt] == neg_inf();
+      const float d = fresh ? (mx == neg_inf() ? 0.0f : mx) : fmaxf(mx, 0.0f);
+      if (!(fresh && mx == neg_inf())) rs.m[rt] = base[rt] + d;
+      const float alpha = fresh ? 1.0f : __builtin_amdgcn_exp2f(-d);  // O and l are 0 while fresh
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[rt][e] -= d;
+      rs.l[rt] *= alpha;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) rs.O[t][rt] *= alpha;
+      }
+    }
+  }
+  half8 ph[kRT];
+  bf16x8 pbf[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
     float sum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(s[rt][e] - muse);
+      const float pe = __builtin_amdgcn_exp2f(s[rt][e]);
       sum += pe;
       if (QUANT)
         ph[rt][e] = (_Float16)pe;
       else
         pbf[rt][e] = (__bf16)pe;
     }
-    rs.l[rt] = rs.l[rt] * alpha + sum;
-    rs.m[rt] = mnew;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) rs.O[t][rt] *= alpha;
-    }
+    rs.l[rt] += sum;
   }
   // values: lane (j, qq) supplies V^T[16t + j][32c + 8qq + 0..7]
 #pragma unroll
