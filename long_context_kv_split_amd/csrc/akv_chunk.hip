@@ -364,6 +364,12 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
       for (int r = 0; r < 4; ++r) s[rt][4 * tp + r] = QUANT ? acc[r] : __builtin_fmaf(acc[r], qs, -base[rt]);
     }
   }
+  // value operands: lane (j, qq) supplies V^T[16t + j][32c + 8qq + 0..7];
+  // read before the softmax, which does not need them, so the reads are in
+  // flight while it runs
+  u32x4 va[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) va[t] = *reinterpret_cast<const u32x4*>(buf + vchunk_off<D>(16 * t + j, 4 * c + qq));
   if (mask) {
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
@@ -424,16 +430,14 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
     }
     rs.l[rt] += sum;
   }
-  // values: lane (j, qq) supplies V^T[16t + j][32c + 8qq + 0..7]
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const u32x4 va = *reinterpret_cast<const u32x4*>(buf + vchunk_off<D>(16 * t + j, 4 * c + qq));
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       if (QUANT)
-        rs.O[t][rt] = cmfma16(__builtin_bit_cast(half8, va), ph[rt], rs.O[t][rt]);
+        rs.O[t][rt] = cmfma16(__builtin_bit_cast(half8, va[t]), ph[rt], rs.O[t][rt]);
       else
-        rs.O[t][rt] = cmfma16bf(__builtin_bit_cast(bf16x8, va), pbf[rt], rs.O[t][rt]);
+        rs.O[t][rt] = cmfma16bf(__builtin_bit_cast(bf16x8, va[t]), pbf[rt], rs.O[t][rt]);
     }
   }
 }
