@@ -328,22 +328,27 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
   // scores: row i of tile tp is token 32c + 8(i/4) + 4tp + i%4, so lane
   // (j, qq) ends up with tokens 32c + 8qq + 0..7 of row j
   float s[kRT][8];
+  // key operands of both 16-token tiles read up front, so the second tile's
+  // reads are in flight while the first tile's products run
+  half8 kh[2][M], kl[2][M];
+  bf16x8 kb[2][M];
 #pragma unroll
   for (int tp = 0; tp < 2; ++tp) {
     const int krow = 32 * c + 8 * (j >> 2) + 4 * tp + (j & 3);
-    half8 kh[M], kl[M];
-    bf16x8 kb[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const int off = kchunk_off<D>(krow, 4 * m + qq);
       const u32x4 raw = *reinterpret_cast<const u32x4*>(buf + off);
       if (QUANT) {
-        kh[m] = __builtin_bit_cast(half8, raw);
-        kl[m] = *reinterpret_cast<const half8*>(buf + ChunkLds<D>::KLO + off);
+        kh[tp][m] = __builtin_bit_cast(half8, raw);
+        kl[tp][m] = *reinterpret_cast<const half8*>(buf + ChunkLds<D>::KLO + off);
       } else {
-        kb[m] = __builtin_bit_cast(bf16x8, raw);
+        kb[tp][m] = __builtin_bit_cast(bf16x8, raw);
       }
     }
+  }
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       // the compressed tier's query carries the score scale, so the tile
@@ -353,11 +358,11 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         if (QUANT) {
-          acc = cmfma16(kh[m], Qh[rt][m], acc);
-          acc = cmfma16(kh[m], Ql[rt][m], acc);
-          acc = cmfma16(kl[m], Qh[rt][m], acc);
+          acc = cmfma16(kh[tp][m], Qh[rt][m], acc);
+          acc = cmfma16(kh[tp][m], Ql[rt][m], acc);
+          acc = cmfma16(kl[tp][m], Qh[rt][m], acc);
         } else {
-          acc = cmfma16bf(kb[m], Qe[rt][m], acc);
+          acc = cmfma16bf(kb[tp][m], Qe[rt][m], acc);
         }
       }
 #pragma unroll
