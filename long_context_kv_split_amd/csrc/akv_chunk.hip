@@ -668,42 +668,80 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p) {
   const int nq = (ql + p.Pq - 1) / p.Pq, ne = (el + p.Pe - 1) / p.Pe;
   const size_t S = (size_t)p.Sq + p.Se;
   const size_t base = ((size_t)(b * p.Hkv + kv) * S) * R + tau * G + g;
+  const size_t firstq = base, firste = base + (size_t)p.Sq * R;
+  // Splits are taken kMU at a time, ascending, with every load of a group
+  // (and the first group of both tiers) issued before any is used: one
+  // memory round trip covers up to kMU splits per tier.  A group's largest
+  // log-sum-exp rescales the running sums when it raises their reference; a
+  // split with no scores (-inf) or a NaN is selected out, never multiplied
+  // by zero.
+  constexpr int kMU = 4;
+  struct Tier {
+    float m = neg_inf(), wsum = 0.0f, acc[E] = {};
+    bool nan = false;
+  } tr[2];
+  // splits past the tier's last are read at a clamped, existing row (every
+  // call has at least one split row) and masked, so no load is conditional
+  auto load = [&](size_t first, int n, int s0, float (&l)[kMU], float (&x)[kMU][E]) {
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) {
+      const bool in = s0 + u < n;
+      const size_t r = first + (size_t)min(s0 + u, max(n - 1, 0)) * R;
+      const float lv = p.part_lse[r];
+      l[u] = in ? lv : neg_inf();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xv = p.part_o[r * D + lane + 64 * e];
+        x[u][e] = in ? xv : 0.0f;
+      }
+    }
+  };
+  auto fold = [&](Tier& t, const float (&l)[kMU], const float (&x)[kMU][E]) {
+    float mc = neg_inf();
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) {
+      t.nan |= l[u] != l[u];
+      mc = fmaxf(mc, l[u]);
+    }
+    if (mc > t.m) {
+      const float f = (t.m == neg_inf()) ? 0.0f : __expf(t.m - mc);
+      t.wsum *= f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) t.acc[e] *= f;
+      t.m = mc;
+    }
+    if (t.m == neg_inf()) return;
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) {
+      const bool ok = l[u] > neg_inf();
+      const float wt = __expf(l[u] - t.m);
+      t.wsum += ok ? wt : 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) t.acc[e] += ok ? wt * x[u][e] : 0.0f;
+    }
+  };
+  {
+    float lq[kMU], xq[kMU][E], le[kMU], xe[kMU][E];
+    load(firstq, nq, 0, lq, xq);
+    load(firste, ne, 0, le, xe);
+    fold(tr[0], lq, xq);
+    fold(tr[1], le, xe);
+    for (int s0 = kMU; s0 < nq; s0 += kMU) {
+      load(firstq, nq, s0, lq, xq);
+      fold(tr[0], lq, xq);
+    }
+    for (int s0 = kMU; s0 < ne; s0 += kMU) {
+      load(firste, ne, s0, le, xe);
+      fold(tr[1], le, xe);
+    }
+  }
   float res_o[2][E], res_l[2];
 #pragma unroll
   for (int tier = 0; tier < 2; ++tier) {
-    const int n = tier ? ne : nq;
-    const size_t first = base + (tier ? (size_t)p.Sq * R : 0);
-    float m = neg_inf(), wsum = 0.0f;
-    float acc[E];
-    bool nan = false;
+    const Tier& t = tr[tier];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-    for (int s = 0; s < n; ++s) {
-      const size_t r = first + (size_t)s * R;
-      const float l = p.part_lse[r];
-      float x[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = p.part_o[r * D + lane + 64 * e];
-      if (l != l) {
-        nan = true;
-        continue;
-      }
-      if (l == neg_inf()) continue;
-      if (l > m) {
-        const float f = (m == neg_inf()) ? 0.0f : __expf(m - l);
-        wsum *= f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] *= f;
-        m = l;
-      }
-      const float wt = __expf(l - m);
-      wsum += wt;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += wt * x[e];
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) res_o[tier][e] = (m == neg_inf()) ? 0.0f : acc[e] / wsum;
-    res_l[tier] = nan ? __builtin_nanf("") : (m == neg_inf() ? neg_inf() : m + __logf(wsum));
+    for (int e = 0; e < E; ++e) res_o[tier][e] = (t.m == neg_inf()) ? 0.0f : t.acc[e] / t.wsum;
+    res_l[tier] = t.nan ? __builtin_nanf("") : (t.m == neg_inf() ? neg_inf() : t.m + __logf(t.wsum));
   }
   // inverse rotation of the compressed-tier output: dim = lane + 64e
 #pragma unroll
