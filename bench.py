@@ -36,6 +36,8 @@ MALL_BYTES = 256 << 20
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["long_context_kv_split_amd/csrc/akv_decode.hip", "long_context_kv_split_amd/csrc/akv_common.h",
                   "long_context_kv_split_amd/csrc/akv_params.h"]
+CHUNK_SOURCES = ["long_context_kv_split_amd/csrc/akv_chunk.hip", "long_context_kv_split_amd/csrc/akv_common.h",
+                 "long_context_kv_split_amd/csrc/akv_params.h"]
 
 
 def source_hash(paths) -> str:
@@ -426,7 +428,8 @@ def bench_chunk(steps, warmup, stream, min_bytes=2 * MALL_BYTES):
             "evict": {"tokens_per_kv_head": w.evict, "us_per_call": ev_c * 1e3, "wall_us_per_call": wall_c * 1e3,
                       "bytes": evict_bytes, "gbps": evict_bytes / (ev_c * 1e-3) / 1e9},
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS["f16"],
-                         "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None,
+                         "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"],
+                         "traffic": traffic_from_profile("chunk512_counters.json", source_hash(CHUNK_SOURCES)),
                          "kernel": "akv_attend_chunk (split + merge kernels, one call)",
                          "algorithmic_flops_per_launch": flops}}
 
