@@ -131,16 +131,22 @@ extern "C" {
  * budget = AKV_DECODE_TARGET_WORKGROUPS / (B * Hkv) splits per kv head and
  * tier capacities Nq = 64 * quant.max_blocks, Ne = 64 * exact.max_blocks
  * tokens, the compressed tier takes the smallest Pq in 256, 512, 768 with
- * ceil(Nq / Pq) + ceil(Ne / AKV_SPLIT_TOKENS_EXACT_DEFAULT) <= budget (else
- * AKV_SPLIT_TOKENS_QUANT_DEFAULT); with rem = budget - ceil(Nq / Pq) >= 1 the
+ * ceil(Nq / Pq) + ceil(Ne / AKV_SPLIT_TOKENS_EXACT_DEFAULT) <= budget; when
+ * none fits (no single round), Pq = ceil(Nq * B * Hkv /
+ * AKV_DECODE_MANY_WORKGROUPS) rounded up to a multiple of 256, at least
+ * AKV_SPLIT_TOKENS_QUANT_DEFAULT and at most AKV_MAX_SPLIT_TOKENS (a few
+ * rounds of longer workgroups).  With rem = budget - ceil(Nq / Pq) >= 1 the
  * exact tier takes Pe = 64 * ceil(exact.max_blocks / rem) clamped to
  * [AKV_MIN_SPLIT_TOKENS, AKV_SPLIT_TOKENS_EXACT_DEFAULT], else the default.
  * E.g. 1 sequence, 4 kv heads, 123,904 + 4,096 tokens: Pq = 1024 (121
- * splits), Pe = 640 (7 splits), 512 workgroups. */
+ * splits), Pe = 640 (7 splits), 512 workgroups; 32 sequences on 4 kv heads
+ * with tables of 880 compressed + 32 exact blocks: Pq = 3584 (16 splits),
+ * Pe = 1024 (2 splits). */
 #define AKV_SPLIT_TOKENS_EXACT_DEFAULT 1024
 #define AKV_SPLIT_TOKENS_QUANT_DEFAULT 1024
 #define AKV_MIN_SPLIT_TOKENS 256
 #define AKV_DECODE_TARGET_WORKGROUPS 512   /* two per compute unit on 256 CUs */
+#define AKV_DECODE_MANY_WORKGROUPS 2048    /* about four rounds */
 /* A decode grid whose splits give fewer workgroups than compute units attends
  * every split with `sub` workgroups (equal runs of whole blocks, each at least
  * AKV_MIN_SUBSPLIT_BLOCKS blocks; sub the largest of AKV_DECODE_MAX_SUBSPLITS,

@@ -112,12 +112,21 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
     const long long nq = (long long)q.max_blocks * AKV_BLOCK_TOKENS;
     const long long ne = (long long)e.max_blocks * AKV_BLOCK_TOKENS;
     const long long se_max = (ne + AKV_SPLIT_TOKENS_EXACT_DEFAULT - 1) / AKV_SPLIT_TOKENS_EXACT_DEFAULT;
-    int pq = AKV_SPLIT_TOKENS_QUANT_DEFAULT;
+    int pq = 0;
     for (int c = AKV_MIN_SPLIT_TOKENS; c < AKV_SPLIT_TOKENS_QUANT_DEFAULT; c += 4 * AKV_BLOCK_TOKENS)
       if ((nq + c - 1) / c + se_max <= budget) {
         pq = c;
         break;
       }
+    if (pq == 0) {
+      // no single round: compressed splits sized for about
+      // AKV_DECODE_MANY_WORKGROUPS workgroups (a few rounds), so that every
+      // workgroup's start-up is spread over more blocks; never below the default
+      const long long want = (nq * units + AKV_DECODE_MANY_WORKGROUPS - 1) / AKV_DECODE_MANY_WORKGROUPS;
+      const long long step = 4 * AKV_BLOCK_TOKENS;
+      pq = (int)std::min<long long>(AKV_MAX_SPLIT_TOKENS,
+                                    std::max<long long>(AKV_SPLIT_TOKENS_QUANT_DEFAULT, (want + step - 1) / step * step));
+    }
     Pq = split_tokens(d->split_tokens_quant, pq);
     const long long rem = budget - (nq + Pq - 1) / Pq;
     int pe = AKV_SPLIT_TOKENS_EXACT_DEFAULT;

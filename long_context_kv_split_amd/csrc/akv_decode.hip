@@ -911,11 +911,18 @@ __device__ inline void merge_two(float oa, float la, float ob, float lb, float& 
   lse = M + __logf(W);
 }
 
+// The split a workgroup takes (see split_rotate).
+__device__ inline int split_of_workgroup(const AttnParams& p) {
+  if (!p.split_rotate) return blockIdx.x;
+  const int S = p.Sq + p.Se, unit = blockIdx.y + p.Hkv * blockIdx.z;
+  return ((int)blockIdx.x + S - unit % S) % S;
+}
+
 template <int D, int W>
 __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   const Lds L = lds_layout(smem);
-  const int sx = blockIdx.x, kv = blockIdx.y, b = p.b0 + blockIdx.z;
+  const int sx = split_of_workgroup(p), kv = blockIdx.y, b = p.b0 + blockIdx.z;
   // the split reads its tier's length itself, in the same round trip as its
   // block ids and query
   if (sx < p.Sq)
@@ -931,7 +938,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void exact_decode_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   const Lds L = lds_layout(smem);
-  const int sx = blockIdx.x, kv = blockIdx.y, b = p.b0 + blockIdx.z;
+  const int sx = split_of_workgroup(p), kv = blockIdx.y, b = p.b0 + blockIdx.z;
   exact_split<D, true>(p, L, b, kv, p.part_base + sx, sx - p.Sq);
 }
 
@@ -1203,7 +1210,16 @@ static void launch_split_w(const AttnParams& p, dim3 grid, hipStream_t stream) {
     hipLaunchKernelGGL((split_decode_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p);
 }
 
-hipError_t launch_decode(const AttnParams& p, int D, hipStream_t stream) {
+// Workgroups are handed to the 8 XCDs round-robin in linear id order, and a
+// unit's (sequence, kv head) splits have consecutive ids: with an even split
+// count in a batch of sequences every unit would start on the same XCDs,
+// which then take all the low-index splits (the ones the short sequences of
+// a ragged batch still have) while others idle.  There each unit's splits
+// are rotated by its index (a bijection, so no workgroup is added).  A
+// single sequence keeps the plain order: its units are alike.
+hipError_t launch_decode(const AttnParams& p0, int D, hipStream_t stream) {
+  AttnParams p = p0;
+  p.split_rotate = p.B > 1 && ((p.Sq + p.Se) & 1) == 0;
   dim3 grid(p.Sq + p.Se, p.Hkv, p.B);
   dim3 mgrid(p.Hq, p.B);
   hipError_t e = launch_decode_qrot(p, D, stream);

@@ -48,6 +48,11 @@ struct AttnParams {
   // workgroups).
   int exact_nt;
   float* qrot;
+  // Decode split kernel: nonzero = the workgroup in column x of unit u
+  // (= y + Hkv z) takes split (x - u) mod (Sq + Se) (set for batches of
+  // sequences with an even split count, so that units start on different
+  // XCDs); 0 = split x.
+  int split_rotate;
 };
 
 }  // namespace akv

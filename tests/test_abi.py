@@ -103,13 +103,21 @@ def _tiers(qblocks, eblocks):
 
 
 def test_decode_split_planner():
-    """One round of <= 512 workgroups when the shape allows it, else 1024-token splits."""
+    """One round of <= 512 workgroups when the shape allows it, else compressed
+    splits sized for about 2,048 workgroups (at least 1,024 tokens)."""
     # 1 sequence x 4 kv heads, 123,904 + 4,096 tokens: 4 * (121 + 7) = 512 workgroups
     assert _plan() == (1024, 640, 121, 7)
     # exact tier only, 32,768 tokens: 128 splits of 256 tokens per kv head
     assert _plan(**_tiers(0, 512)) == (256, 256, 0, 128)
-    # 32 sequences (ragged batch, tables of 1,024 + 32 blocks): no room, the defaults
-    assert _plan(B=32, **_tiers(1024, 32)) == (1024, 1024, 64, 2)
+    # 32 sequences (tables of 1,024 + 32 blocks): no single round; compressed
+    # splits for about 2,048 workgroups, ceil(65,536 * 128 / 2,048) = 4,096
+    # tokens (16 splits), the exact tier at its default
+    assert _plan(B=32, **_tiers(1024, 32)) == (4096, 1024, 16, 2)
+    # the ragged batch's tables (880 + 32 blocks): 56,320 * 128 / 2,048 = 3,520 -> 3,584
+    assert _plan(B=32, **_tiers(880, 32)) == (3584, 1024, 16, 2)
+    # never below the 1,024-token default: 8 sequences of 16,384 compressed tokens
+    # (512 / 32 = 16 slots per kv head, 768-token splits need 22)
+    assert _plan(B=8, **_tiers(256, 32)) == (1024, 1024, 16, 2)
     # 4 query heads on 1 kv head, 384 + 128 tokens: the smallest splits
     assert _plan(Hq=4, Hkv=1, d=64, **_tiers(6, 2)) == (256, 256, 2, 1)
     # a 28,672 + 4,608-token history: 256-token compressed splits leave 16 slots
@@ -174,7 +182,7 @@ def test_noalloc_validation_and_size_limit():
     tiers = dict(quant=good_desc().quant, exact=good_desc().exact)
     tiers["quant"].max_blocks = tiers["quant"].num_blocks = 1024
     tiers["exact"].max_blocks = tiers["exact"].num_blocks = 32
-    big = good_desc(B=64, **tiers)
+    big = good_desc(B=64, split_tokens_quant=1024, **tiers)  # 64 * 4 * (64 + 2) * 8 partial rows
     assert akv.akv_decode_workspace_bytes(big) > akv.NOALLOC_SCRATCH_BYTES
     assert f(big) == akv.AKV_ERR_WORKSPACE
     assert "scratch" in akv.akv_last_error()
@@ -210,7 +218,7 @@ def test_unsupported():
     assert call(good_desc(Tq=513), chunk=True) == akv.AKV_ERR_UNSUPPORTED
     assert call(good_desc(Tq=4, exact=akv.ExactTier()), chunk=True) == akv.AKV_ERR_UNSUPPORTED
     # workspace sizes that would approach the size_t range are refused, not wrapped
-    huge = good_desc(B=65535, Hkv=65535, Hq=8 * 65535)
+    huge = good_desc(B=65535, Hkv=65535, Hq=8 * 65535, split_tokens_quant=1024)  # 2^32 * 125 * 8 rows
     assert call(huge) == akv.AKV_ERR_UNSUPPORTED
     assert akv.akv_decode_workspace_bytes(huge) == 0
     assert call(good_desc(B=65535, Hkv=8000, Hq=8 * 8000, Tq=512), chunk=True) == akv.AKV_ERR_UNSUPPORTED
