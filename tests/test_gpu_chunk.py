@@ -64,6 +64,20 @@ def test_chunk_small(cfg):
     assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, f"chunk {cfg} {kw}")
 
 
+def test_chunk_peaked_scores():
+    """Queries scaled by 16 (exact in bfloat16): scores spread over tens of
+    units, so a split's running maximum keeps rising well past the compressed
+    tier's 2^8 allowance and the softmax reference moves (rescaling O and l)
+    many times per split, while each row's weight sits on a few tokens."""
+    w = synth.make_small("chunk_peaked", B=1, Hq=32, Hkv=4, d=128, quant=[1500], exact=[400], Tq=64,
+                         causal_tail=64)
+    w.q = synth.f64_to_bf16_bits(synth.bf16_bits_to_f32(w.q).astype(np.float64) * 16.0)
+    dw = run_chunk(w)
+    o_ref, lse_ref, ek, ev = oracle_case(w)
+    assert np.max(lse_ref) - np.min(lse_ref) > 20.0  # the scale really spreads the scores
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "chunk, queries x16")
+
+
 def test_chunk_deterministic_and_paged_equals_contiguous():
     akv, harness = _mods()
     w = synth.make_small("chunk_det", B=1, Hq=32, Hkv=4, d=128, quant=[1200], exact=[400], Tq=100,

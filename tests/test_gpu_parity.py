@@ -226,6 +226,19 @@ def test_decode_small(cfg):
     assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, f"small {cfg}")
 
 
+def test_decode_peaked_scores():
+    """Queries scaled by 16 (exact in bfloat16): scores spread over tens of
+    units, so each split's running maximum keeps rising and the online softmax
+    rescales its sums many times, while each row's weight sits on a few
+    tokens; two sequences of different lengths."""
+    w = synth.make_small("peaked", B=2, Hq=32, Hkv=4, d=128, quant=[3000, 900], exact=[300, 130])
+    w.q = synth.f64_to_bf16_bits(synth.bf16_bits_to_f32(w.q).astype(np.float64) * 16.0)
+    dw = run_case(w)
+    o_ref, lse_ref, _, _ = oracle_case(w)
+    assert np.max(lse_ref) - np.min(lse_ref) > 20.0  # the scale really spreads the scores
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "decode, queries x16")
+
+
 def test_tiny_two_splits():
     """The tiny config: one split per tier (384 compressed, 128 exact tokens),
     merged by log-sum-exp."""
