@@ -49,6 +49,10 @@ CASES = [
     dict(B=1, Hq=32, Hkv=4, d=128, quant=[2000], exact=[600], Tq=64, outlier_frac=0.01),
     # one query: the chunk degenerates to decode over the whole history
     dict(B=1, Hq=32, Hkv=4, d=128, quant=[1500], exact=[100], Tq=1),
+    # one query head per kv head: 50 rows per kv head, a single ragged row group
+    dict(B=1, Hq=4, Hkv=4, d=128, quant=[600], exact=[200], Tq=50),
+    # two query heads per kv head, d 64
+    dict(B=1, Hq=8, Hkv=4, d=64, quant=[500], exact=[100], Tq=20, split_quant=128),
 ]
 
 

@@ -216,6 +216,10 @@ def test_compress_odd_destination_start(d, width):
          outlier_frac=0.01),
     dict(B=2, Hq=4, Hkv=1, d=64, quant=[383, 64], exact=[129, 0], split_exact=64, split_quant=128),
     dict(B=1, Hq=12, Hkv=2, d=128, quant=[777], exact=[65], split_exact=64, split_quant=192),
+    # one query head per kv head (15 of the 16 matrix columns are padding), ragged pair
+    dict(B=2, Hq=4, Hkv=4, d=128, quant=[700, 300], exact=[200, 65], split_exact=0, split_quant=0),
+    # two query heads per kv head, d 64
+    dict(B=1, Hq=8, Hkv=4, d=64, quant=[900], exact=[130], split_exact=64, split_quant=256),
 ])
 def test_decode_small(cfg):
     w = synth.make_small("small", **cfg)
