@@ -220,6 +220,9 @@ def test_compress_odd_destination_start(d, width):
     dict(B=2, Hq=4, Hkv=4, d=128, quant=[700, 300], exact=[200, 65], split_exact=0, split_quant=0),
     # two query heads per kv head, d 64
     dict(B=1, Hq=8, Hkv=4, d=64, quant=[900], exact=[130], split_exact=64, split_quant=256),
+    # three sequences with 4 + 2 = 6 splits each (an even count in a batch: each
+    # unit's splits are rotated over the XCDs), one with no compressed tier
+    dict(B=3, Hq=8, Hkv=2, d=128, quant=[1000, 300, 0], exact=[256, 64, 130], split_exact=128, split_quant=256),
 ])
 def test_decode_small(cfg):
     w = synth.make_small("small", **cfg)
