@@ -625,9 +625,11 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
 }
 
 // grid (Hkv * nrg, Sq + Se, B): the long compressed-tier splits come first in
-// dispatch order, the shorter exact-tier splits fill in behind them.
+// dispatch order, the shorter exact-tier splits fill in behind them.  At
+// d = 64 three workgroups share a compute unit (168 VGPRs, a few spilled,
+// and 27 KB of LDS each), at d = 128 two.
 template <int D>
-__global__ __launch_bounds__(kCThreads, 2) void chunk_split_kernel(AttnParams p, int nrg) {
+__global__ __launch_bounds__(kCThreads, D == 64 ? 3 : 2) void chunk_split_kernel(AttnParams p, int nrg) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[ChunkLds<D>::BYTES];
   const int kv = blockIdx.x / nrg, rg = blockIdx.x - kv * nrg, sx = blockIdx.y, b = blockIdx.z;
   const int ql = p.qmax ? p.qlen[b] : 0;
