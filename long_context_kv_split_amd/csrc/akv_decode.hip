@@ -1013,24 +1013,48 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   // (2)
   if (w < 2) {
     const int s0 = w ? Sq : 0, n = w ? ne : nq;
-    float m = neg_inf(), nan = 0.0f;
-    for (int i = lane; i < n; i += 64) {
-      const float l = wsh[s0 + i];
-      if (l != l) nan = 1.0f;
-      else m = fmaxf(m, l);
+    float m = neg_inf(), nan = 0.0f, sum = 0.0f;
+    if (n <= 128) {
+      // up to two splits per lane, held in registers between the passes
+      // (the same operations in the same order as the general loops below)
+      const float l0 = lane < n ? wsh[s0 + lane] : neg_inf();
+      const float l1 = lane + 64 < n ? wsh[s0 + lane + 64] : neg_inf();
+      if (lane < n) {
+        if (l0 != l0) nan = 1.0f;
+        else m = fmaxf(m, l0);
+      }
+      if (lane + 64 < n) {
+        if (l1 != l1) nan = 1.0f;
+        else m = fmaxf(m, l1);
+      }
+      m = wave_max(m);
+      nan = wave_max(nan);
+      const float e0 = (m == neg_inf() || l0 != l0) ? 0.0f : __expf(l0 - m);
+      const float e1 = (m == neg_inf() || l1 != l1) ? 0.0f : __expf(l1 - m);
+      if (lane < n) sum += e0;
+      if (lane + 64 < n) sum += e1;
+      sum = wave_sum(sum);
+      const float r = sum > 0.0f ? 1.0f / sum : 0.0f;
+      if (lane < n) wsh[s0 + lane] = e0 * r;
+      if (lane + 64 < n) wsh[s0 + lane + 64] = e1 * r;
+    } else {
+      for (int i = lane; i < n; i += 64) {
+        const float l = wsh[s0 + i];
+        if (l != l) nan = 1.0f;
+        else m = fmaxf(m, l);
+      }
+      m = wave_max(m);
+      nan = wave_max(nan);
+      for (int i = lane; i < n; i += 64) {
+        const float l = wsh[s0 + i];
+        const float e = (m == neg_inf() || l != l) ? 0.0f : __expf(l - m);
+        wsh[s0 + i] = e;
+        sum += e;
+      }
+      sum = wave_sum(sum);
+      const float r = sum > 0.0f ? 1.0f / sum : 0.0f;
+      for (int i = lane; i < n; i += 64) wsh[s0 + i] *= r;
     }
-    m = wave_max(m);
-    nan = wave_max(nan);
-    float sum = 0.0f;
-    for (int i = lane; i < n; i += 64) {
-      const float l = wsh[s0 + i];
-      const float e = (m == neg_inf() || l != l) ? 0.0f : __expf(l - m);
-      wsh[s0 + i] = e;
-      sum += e;
-    }
-    sum = wave_sum(sum);
-    const float r = sum > 0.0f ? 1.0f / sum : 0.0f;
-    for (int i = lane; i < n; i += 64) wsh[s0 + i] *= r;
     if (lane == 0) {
       stats[w][0] = (m == neg_inf()) ? neg_inf() : m + __logf(sum);
       stats[w][1] = (bad || nan != 0.0f) ? 1.0f : 0.0f;
@@ -1047,11 +1071,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
         xo[k] = *reinterpret_cast<const float4v*>(p.part_o + (base + (s < S ? s : 0)) * D + 4 * c4);
       }
     }
+    // every weight read first (a clamped, existing slot for splits past S),
+    // then the sums in the same order with selects instead of branches
+    float wv[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int s = s0 + ph + k * PH;
-      if (s < nq) aq += wsh[s] * xo[k];
-      else if (s >= Sq && s - Sq < ne) ae += wsh[s] * xo[k];
+      wv[k] = wsh[s < S ? s : 0];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int s = s0 + ph + k * PH;
+      const bool inq = s < nq, ine = !inq && s >= Sq && s - Sq < ne;
+      const float4v t = wv[k] * xo[k];
+      aq = inq ? aq + t : aq;
+      ae = ine ? ae + t : ae;
     }
   }
   phase[0][ph * C4 + c4] = aq;
