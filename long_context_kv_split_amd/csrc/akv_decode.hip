@@ -1159,6 +1159,155 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   }
 }
 
+// The merge for calls with at most 128 splits per sequence and the Walsh-
+// Hadamard rotation: one workgroup of 4 waves per (query head, sequence),
+// one barrier.  Every wave reads all the splits' lse values (lane l: splits
+// l and l + 64) and forms both tiers' weights w_s = exp(lse_s - M) / W
+// itself, with the same operations in the same order in every wave, so no
+// wave waits for another before its weighted sums; wave v sums w_s o_s over
+// splits v, v + 4, ... in ascending order, lane l holding dims E l ..
+// E l + E - 1 of every split row (one coalesced row per load), each split's
+// weight broadcast from the lane that holds it.  Wave 0 then adds the four
+// waves' sums in wave order, inverse-rotates the compressed-tier output
+// (once per head) and merges the two tiers.  KS = splits per wave (the call's
+// split count rounded up); rows past the last split are read at row 0 and
+// never used, and inactive splits are skipped, never multiplied.
+constexpr int kFastMergeWaves = 4;
+constexpr int kFastMergeSplits = 128;
+
+template <int D, int KS>
+__global__ __launch_bounds__(64 * kFastMergeWaves) void merge_fast_kernel(AttnParams p) {
+  constexpr int E = D / 64;
+  static_assert(KS * kFastMergeWaves <= kFastMergeSplits, "lse values are held two per lane");
+  __shared__ __attribute__((aligned(16))) float part[kFastMergeWaves][2][D];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.G, kv = h / G, g = h - kv * G;
+  const int Sq = p.Sq, S = p.Sq + p.Se;
+  const size_t base = part_row(p, b, kv, g, 0);
+  // every request first: lengths, all lse values, this wave's split rows
+  const int ql = p.qmax ? p.qlen[b] : 0;
+  const int el = p.emax ? p.elen[b] : 0;
+  const float l0 = p.part_lse[base + (lane < S ? lane : 0)];
+  const float l1 = p.part_lse[base + (lane + 64 < S ? lane + 64 : 0)];
+  float xo[KS][E];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int s = w + kFastMergeWaves * k;
+    const float* src = p.part_o + (base + (s < S ? s : 0)) * D + E * lane;
+    if constexpr (E == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(src);
+      xo[k][0] = v.x;
+      xo[k][1] = v.y;
+    } else {
+      xo[k][0] = *src;
+    }
+  }
+  const bool bad = ql < 0 || ql > 64 * p.qmax || el < 0 || el > 64 * p.emax;
+  const int nq = __builtin_amdgcn_readfirstlane(bad ? 0 : (ql + p.Pq - 1) / p.Pq);
+  const int ne = __builtin_amdgcn_readfirstlane(bad ? 0 : (el + p.Pe - 1) / p.Pe);
+  // tier weights, in every wave
+  const bool q0 = lane < nq, q1 = lane + 64 < nq;
+  const bool e0 = lane >= Sq && lane - Sq < ne, e1 = lane + 64 >= Sq && lane + 64 - Sq < ne;
+  const bool f0 = l0 == l0, f1 = l1 == l1;
+  const bool nanq = __ballot((q0 && !f0) || (q1 && !f1)) != 0;
+  const bool nane = __ballot((e0 && !f0) || (e1 && !f1)) != 0;
+  float mq = fmaxf((q0 && f0) ? l0 : neg_inf(), (q1 && f1) ? l1 : neg_inf());
+  float me = fmaxf((e0 && f0) ? l0 : neg_inf(), (e1 && f1) ? l1 : neg_inf());
+  mq = wave_max(mq);
+  me = wave_max(me);
+  const float x0 = (q0 && f0 && mq != neg_inf()) ? __expf(l0 - mq) : 0.0f;
+  const float x1 = (q1 && f1 && mq != neg_inf()) ? __expf(l1 - mq) : 0.0f;
+  const float y0 = (e0 && f0 && me != neg_inf()) ? __expf(l0 - me) : 0.0f;
+  const float y1 = (e1 && f1 && me != neg_inf()) ? __expf(l1 - me) : 0.0f;
+  const float Wq = wave_sum(x0 + x1), We = wave_sum(y0 + y1);
+  const float rq = Wq > 0.0f ? 1.0f / Wq : 0.0f, re = We > 0.0f ? 1.0f / We : 0.0f;
+  // each split's weight in its own tier (0 for inactive splits, never used)
+  const float wt0 = q0 ? x0 * rq : y0 * re;
+  const float wt1 = q1 ? x1 * rq : y1 * re;
+  float aq[E], ae[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) aq[e] = ae[e] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int s = w + kFastMergeWaves * k;  // wave-uniform; s < 64 exactly when k < 16
+    const float ws = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, k < 64 / kFastMergeWaves ? wt0 : wt1), s & 63));
+    if (s < nq) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) aq[e] = fmaf(ws, xo[k][e], aq[e]);
+    } else if (s >= Sq && s - Sq < ne) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) ae[e] = fmaf(ws, xo[k][e], ae[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    part[w][0][E * lane + e] = aq[e];
+    part[w][1][E * lane + e] = ae[e];
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float oq[E], oe[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float vq = part[0][0][E * lane + e], ve = part[0][1][E * lane + e];
+#pragma unroll
+    for (int v = 1; v < kFastMergeWaves; ++v) {
+      vq += part[v][0][E * lane + e];
+      ve += part[v][1][E * lane + e];
+    }
+    oq[e] = vq;
+    oe[e] = ve;
+  }
+  // inverse rotation (H o_rot) * RN(1/sqrt d): dim E l + e, bit 0 in the
+  // lane when E = 2, the other bits across lanes
+  if constexpr (E == 2) {
+    const float a = oq[0], c = oq[1];
+    oq[0] = a + c;
+    oq[1] = a - c;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    oq[e] = lane_butterfly<1>(oq[e], lane);
+    oq[e] = lane_butterfly<2>(oq[e], lane);
+    oq[e] = lane_butterfly<4>(oq[e], lane);
+    oq[e] = lane_butterfly<8>(oq[e], lane);
+    oq[e] = lane_butterfly<16>(oq[e], lane);
+    oq[e] = lane_butterfly<32>(oq[e], lane);
+  }
+  const float rd = inv_sqrt_d(D);
+  const float lq = (bad || nanq) ? __builtin_nanf("") : (mq == neg_inf() ? neg_inf() : mq + __logf(Wq));
+  const float le = (bad || nane) ? __builtin_nanf("") : (me == neg_inf() ? neg_inf() : me + __logf(We));
+  float* out = p.o + ((size_t)b * p.Hq + h) * D + E * lane;
+  float o[E], lse = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) merge_two(oq[e] * rd, lq, oe[e], le, o[e], lse);
+  if constexpr (E == 2)
+    *reinterpret_cast<float2*>(out) = float2{o[0], o[1]};
+  else
+    out[0] = o[0];
+  if (lane == 0) p.lse[(size_t)b * p.Hq + h] = lse;
+}
+
+// The merge of a decode call: the 4-wave merge where it applies, else the
+// general one (more than 128 splits, or a caller-given rotation).
+template <int D>
+void launch_merge_d(const AttnParams& p, hipStream_t stream) {
+  const dim3 mgrid(p.Hq, p.B), fthreads(64 * kFastMergeWaves);
+  const int S = p.Sq + p.Se;
+  if (p.rot || S > kFastMergeSplits)
+    hipLaunchKernelGGL(merge_kernel<D>, mgrid, dim3(kMergeThreads), 0, stream, p);
+  else if (S <= 4 * kFastMergeWaves)
+    hipLaunchKernelGGL((merge_fast_kernel<D, 4>), mgrid, fthreads, 0, stream, p);
+  else if (S <= 8 * kFastMergeWaves)
+    hipLaunchKernelGGL((merge_fast_kernel<D, 8>), mgrid, fthreads, 0, stream, p);
+  else if (S <= 16 * kFastMergeWaves)
+    hipLaunchKernelGGL((merge_fast_kernel<D, 16>), mgrid, fthreads, 0, stream, p);
+  else
+    hipLaunchKernelGGL((merge_fast_kernel<D, 32>), mgrid, fthreads, 0, stream, p);
+}
+
 // --------------------------------------------------------------- standalone merge
 // Ascending-order merge of n partials of one row (akv_lse_merge).
 __device__ inline void merge_run(const float* po, const float* pl, size_t first, size_t stride, int n, int D,
@@ -1255,15 +1404,14 @@ hipError_t launch_decode(const AttnParams& p0, int D, hipStream_t stream) {
   AttnParams p = p0;
   p.split_rotate = p.B > 1 && ((p.Sq + p.Se) & 1) == 0;
   dim3 grid(p.Sq + p.Se, p.Hkv, p.B);
-  dim3 mgrid(p.Hq, p.B);
   hipError_t e = launch_decode_qrot(p, D, stream);
   if (e != hipSuccess) return e;
   if (D == 64) {
     launch_split_w<64>(p, grid, stream);
-    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);
+    launch_merge_d<64>(p, stream);
   } else {
     launch_split_w<128>(p, grid, stream);
-    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
+    launch_merge_d<128>(p, stream);
   }
   return hipGetLastError();
 }
@@ -1280,11 +1428,10 @@ hipError_t launch_decode_splits(const AttnParams& p, int D, int splits, int seqs
 }
 
 hipError_t launch_decode_merge(const AttnParams& p, int D, hipStream_t stream) {
-  dim3 mgrid(p.Hq, p.B);
   if (D == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, p);
+    launch_merge_d<64>(p, stream);
   else
-    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, p);
+    launch_merge_d<128>(p, stream);
   return hipGetLastError();
 }
 

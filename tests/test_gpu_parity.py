@@ -223,6 +223,11 @@ def test_compress_odd_destination_start(d, width):
     # three sequences with 4 + 2 = 6 splits each (an even count in a batch: each
     # unit's splits are rotated over the XCDs), one with no compressed tier
     dict(B=3, Hq=8, Hkv=2, d=128, quant=[1000, 300, 0], exact=[256, 64, 130], split_exact=128, split_quant=256),
+    # 125 + 3 = 128 splits (the most the 4-wave merge takes; the exact tier's
+    # splits sit past lane 63), the short sequence leaving most of them inactive
+    dict(B=2, Hq=8, Hkv=2, d=128, quant=[8000, 100], exact=[190, 64], split_exact=64, split_quant=64),
+    # 141 + 16 = 157 splits: the general merge
+    dict(B=2, Hq=4, Hkv=1, d=64, quant=[9000, 0], exact=[1000, 70], split_exact=64, split_quant=64),
 ])
 def test_decode_small(cfg):
     w = synth.make_small("small", **cfg)
