@@ -24,9 +24,10 @@ precision):
 * the same encoded form at 2 and 3 bits (``width``): the 4- and 8-level
   Lloyd-Max tables for N(0,1) in place of the 16-level one, every other step
   unchanged;
-* the log-sum-exp merge of normalized partials (the attention statistic added
-  to the paged-attention path, "Bringing a serving stack up on new silicon",
-  section "What I built"), for the standalone merge entry point.
+* the log-sum-exp merge of normalized partials (each partial carries the
+  per-row log-sum-exp that "Bringing a serving stack up on new silicon",
+  section "What I built", makes paged attention return so that partials can
+  be combined), for the standalone merge entry point.
 
 The decoded history is formed in *unrotated* space with the explicit matrix
 H/sqrt(d) (not a fast transform), so the oracle's attention is ordinary
