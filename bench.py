@@ -405,6 +405,30 @@ def bench_widths(w, ev4_ms, stream, steps=500, warmup=20):
     return out
 
 
+def bench_chunk_rotation(w, ev_hadamard_ms, stream, steps=40, warmup=5, min_bytes=2 * MALL_BYTES):
+    """The 512-query chunk with the compressed tier under a QR rotation: the
+    queries rotated by R once per call, each (query, head) output by R^T."""
+    from long_context_kv_split_amd import akv, harness, synth
+    R = synth.qr_rotation(w.d, seed=0)
+    dw = harness.DeviceWorkload(w, rotation=R)
+    n_rep = max(1, -(-min_bytes // w.kv_bytes()))
+    dw.add_replicas(n_rep)
+    descs = [dw.desc(r) for r in range(n_rep)]
+    dw.ensure_ws(descs[0], chunk=True)
+    h = stream.cuda_stream
+    ws, wsb = harness.ptr(dw.ws), dw.ws_bytes
+
+    def call(r):
+        st = akv.akv_attend_chunk(descs[r], ws, wsb, h)
+        if st:
+            akv.check(st)
+
+    ev_ms, _ = time_calls(call, n_rep, warmup, steps, stream, AUX_WARM_MS)
+    del dw
+    return {"chunk_us_per_call": ev_ms * 1e3, "chunk_us_per_call_hadamard": ev_hadamard_ms * 1e3,
+            "chunk_tflops": chunk_flops(w) / (ev_ms * 1e-3) / 1e12}
+
+
 def chunk_flops(w) -> float:
     """QK^T + PV multiply-adds x 2 of one chunk call: every query sees the whole
     history before the chunk plus, causally, (Tq + 1) / 2 chunk tokens on average."""
@@ -609,6 +633,11 @@ def main():
             chunk = bench_chunk(max(20, args.steps // 20), 5, stream)
             workloads["chunk"] = chunk.pop("_workload")
             log(f"bench: chunk {chunk['us_per_call']:.1f} us/call, {chunk['roofline']['achieved']:.1f} TFLOP/s")
+            if rot is not None:
+                rc = bench_chunk_rotation(workloads["chunk"], chunk["us_per_call"] * 1e-3, stream)
+                rot.update(rc)
+                rot["workload"] += "; the 512-query chunk with a QR rotation"
+                log(f"bench: QR chunk {rc['chunk_us_per_call']:.1f} us/call (Hadamard {chunk['us_per_call']:.1f})")
         copy_calibration()
     copy_meas = device_copy_gbps()
     log(f"bench: device copy {copy_meas['gbps']:.0f} GB/s (read + write)")

@@ -77,11 +77,11 @@
  * normalized Walsh-Hadamard rotation above.  Otherwise it is a device
  * pointer to a float32 [d][d] row-major orthogonal matrix R, 16-byte
  * aligned: the encoder stores codes of y = R x (y_i summed in ascending k,
- * one float32 multiply and add per term, no 1/sqrt(d) step), decode rotates
- * each query by R once per call (workspace grows by 4*B*Hq*d bytes) and the
- * compressed-tier output by R^T once per head, and the unrotated vector is
- * R^T times the rotated one.  The same R must be used to encode and to
- * attend.  akv_attend_chunk takes NULL only (AKV_ERR_UNSUPPORTED otherwise).
+ * one float32 multiply and add per term, no 1/sqrt(d) step), decode and the
+ * prefill chunk rotate each query by R once per call (workspace grows by
+ * 4*B*Tq*Hq*d bytes) and the compressed-tier output by R^T once per
+ * (query, head), and the unrotated vector is R^T times the rotated one.  The
+ * same R must be used to encode and to attend.
  *
  * Code width: every descriptor that encodes or reads the compressed tier has
  * a `code_bits` field, w = 4 (or 0) for the 16-level table and layout above,

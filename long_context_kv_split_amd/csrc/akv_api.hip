@@ -96,7 +96,6 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   if (!chunk && d->Tq != 1) return fail(AKV_ERR_UNSUPPORTED, "decode takes Tq = 1 (got %d)", d->Tq);
   if (chunk && d->Tq > AKV_MAX_CHUNK) return fail(AKV_ERR_UNSUPPORTED, "chunk Tq %d > %d", d->Tq, AKV_MAX_CHUNK);
   if (chunk && e.max_blocks == 0) return fail(AKV_ERR_UNSUPPORTED, "chunk needs the exact tier (it holds the chunk)");
-  if (chunk && d->rotation) return fail(AKV_ERR_UNSUPPORTED, "the chunk takes the Walsh-Hadamard rotation only");
   if (!width_ok(d->code_bits)) return fail(AKV_ERR_UNSUPPORTED, "code_bits %d (supported: 2, 3, 4)", d->code_bits);
   if (chunk && akv::code_width(d->code_bits) != 4) return fail(AKV_ERR_UNSUPPORTED, "the chunk takes 4-bit codes only");
   if (d->B > 65535 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
@@ -209,7 +208,7 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   po = (po + 255) & ~(size_t)255;
   plan->ws_bytes = po + plan->part_rows * sizeof(float);
   plan->qrot_off = (plan->ws_bytes + 255) & ~(size_t)255;
-  if (d->rotation) plan->ws_bytes = plan->qrot_off + (size_t)d->B * d->Hq * d->d * sizeof(float);
+  if (d->rotation) plan->ws_bytes = plan->qrot_off + (size_t)d->B * d->Tq * d->Hq * d->d * sizeof(float);
   return AKV_OK;
 }
 

@@ -448,7 +448,7 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
 }
 
 // ---------------------------------------------------------------- one split
-template <int D, bool QUANT>
+template <int D, bool QUANT, bool ROT>
 __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int kv, int rg, int sx, int start,
                             int end, int el) {
   constexpr int M = D / 32, NT = D / 16;
@@ -507,7 +507,24 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
       raw[m] = *reinterpret_cast<const u32x4*>(qsrc + 32 * m);
       if (r >= R) raw[m] = u32x4{0, 0, 0, 0};
     }
-    if (QUANT) {
+    if constexpr (QUANT && ROT) {
+      // a given rotation R: R q was formed once per call (qrot_kernel); the
+      // compressed tier is read through it as it is
+      const float* qr = p.qrot + (((size_t)b * p.Tq + tau) * p.Hq + kv * G + g) * D + 8 * qq;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float4v a = *reinterpret_cast<const float4v*>(qr + 32 * m);
+        float4v c = *reinterpret_cast<const float4v*>(qr + 32 * m + 4);
+        if (r >= R) a = c = float4v{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = fp32_pinned((e < 4 ? a[e] : c[e - 4]) * p.qscale2);
+          const _Float16 hi = (_Float16)x;
+          Qh[rt][m][e] = hi;
+          Ql[rt][m][e] = (_Float16)(x - (float)hi);
+        }
+      }
+    } else if constexpr (QUANT) {
       float v[M][8];
 #pragma unroll
       for (int m = 0; m < M; ++m)
@@ -628,7 +645,8 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
 // dispatch order, the shorter exact-tier splits fill in behind them.  At
 // d = 64 three workgroups share a compute unit (168 VGPRs, a few spilled,
 // and 27 KB of LDS each), at d = 128 two.
-template <int D>
+// ROT: a caller-given rotation (the rotated queries come from qrot_kernel).
+template <int D, bool ROT>
 __global__ __launch_bounds__(kCThreads, D == 64 ? 3 : 2) void chunk_split_kernel(AttnParams p, int nrg) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[ChunkLds<D>::BYTES];
   const int kv = blockIdx.x / nrg, rg = blockIdx.x - kv * nrg, sx = blockIdx.y, b = blockIdx.z;
@@ -643,17 +661,34 @@ __global__ __launch_bounds__(kCThreads, D == 64 ? 3 : 2) void chunk_split_kernel
   if (start >= len) return;
   const int end = min(start + P, len);
   if (quant)
-    chunk_split<D, true>(p, smem, b, kv, rg, sx, start, end, el);
+    chunk_split<D, true, ROT>(p, smem, b, kv, rg, sx, start, end, el);
   else
-    chunk_split<D, false>(p, smem, b, kv, rg, sx, start, end, el);
+    chunk_split<D, false, false>(p, smem, b, kv, rg, sx, start, end, el);
 }
 
-// ---- merge: one wave per (sequence, query token, query head)
-template <int D>
-__global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p) {
-  constexpr int E = D / 64;
+// ---- merge: one wave per (sequence, query token, query head).  With a
+// given rotation a workgroup takes kRotMergeRows rows and holds R in LDS for
+// their R^T step.
+constexpr int kRotMergeRows = 16;
+
+template <int D, bool ROT>
+__global__ __launch_bounds__(ROT ? 64 * kRotMergeRows : 256) void chunk_merge_kernel(AttnParams p) {
+  constexpr int E = D / 64, ROWS = ROT ? kRotMergeRows : 4;
+  // R (D x D floats) in dynamic LDS, given at launch with a rotation only
+  extern __shared__ __attribute__((aligned(16))) float rsh[];
+  if constexpr (ROT) {
+    // R staged before any wave can leave, all of a thread's loads in flight together
+    constexpr int PER = D * D / 4 / (64 * ROWS);
+    static_assert(PER * 64 * ROWS * 4 == D * D, "R staging covers the matrix");
+    float4v x[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) x[u] = reinterpret_cast<const float4v*>(p.rot)[threadIdx.x + u * 64 * ROWS];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) reinterpret_cast<float4v*>(rsh)[threadIdx.x + u * 64 * ROWS] = x[u];
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
-  const int rowq = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y;
+  const int rowq = blockIdx.x * ROWS + (threadIdx.x >> 6), b = blockIdx.y;
   if (rowq >= p.Tq * p.Hq) return;
   const int tau = rowq / p.Hq, h = rowq - tau * p.Hq;
   const int G = p.G, kv = h / G, g = h - kv * G, R = p.Tq * G;
@@ -746,19 +781,44 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p) {
     res_l[tier] = t.nan ? __builtin_nanf("") : (t.m == neg_inf() ? neg_inf() : t.m + __logf(t.wsum));
   }
   // inverse rotation of the compressed-tier output: dim = lane + 64e
+  float rd = inv_sqrt_d(D);
+  if constexpr (ROT) {
+    // R^T o_rot: dim t of the result is sum_k R[k][t] o_rot[k], in four
+    // ascending partial sums (k mod 4) added in order, each o_rot[k] read
+    // from the lane that holds it
+    float acc[4][E];
 #pragma unroll
-  for (int hh = 1; hh < 64; hh <<= 1)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float o = __shfl_xor(res_o[0][e], hh);
-      res_o[0][e] = (lane & hh) ? (o - res_o[0][e]) : (res_o[0][e] + o);
+      for (int e = 0; e < E; ++e) acc[j][e] = 0.0f;
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = k0 + j;
+        const float ok = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (k < 64) ? res_o[0][0] : res_o[0][E - 1]), k & 63));
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[j][e] = fmaf(rsh[k * D + lane + 64 * e], ok, acc[j][e]);
+      }
     }
-  if constexpr (E == 2) {
-    const float a = res_o[0][0], c = res_o[0][1];
-    res_o[0][0] = a + c;
-    res_o[0][1] = a - c;
+#pragma unroll
+    for (int e = 0; e < E; ++e) res_o[0][e] = (acc[0][e] + acc[1][e]) + (acc[2][e] + acc[3][e]);
+    rd = 1.0f;
+  } else {
+#pragma unroll
+    for (int hh = 1; hh < 64; hh <<= 1)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float o = __shfl_xor(res_o[0][e], hh);
+        res_o[0][e] = (lane & hh) ? (o - res_o[0][e]) : (res_o[0][e] + o);
+      }
+    if constexpr (E == 2) {
+      const float a = res_o[0][0], c = res_o[0][1];
+      res_o[0][0] = a + c;
+      res_o[0][1] = a - c;
+    }
   }
-  const float rd = inv_sqrt_d(D);
   const float la = res_l[0], lb = res_l[1];
   const bool bad = la != la || lb != lb;
   const float Mx = fmaxf(la, lb);
@@ -779,17 +839,29 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p) {
   if (lane == 0) *lout = bad ? __builtin_nanf("") : (none ? neg_inf() : Mx + __logf(W));
 }
 
+hipError_t launch_decode_qrot(const AttnParams& p, int D, hipStream_t stream);
+
 hipError_t launch_chunk(const AttnParams& p, int D, hipStream_t stream) {
+  hipError_t qe = launch_decode_qrot(p, D, stream);
+  if (qe != hipSuccess) return qe;
   const int R = p.Tq * p.G;
   const int nrg = (R + kRowsPerWG - 1) / kRowsPerWG;
   const dim3 grid(p.Hkv * nrg, p.Sq + p.Se, p.B);
-  const dim3 mgrid((p.Tq * p.Hq + 3) / 4, p.B);
-  if (D == 64) {
-    hipLaunchKernelGGL(chunk_split_kernel<64>, grid, dim3(kCThreads), 0, stream, p, nrg);
-    hipLaunchKernelGGL(chunk_merge_kernel<64>, mgrid, dim3(256), 0, stream, p);
+  const dim3 mgrid((p.Tq * p.Hq + 3) / 4, p.B), rgrid((p.Tq * p.Hq + kRotMergeRows - 1) / kRotMergeRows, p.B);
+  if (D == 64 && p.rot) {
+    hipLaunchKernelGGL((chunk_split_kernel<64, true>), grid, dim3(kCThreads), 0, stream, p, nrg);
+    hipLaunchKernelGGL((chunk_merge_kernel<64, true>), rgrid, dim3(64 * kRotMergeRows), 64 * 64 * sizeof(float),
+                       stream, p);
+  } else if (D == 64) {
+    hipLaunchKernelGGL((chunk_split_kernel<64, false>), grid, dim3(kCThreads), 0, stream, p, nrg);
+    hipLaunchKernelGGL((chunk_merge_kernel<64, false>), mgrid, dim3(256), 0, stream, p);
+  } else if (p.rot) {
+    hipLaunchKernelGGL((chunk_split_kernel<128, true>), grid, dim3(kCThreads), 0, stream, p, nrg);
+    hipLaunchKernelGGL((chunk_merge_kernel<128, true>), rgrid, dim3(64 * kRotMergeRows), 128 * 128 * sizeof(float),
+                       stream, p);
   } else {
-    hipLaunchKernelGGL(chunk_split_kernel<128>, grid, dim3(kCThreads), 0, stream, p, nrg);
-    hipLaunchKernelGGL(chunk_merge_kernel<128>, mgrid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((chunk_split_kernel<128, false>), grid, dim3(kCThreads), 0, stream, p, nrg);
+    hipLaunchKernelGGL((chunk_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }

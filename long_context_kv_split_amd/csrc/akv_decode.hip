@@ -771,7 +771,7 @@ struct EUnit {
 // read in 64-byte pieces by four instructions, so they keep normal loads).
 template <int D, bool NTV>
 __device__ inline void exact_load(EUnit<D>& u, const AttnParams& p, int pb, int kv, int c, int j, int qq, int lane) {
-  constexpr int MK = D / 32, NT = D / 16;
+  constexpr int MK = D / 32;
   const uint16_t* kslab = p.ek + ((size_t)pb * p.Hkv + kv) * kBlock * D;
   const uint16_t* vslab = p.ev + ((size_t)pb * p.Hkv + kv) * kBlock * D;
 #pragma unroll
@@ -1350,34 +1350,88 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* op, const f
   }
 }
 
-// q' = R q for every (sequence, query head), once per call, when the
-// compressed tier uses a given rotation R: thread i takes row i of R.
-// The query value is requested first and the whole row after it, so one
-// round trip covers both.
-template <int D>
+// q' = R q for every (sequence, query token, query head), once per call, when
+// the compressed tier uses a given rotation R.  A workgroup takes up to
+// kQrotTokens query tokens of one head: their query values are requested
+// first; R is staged in LDS (coalesced, rows padded to D + 1 floats so that
+// thread i reading row i hits bank (i + k) mod 64) and thread i keeps row i
+// in registers; the queries then replace R in LDS and thread i forms
+// output i of each, two queries at a time with four partial sums each
+// (k mod 4, ascending k, added in order).  NT: tokens per workgroup
+// (kQrotTokens for a chunk; 1 for decode, where each of the few workgroups
+// reads its rows of R directly).
+constexpr int kQrotTokens = 32;
+
+template <int D, int NT>
 __global__ __launch_bounds__(D) void qrot_kernel(AttnParams p) {
-  __shared__ float qs[D];
-  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
-  const uint16_t qb = p.q[((size_t)b * p.Hq + h) * D + i];
-  const float4v* row = reinterpret_cast<const float4v*>(p.rot + (size_t)i * D);
-  float4v r[D / 4];
+  __shared__ float rs[NT == 1 ? D : D * (D + 1)];
+  static_assert(NT == 1 || NT * D <= D * (D + 1), "the queries fit where R was staged");
+  // tokens y NT .. of sequence z, head x: rows (z Tq + t) Hq + x of q and qrot
+  const int h = blockIdx.x, i = threadIdx.x;
+  const int t0 = blockIdx.y * NT, nt = min(NT, p.Tq - t0);
+  const size_t b0 = (size_t)blockIdx.z * p.Tq + t0;
+  if constexpr (NT == 1) {
+    // one query: thread i reads row i of R straight into registers, the
+    // query value requested first so that one round trip covers both
+    float* qs = rs;
+    const uint16_t q1 = p.q[(b0 * p.Hq + h) * D + i];
+    const float4v* row = reinterpret_cast<const float4v*>(p.rot + (size_t)i * D);
+    float4v r[D / 4];
 #pragma unroll
-  for (int k4 = 0; k4 < D / 4; ++k4) r[k4] = row[k4];
-  qs[i] = bf16_bits_to_float(qb);
-  __syncthreads();
-  float acc = 0.0f;
+    for (int k4 = 0; k4 < D / 4; ++k4) r[k4] = row[k4];
+    qs[i] = bf16_bits_to_float(q1);
+    __syncthreads();
+    float acc = 0.0f;
 #pragma unroll
-  for (int k4 = 0; k4 < D / 4; ++k4)
-    acc += r[k4][0] * qs[4 * k4] + r[k4][1] * qs[4 * k4 + 1] + r[k4][2] * qs[4 * k4 + 2] + r[k4][3] * qs[4 * k4 + 3];
-  p.qrot[((size_t)b * p.Hq + h) * D + i] = acc;
+    for (int k4 = 0; k4 < D / 4; ++k4)
+      acc += r[k4][0] * qs[4 * k4] + r[k4][1] * qs[4 * k4 + 1] + r[k4][2] * qs[4 * k4 + 2] + r[k4][3] * qs[4 * k4 + 3];
+    p.qrot[(b0 * p.Hq + h) * D + i] = acc;
+  } else {
+    uint16_t qb[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) qb[t] = p.q[((b0 + min(t, nt - 1)) * p.Hq + h) * D + i];
+#pragma unroll 4
+    for (int e = i; e < D * D; e += D) rs[(e / D) * (D + 1) + e % D] = p.rot[e];
+    __syncthreads();
+    float4v r[D / 4];
+#pragma unroll
+    for (int k4 = 0; k4 < D / 4; ++k4)
+      r[k4] = float4v{rs[i * (D + 1) + 4 * k4], rs[i * (D + 1) + 4 * k4 + 1], rs[i * (D + 1) + 4 * k4 + 2],
+                      rs[i * (D + 1) + 4 * k4 + 3]};
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) rs[t * D + i] = bf16_bits_to_float(qb[t]);
+    __syncthreads();
+    for (int t = 0; t < nt; t += 2) {
+      const float* u = rs + t * D;
+      const float* v = rs + min(t + 1, NT - 1) * D;
+      float au[4] = {0.0f, 0.0f, 0.0f, 0.0f}, av[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k4 = 0; k4 < D / 4; ++k4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          au[j] = fmaf(r[k4][j], u[4 * k4 + j], au[j]);
+          av[j] = fmaf(r[k4][j], v[4 * k4 + j], av[j]);
+        }
+      p.qrot[((b0 + t) * p.Hq + h) * D + i] = (au[0] + au[1]) + (au[2] + au[3]);
+      if (t + 1 < nt) p.qrot[((b0 + t + 1) * p.Hq + h) * D + i] = (av[0] + av[1]) + (av[2] + av[3]);
+    }
+  }
 }
 
 hipError_t launch_decode_qrot(const AttnParams& p, int D, hipStream_t stream) {
   if (!p.rot) return hipSuccess;
-  if (D == 64)
-    hipLaunchKernelGGL(qrot_kernel<64>, dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  if (D == 64) {
+    if (p.Tq == 1)
+      hipLaunchKernelGGL((qrot_kernel<64, 1>), dim3(p.Hq, 1, p.B), dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((qrot_kernel<64, kQrotTokens>), dim3(p.Hq, (p.Tq + kQrotTokens - 1) / kQrotTokens, p.B),
+                         dim3(64), 0, stream, p);
+  } else if (p.Tq == 1)
+    hipLaunchKernelGGL((qrot_kernel<128, 1>), dim3(p.Hq, 1, p.B), dim3(128), 0, stream, p);
   else
-    hipLaunchKernelGGL(qrot_kernel<128>, dim3(p.Hq, p.B), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((qrot_kernel<128, kQrotTokens>), dim3(p.Hq, (p.Tq + kQrotTokens - 1) / kQrotTokens, p.B),
+                       dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 

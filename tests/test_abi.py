@@ -397,8 +397,8 @@ def test_staged_decode_validation_order():
 
 
 def test_rotation_field():
-    """A given rotation: 16-byte aligned, refused by the chunk, and the decode
-    workspace grows by the rotated queries (4 B * Hq * d bytes, 256-aligned)."""
+    """A given rotation: 16-byte aligned, and the decode and chunk workspaces
+    grow by the rotated queries (4 B * Tq * Hq * d bytes, 256-aligned)."""
     d = good_desc()
     need = akv.akv_decode_workspace_bytes(d)
     dr = good_desc(rotation=FAKE + 0x800000)
@@ -407,8 +407,12 @@ def test_rotation_field():
     assert need + extra <= need_r <= need + extra + 256
     assert call(dr, ws_bytes=need_r - 1) == akv.AKV_ERR_WORKSPACE
     assert call(good_desc(rotation=FAKE + 8)) == akv.AKV_ERR_ALIGN
-    assert call(good_desc(Tq=4, rotation=FAKE + 0x800000), chunk=True) == akv.AKV_ERR_UNSUPPORTED
-    assert "rotation" in akv.akv_last_error()
+    dc, dcr = good_desc(Tq=4), good_desc(Tq=4, rotation=FAKE + 0x800000)
+    need_c, need_cr = akv.akv_chunk_workspace_bytes(dc), akv.akv_chunk_workspace_bytes(dcr)
+    extra_c = 4 * dc.B * dc.Tq * dc.Hq * dc.d
+    assert need_c + extra_c <= need_cr <= need_c + extra_c + 256
+    assert call(dcr, ws_bytes=need_cr - 1, chunk=True) == akv.AKV_ERR_WORKSPACE
+    assert call(good_desc(Tq=4, rotation=FAKE + 8), chunk=True) == akv.AKV_ERR_ALIGN
     assert akv.akv_compress_evicted(compress_desc(rotation=FAKE + 4)) == akv.AKV_ERR_ALIGN
     assert akv.akv_append_evict(append_desc(rotation=FAKE + 4)) == akv.AKV_ERR_ALIGN
 

@@ -4,8 +4,8 @@ The QuantForge walkthrough (section 5, "README Polish") compares the
 Walsh-Hadamard rotation with a QR one.  With a rotation R passed in the
 descriptors the encoder computes y = R x (float32, ascending k, no fused
 multiply-add), so codes and scales are bit-exact against the oracle's dense
-encoder; decode rotates the query by R and the compressed-tier output by R^T,
-within the attention tolerances.  The chunk entry point refuses a rotation.
+encoder; decode and the prefill chunk rotate the query by R and the
+compressed-tier output by R^T, within the attention tolerances.
 """
 import numpy as np
 import pytest
@@ -132,11 +132,36 @@ def test_qr_staged_equals_resident():
     assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "QR staged vs oracle")
 
 
-def test_qr_chunk_refused():
+@pytest.mark.parametrize("cfg", [
+    # 160 rows: two row groups, the second ragged; several splits per tier
+    dict(B=1, Hq=8, Hkv=2, d=128, quant=[1000], exact=[300], Tq=40, split_exact=128, split_quant=256),
+    # G = 6 (a row group boundary inside a query's heads) and a sequence with
+    # no compressed tier
+    dict(B=2, Hq=12, Hkv=2, d=128, quant=[300, 0], exact=[65, 80], Tq=17, split_quant=64),
+    # head dim 64, outlier channels
+    dict(B=1, Hq=4, Hkv=1, d=64, quant=[383], exact=[129], Tq=33, split_exact=64, split_quant=128,
+         outlier_frac=0.02),
+])
+def test_qr_chunk_parity(cfg):
     akv, harness = _mods()
-    w = synth.make_small("qr_chunk", B=1, Hq=8, Hkv=2, d=128, quant=[256], exact=[128], causal_tail=64)
-    dw = harness.DeviceWorkload(w, rotation=synth.qr_rotation(128))
-    desc = dw.desc()
-    dw.ensure_ws(desc, chunk=False)
-    st = akv.akv_attend_chunk(desc, harness.ptr(dw.ws), dw.ws_bytes, harness.stream_handle())
-    assert st == akv.AKV_ERR_UNSUPPORTED, akv.akv_last_error()
+    cfg = dict(cfg)
+    kw = {k: cfg.pop(k) for k in ("split_exact", "split_quant") if k in cfg}
+    w = synth.make_small("qr_chunk", causal_tail=cfg["Tq"], **cfg)
+    R = synth.qr_rotation(w.d, seed=5)
+    _say(f"QR chunk: B={w.B} Tq={w.Tq} Hq={w.Hq} Hkv={w.Hkv} d={w.d} quant={list(w.quant_len)} "
+         f"exact={list(w.exact_len)} {kw}")
+    dw = harness.DeviceWorkload(w, rotation=R)
+    akv.check(dw.attend(**kw))
+    torch.cuda.synchronize()
+    o, lse = dw.o.cpu().numpy(), dw.lse.cpu().numpy()
+    ek, ev = _encoded(w, R)
+    qs = [b for b in range(w.B) if w.quant_len[b]]
+    assert_codes(dw, w, {b: ek[b] for b in qs}, {b: ev[b] for b in qs}, "QR chunk")
+    o_ref, lse_ref = O.reference_outputs(w, [ek[b] for b in range(w.B)], [ev[b] for b in range(w.B)],
+                                         rotation=R)
+    assert_attention(o, lse, o_ref, lse_ref, f"QR chunk {cfg} {kw}")
+    # deterministic: a second call gives the same bytes
+    o1, l1 = dw.o.clone(), dw.lse.clone()
+    akv.check(dw.attend(**kw))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, dw.o) and torch.equal(l1, dw.lse)
