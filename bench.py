@@ -405,13 +405,13 @@ def bench_widths(w, ev4_ms, stream, steps=500, warmup=20):
     return out
 
 
-def bench_chunk_rotation(w, ev_hadamard_ms, stream, steps=40, warmup=5, min_bytes=2 * MALL_BYTES):
-    """The 512-query chunk with the compressed tier under a QR rotation: the
-    queries rotated by R once per call, each (query, head) output by R^T."""
-    from long_context_kv_split_amd import akv, harness, synth
-    R = synth.qr_rotation(w.d, seed=0)
-    dw = harness.DeviceWorkload(w, rotation=R)
-    n_rep = max(1, -(-min_bytes // w.kv_bytes()))
+def bench_chunk_variant(w, stream, rotation=None, width=4, steps=40, warmup=5, min_bytes=2 * MALL_BYTES):
+    """Time per call (ms) of the 512-query chunk with the compressed tier under
+    a given rotation (queries rotated by R once per call, each (query, head)
+    output by R^T) and / or at code width 2 or 3."""
+    from long_context_kv_split_amd import akv, harness
+    dw = harness.DeviceWorkload(w, rotation=rotation, width=width)
+    n_rep = max(1, -(-min_bytes // w.kv_bytes(width)))
     dw.add_replicas(n_rep)
     descs = [dw.desc(r) for r in range(n_rep)]
     dw.ensure_ws(descs[0], chunk=True)
@@ -425,8 +425,7 @@ def bench_chunk_rotation(w, ev_hadamard_ms, stream, steps=40, warmup=5, min_byte
 
     ev_ms, _ = time_calls(call, n_rep, warmup, steps, stream, AUX_WARM_MS)
     del dw
-    return {"chunk_us_per_call": ev_ms * 1e3, "chunk_us_per_call_hadamard": ev_hadamard_ms * 1e3,
-            "chunk_tflops": chunk_flops(w) / (ev_ms * 1e-3) / 1e12}
+    return ev_ms
 
 
 def chunk_flops(w) -> float:
@@ -634,10 +633,18 @@ def main():
             workloads["chunk"] = chunk.pop("_workload")
             log(f"bench: chunk {chunk['us_per_call']:.1f} us/call, {chunk['roofline']['achieved']:.1f} TFLOP/s")
             if rot is not None:
-                rc = bench_chunk_rotation(workloads["chunk"], chunk["us_per_call"] * 1e-3, stream)
-                rot.update(rc)
+                from long_context_kv_split_amd import synth
+                wc = workloads["chunk"]
+                qr_ms = bench_chunk_variant(wc, stream, rotation=synth.qr_rotation(wc.d, seed=0))
+                rot.update({"chunk_us_per_call": qr_ms * 1e3, "chunk_us_per_call_hadamard": chunk["us_per_call"],
+                            "chunk_tflops": chunk_flops(wc) / (qr_ms * 1e-3) / 1e12})
                 rot["workload"] += "; the 512-query chunk with a QR rotation"
-                log(f"bench: QR chunk {rc['chunk_us_per_call']:.1f} us/call (Hadamard {chunk['us_per_call']:.1f})")
+                log(f"bench: QR chunk {qr_ms * 1e3:.1f} us/call (Hadamard {chunk['us_per_call']:.1f})")
+                widths["chunk"] = {"4": chunk["us_per_call"]}
+                widths["workload"] += "; chunk: the 512-query chunk's us per call at widths 4, 3, 2"
+                for width in (3, 2):
+                    widths["chunk"][str(width)] = bench_chunk_variant(wc, stream, width=width) * 1e3
+                log("bench: chunk widths " + ", ".join(f"{k}-bit {v:.1f} us" for k, v in widths["chunk"].items()))
         copy_calibration()
     copy_meas = device_copy_gbps()
     log(f"bench: device copy {copy_meas['gbps']:.0f} GB/s (read + write)")

@@ -103,7 +103,6 @@
  *       32m + 8a + 2b and + 1;
  *     V: byte ((c*4 + a)*16 + i)*(d/16) + 4*n + b, bits 2*h + {0, 1}, holds
  *       dim 16(4n + h) + i of tokens 32c + 8a + 2b and + 1.
- * akv_attend_chunk takes w = 4 only (AKV_ERR_UNSUPPORTED otherwise).
  *
  * Block tables: int32 [B][max_blocks]; entry j of row b is the pool block of
  * tier-local tokens [64j, 64j+64) of sequence b.  Tier lengths: int32 [B].

@@ -97,7 +97,6 @@ akv_status check_attn(const akv_attn_desc* d, bool chunk, Plan* plan, bool stage
   if (chunk && d->Tq > AKV_MAX_CHUNK) return fail(AKV_ERR_UNSUPPORTED, "chunk Tq %d > %d", d->Tq, AKV_MAX_CHUNK);
   if (chunk && e.max_blocks == 0) return fail(AKV_ERR_UNSUPPORTED, "chunk needs the exact tier (it holds the chunk)");
   if (!width_ok(d->code_bits)) return fail(AKV_ERR_UNSUPPORTED, "code_bits %d (supported: 2, 3, 4)", d->code_bits);
-  if (chunk && akv::code_width(d->code_bits) != 4) return fail(AKV_ERR_UNSUPPORTED, "the chunk takes 4-bit codes only");
   if (d->B > 65535 || d->Hkv > 65535) return fail(AKV_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
   int Pe, Pq;
   if (!chunk) {

@@ -109,15 +109,43 @@ __device__ inline int vchunk_off(int dim, int c) {
 // Register copy of one block's share for this thread.
 // A block's staging work is cut into 512 slots; thread t takes slots
 // t + kCThreads * u (u < kVT).
-template <int D>
+// W: code width.  At W = 4 a code dword holds four table fields (bytes, two
+// codes each); at W = 2 and 3 it is the pair-plane dword whose nibbles
+// (at W = 3 with two high-plane bits above each) form the fields.
+template <int D, int W>
 struct QRegs {
   static constexpr int KDW = D / 64;  // K code dwords per slot
   static constexpr int VDW = D / 64;  // V code dwords per slot
   uint32_t kc[kVT][KDW];
+  uint32_t kh[kVT][KDW];  // W = 3: the high-plane bits of the slot's K dims
   uint32_t ks[kVT][KDW];  // fp16 K scale of each dword's group (low 16 bits)
   uint32_t vc[kVT][VDW];
+  uint32_t vh[kVT][VDW];  // W = 3: the high-plane bits of the slot's V tiles
   u32x4 vs[kVT];          // fp16 V scales of the slot's group, tokens tok0 .. tok0 + 7
 };
+
+// Table fields of K dword k of slot u (group m, dims 32m + 8a + 2b, +1 in
+// byte b) and of V dword k (value tile tt).
+template <int D, int W>
+__device__ inline uint32_t chunk_kfield(const QRegs<D, W>& r, int u, int k, int m) {
+  if constexpr (W == 4) {
+    return r.kc[u][k];
+  } else {
+    uint32_t f = (r.kc[u][k] >> (4 * (m & 1))) & 0x0F0F0F0Fu;
+    if constexpr (W == 3) f |= ((r.kh[u][k] >> (2 * m)) & 0x03030303u) << 4;
+    return f;
+  }
+}
+template <int D, int W>
+__device__ inline uint32_t chunk_vfield(const QRegs<D, W>& r, int u, int k, int tt) {
+  if constexpr (W == 4) {
+    return r.vc[u][k];
+  } else {
+    uint32_t f = (r.vc[u][k] >> (4 * (tt & 1))) & 0x0F0F0F0Fu;
+    if constexpr (W == 3) f |= ((r.vh[u][k] >> (2 * (tt & 3))) & 0x03030303u) << 4;
+    return f;
+  }
+}
 template <int D>
 struct ERegs {
   static constexpr int KCH = 64 * D / 8 / 512;  // 16-byte K chunks per slot
@@ -137,33 +165,59 @@ __device__ inline int qk_dword(int t, int k) {
   }
 }
 
-template <int D>
-__device__ inline void quant_fetch(QRegs<D>& r, const AttnParams& p, int pb, int kv) {
+template <int D, int W>
+__device__ inline void quant_fetch(QRegs<D, W>& r, const AttnParams& p, int pb, int kv) {
   constexpr int M = D / 32;
   const int t = threadIdx.x;
   const size_t slab = (size_t)pb * p.Hkv + kv;
-  const uint32_t* kcs = reinterpret_cast<const uint32_t*>(p.kc + slab * (32 * D));
-  const uint32_t* vcs = reinterpret_cast<const uint32_t*>(p.vc + slab * (32 * D));
+  const uint32_t* kcs = reinterpret_cast<const uint32_t*>(p.kc + slab * (8 * W * D));
+  const uint32_t* vcs = reinterpret_cast<const uint32_t*>(p.vc + slab * (8 * W * D));
   const uint16_t* kss = p.ks + slab * (2 * D);
   const uint16_t* vss = p.vs + slab * (2 * D);
 #pragma unroll
   for (int u = 0; u < kVT; ++u) {
     const int v = t + kCThreads * u, tok = v >> 3;
 #pragma unroll
-    for (int k = 0; k < QRegs<D>::KDW; ++k) {
-      const int wi = qk_dword<D>(v, k);
-      r.kc[u][k] = kcs[tok * (D / 8) + wi];
-      r.ks[u][k] = kss[(wi % M) * 64 + tok];
+    for (int k = 0; k < QRegs<D, W>::KDW; ++k) {
+      const int wi = qk_dword<D>(v, k), m = wi % M, a = wi / M;
+      if constexpr (W == 4) {
+        r.kc[u][k] = kcs[tok * (D / 8) + wi];
+      } else {
+        // pair plane: token rows of D/4 bytes, dword (D/64) a + m/2 holds
+        // groups m & ~1 and m | 1 in its low and high nibbles
+        r.kc[u][k] = kcs[tok * (D / 16) + (D / 64) * a + (m >> 1)];
+        if constexpr (W == 3) {
+          // high plane after the pair plane: token rows of D/8 bytes; the
+          // two bits of dims 32m + 8a + 2b, +1 at row bit 8 M a + 2 M b + 2m
+          const unsigned char* hrow = reinterpret_cast<const unsigned char*>(kcs) + 16 * D + tok * (D / 8);
+          if constexpr (D == 128) {
+            r.kh[u][k] = reinterpret_cast<const uint32_t*>(hrow)[a];
+          } else {  // 16 bits per a: nibble b -> byte b
+            const uint32_t h = reinterpret_cast<const uint16_t*>(hrow)[a];
+            r.kh[u][k] = (h & 0xFu) | ((h << 4) & 0xF00u) | ((h << 8) & 0xF0000u) | ((h << 12) & 0xF000000u);
+          }
+        }
+      }
+      r.ks[u][k] = kss[m * 64 + tok];
     }
     // V: slots run over i (dim within 16), then over 4 dword columns, then 8
     // token groups (c, a); dword of tile t at c*16D + (t/4)*1 KB + (16a + i)*16 + 4(t%4) bytes
     const int i = v & 15, tq = (v >> 4) & 3, ca = v >> 6;
 #pragma unroll
-    for (int k = 0; k < QRegs<D>::VDW; ++k) {
-      const int tt = tq * QRegs<D>::VDW + k;
-      r.vc[u][k] = vcs[(ca >> 2) * 4 * D + (tt >> 2) * 256 + ((ca & 3) * 16 + i) * 4 + (tt & 3)];
+    for (int k = 0; k < QRegs<D, W>::VDW; ++k) {
+      const int tt = tq * QRegs<D, W>::VDW + k;
+      if constexpr (W == 4) {
+        r.vc[u][k] = vcs[(ca >> 2) * 4 * D + (tt >> 2) * 256 + ((ca & 3) * 16 + i) * 4 + (tt & 3)];
+      } else {
+        // pair plane: D/8 bytes per (token group ca, lane dim i), dword tt/2
+        // holds tiles tt & ~1 and tt | 1 in its low and high nibbles
+        r.vc[u][k] = vcs[(ca * 16 + i) * (D / 32) + (tt >> 1)];
+        if constexpr (W == 3)  // high plane: D/16 bytes per (ca, i), dword tt/4, bits 2 (tt % 4) of each byte
+          r.vh[u][k] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(vcs) + 16 * D)
+              [(ca * 16 + i) * (D / 64) + (tt >> 2)];
+      }
     }
-    const int g = (16 * tq * QRegs<D>::VDW + i) >> 5;
+    const int g = (16 * tq * QRegs<D, W>::VDW + i) >> 5;
     r.vs[u] = *reinterpret_cast<const u32x4*>(vss + g * 64 + 8 * ca);
   }
 }
@@ -193,23 +247,25 @@ __device__ inline void exact_fetch(ERegs<D>& r, const AttnParams& p, int pb, int
 }
 
 // Compressed K -> LDS (fp16 hi + lo of the fp32 product level x scale).
-template <int D>
-__device__ inline void quant_stage_k(const QRegs<D>& r, unsigned char* smem, unsigned char* buf, int nvalid) {
+template <int D, int W>
+__device__ inline void quant_stage_k(const QRegs<D, W>& r, unsigned char* smem, unsigned char* buf, int nvalid) {
   constexpr int M = D / 32;
   const float2* klut = reinterpret_cast<const float2*>(smem + ChunkLds<D>::KLUT);
   // every table read of this thread's share first, so they are in flight
   // together, then the products and conversions
-  float2 lvs[kVT][QRegs<D>::KDW][4];
+  float2 lvs[kVT][QRegs<D, W>::KDW][4];
 #pragma unroll
   for (int u = 0; u < kVT; ++u)
 #pragma unroll
-    for (int k = 0; k < QRegs<D>::KDW; ++k)
+    for (int k = 0; k < QRegs<D, W>::KDW; ++k) {
+      const uint32_t f = chunk_kfield<D, W>(r, u, k, qk_dword<D>(threadIdx.x + kCThreads * u, k) % M);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) lvs[u][k][b] = klut[(r.kc[u][k] >> (8 * b)) & 0xFFu];
+      for (int b = 0; b < 4; ++b) lvs[u][k][b] = klut[(f >> (8 * b)) & 0xFFu];
+    }
 #pragma unroll
   for (int u = 0; u < kVT; ++u)
 #pragma unroll
-  for (int k = 0; k < QRegs<D>::KDW; ++k) {
+  for (int k = 0; k < QRegs<D, W>::KDW; ++k) {
     const int v = threadIdx.x + kCThreads * u, tok = v >> 3;
     const int wi = qk_dword<D>(v, k), m = wi % M, a = wi / M;
     const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(tok < nvalid ? r.ks[u][k] & 0xFFFFu : 0u));
@@ -231,8 +287,8 @@ __device__ inline void quant_stage_k(const QRegs<D>& r, unsigned char* smem, uns
 }
 
 // Compressed V -> LDS as V^T (fp16 level pair x fp16 scale pair).
-template <int D>
-__device__ inline void quant_stage_v(const QRegs<D>& r, unsigned char* smem, unsigned char* buf, int nvalid) {
+template <int D, int W>
+__device__ inline void quant_stage_v(const QRegs<D, W>& r, unsigned char* smem, unsigned char* buf, int nvalid) {
   const uint32_t* vlut = reinterpret_cast<const uint32_t*>(smem + ChunkLds<D>::VLUT);
 #pragma unroll
   for (int u = 0; u < kVT; ++u) {
@@ -246,12 +302,13 @@ __device__ inline void quant_stage_v(const QRegs<D>& r, unsigned char* smem, uns
       }
     }
 #pragma unroll
-    for (int k = 0; k < QRegs<D>::VDW; ++k) {
-      const int dim = 16 * (tq * QRegs<D>::VDW + k) + i;
+    for (int k = 0; k < QRegs<D, W>::VDW; ++k) {
+      const int tt = tq * QRegs<D, W>::VDW + k, dim = 16 * tt + i;
+      const uint32_t f = chunk_vfield<D, W>(r, u, k, tt);
       u32x4 out;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const half2v lv = __builtin_bit_cast(half2v, vlut[(r.vc[u][k] >> (8 * b)) & 0xFFu]);
+        const half2v lv = __builtin_bit_cast(half2v, vlut[(f >> (8 * b)) & 0xFFu]);
         // copy the element out first: a bit cast applied to a vector element
         // expression reads element 0 whatever the index
         const uint32_t sb = sc[b];
@@ -448,11 +505,11 @@ __device__ inline void compute_half(const unsigned char* buf, int c, bool mask, 
 }
 
 // ---------------------------------------------------------------- one split
-template <int D, bool QUANT, bool ROT>
+template <int D, bool QUANT, bool ROT, int W>
 __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int kv, int rg, int sx, int start,
                             int end, int el) {
   constexpr int M = D / 32, NT = D / 16;
-  using Regs = typename std::conditional<QUANT, QRegs<D>, ERegs<D>>::type;
+  using Regs = typename std::conditional<QUANT, QRegs<D, W>, ERegs<D>>::type;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, qq = lane >> 4;
   const int G = p.G, R = p.Tq * G;
@@ -475,15 +532,25 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
   auto raw_id = [&](int n) { return n < nb ? table[(start >> 6) + n] : 0; };
   auto fetch = [&](Regs& r, int pb) {
     if constexpr (QUANT)
-      quant_fetch<D>(r, p, checked(pb), kv);
+      quant_fetch<D, W>(r, p, checked(pb), kv);
     else
       exact_fetch<D>(r, p, checked(pb), kv);
   };
 
-  // ---- byte tables (compressed tier)
-  for (int e = tid; QUANT && e < 256; e += kCThreads) {
-    const float c0 = __builtin_bit_cast(float, kLevelBits[e & 15]);
-    const float c1 = __builtin_bit_cast(float, kLevelBits[e >> 4]);
+  // ---- field tables (compressed tier): entry e holds the levels of the two
+  // codes of field e (W = 4: nibbles; W = 2: 2-bit halves; W = 3: 2-bit
+  // halves with their top bits in bits 4 and 5)
+  for (int e = tid; QUANT && e < (1 << (2 * W)); e += kCThreads) {
+    int i0, i1;
+    if constexpr (W == 4) {
+      i0 = e & 15, i1 = e >> 4;
+    } else if constexpr (W == 3) {
+      i0 = (e & 3) | (((e >> 4) & 1) << 2), i1 = ((e >> 2) & 3) | (((e >> 5) & 1) << 2);
+    } else {
+      i0 = e & 3, i1 = (e >> 2) & 3;
+    }
+    const float c0 = __builtin_bit_cast(float, level_bits<W>()[i0]);
+    const float c1 = __builtin_bit_cast(float, level_bits<W>()[i1]);
     reinterpret_cast<float2*>(smem + ChunkLds<D>::KLUT)[e] = float2{c0, c1};
     reinterpret_cast<half2v*>(smem + ChunkLds<D>::VLUT)[e] = half2v{(_Float16)c0, (_Float16)c1};
   }
@@ -599,8 +666,8 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
   for (int n = 0; n < nb; ++n) {
     if (n) __syncthreads();  // every wave is done with the previous block
     if constexpr (QUANT) {
-      quant_stage_k<D>(regs, smem, buf, nvalid_of(n));
-      quant_stage_v<D>(regs, smem, buf, nvalid_of(n));
+      quant_stage_k<D, W>(regs, smem, buf, nvalid_of(n));
+      quant_stage_v<D, W>(regs, smem, buf, nvalid_of(n));
     } else {
       exact_stage_k<D>(regs, buf, nvalid_of(n));
       exact_stage_v<D>(regs, buf, nvalid_of(n));
@@ -645,8 +712,9 @@ __device__ void chunk_split(const AttnParams& p, unsigned char* smem, int b, int
 // dispatch order, the shorter exact-tier splits fill in behind them.  At
 // d = 64 three workgroups share a compute unit (168 VGPRs, a few spilled,
 // and 27 KB of LDS each), at d = 128 two.
-// ROT: a caller-given rotation (the rotated queries come from qrot_kernel).
-template <int D, bool ROT>
+// ROT: a caller-given rotation (the rotated queries come from qrot_kernel);
+// W: the compressed tier's code width.
+template <int D, bool ROT, int W>
 __global__ __launch_bounds__(kCThreads, D == 64 ? 3 : 2) void chunk_split_kernel(AttnParams p, int nrg) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[ChunkLds<D>::BYTES];
   const int kv = blockIdx.x / nrg, rg = blockIdx.x - kv * nrg, sx = blockIdx.y, b = blockIdx.z;
@@ -661,9 +729,9 @@ __global__ __launch_bounds__(kCThreads, D == 64 ? 3 : 2) void chunk_split_kernel
   if (start >= len) return;
   const int end = min(start + P, len);
   if (quant)
-    chunk_split<D, true, ROT>(p, smem, b, kv, rg, sx, start, end, el);
+    chunk_split<D, true, ROT, W>(p, smem, b, kv, rg, sx, start, end, el);
   else
-    chunk_split<D, false, false>(p, smem, b, kv, rg, sx, start, end, el);
+    chunk_split<D, false, false, 4>(p, smem, b, kv, rg, sx, start, end, el);
 }
 
 // ---- merge: one wave per (sequence, query token, query head).  With a
@@ -841,6 +909,23 @@ __global__ __launch_bounds__(ROT ? 64 * kRotMergeRows : 256) void chunk_merge_ke
 
 hipError_t launch_decode_qrot(const AttnParams& p, int D, hipStream_t stream);
 
+template <int D, bool ROT>
+static void launch_chunk_split_w(const AttnParams& p, dim3 grid, int nrg, hipStream_t stream) {
+  if (p.qw == 2)
+    hipLaunchKernelGGL((chunk_split_kernel<D, ROT, 2>), grid, dim3(kCThreads), 0, stream, p, nrg);
+  else if (p.qw == 3)
+    hipLaunchKernelGGL((chunk_split_kernel<D, ROT, 3>), grid, dim3(kCThreads), 0, stream, p, nrg);
+  else
+    hipLaunchKernelGGL((chunk_split_kernel<D, ROT, 4>), grid, dim3(kCThreads), 0, stream, p, nrg);
+}
+template <int D>
+static void launch_chunk_split(const AttnParams& p, dim3 grid, int nrg, hipStream_t stream) {
+  if (p.rot)
+    launch_chunk_split_w<D, true>(p, grid, nrg, stream);
+  else
+    launch_chunk_split_w<D, false>(p, grid, nrg, stream);
+}
+
 hipError_t launch_chunk(const AttnParams& p, int D, hipStream_t stream) {
   hipError_t qe = launch_decode_qrot(p, D, stream);
   if (qe != hipSuccess) return qe;
@@ -848,20 +933,20 @@ hipError_t launch_chunk(const AttnParams& p, int D, hipStream_t stream) {
   const int nrg = (R + kRowsPerWG - 1) / kRowsPerWG;
   const dim3 grid(p.Hkv * nrg, p.Sq + p.Se, p.B);
   const dim3 mgrid((p.Tq * p.Hq + 3) / 4, p.B), rgrid((p.Tq * p.Hq + kRotMergeRows - 1) / kRotMergeRows, p.B);
-  if (D == 64 && p.rot) {
-    hipLaunchKernelGGL((chunk_split_kernel<64, true>), grid, dim3(kCThreads), 0, stream, p, nrg);
-    hipLaunchKernelGGL((chunk_merge_kernel<64, true>), rgrid, dim3(64 * kRotMergeRows), 64 * 64 * sizeof(float),
-                       stream, p);
-  } else if (D == 64) {
-    hipLaunchKernelGGL((chunk_split_kernel<64, false>), grid, dim3(kCThreads), 0, stream, p, nrg);
-    hipLaunchKernelGGL((chunk_merge_kernel<64, false>), mgrid, dim3(256), 0, stream, p);
-  } else if (p.rot) {
-    hipLaunchKernelGGL((chunk_split_kernel<128, true>), grid, dim3(kCThreads), 0, stream, p, nrg);
-    hipLaunchKernelGGL((chunk_merge_kernel<128, true>), rgrid, dim3(64 * kRotMergeRows), 128 * 128 * sizeof(float),
-                       stream, p);
+  if (D == 64) {
+    launch_chunk_split<64>(p, grid, nrg, stream);
+    if (p.rot)
+      hipLaunchKernelGGL((chunk_merge_kernel<64, true>), rgrid, dim3(64 * kRotMergeRows), 64 * 64 * sizeof(float),
+                         stream, p);
+    else
+      hipLaunchKernelGGL((chunk_merge_kernel<64, false>), mgrid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((chunk_split_kernel<128, false>), grid, dim3(kCThreads), 0, stream, p, nrg);
-    hipLaunchKernelGGL((chunk_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, p);
+    launch_chunk_split<128>(p, grid, nrg, stream);
+    if (p.rot)
+      hipLaunchKernelGGL((chunk_merge_kernel<128, true>), rgrid, dim3(64 * kRotMergeRows), 128 * 128 * sizeof(float),
+                         stream, p);
+    else
+      hipLaunchKernelGGL((chunk_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }

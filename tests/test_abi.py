@@ -418,14 +418,15 @@ def test_rotation_field():
 
 
 def test_code_width_field():
-    """code_bits: 0/4, 3 and 2 served; others UNSUPPORTED; the chunk takes 4
-    only; the checkpoint image's compressed slots scale as (16 w + 8) Hkv d."""
+    """code_bits: 0/4, 3 and 2 served (decode and chunk); others UNSUPPORTED;
+    the checkpoint image's compressed slots scale as (16 w + 8) Hkv d."""
     for cb in (0, 2, 3, 4):
         assert call(good_desc(code_bits=cb), ws=0) == akv.AKV_ERR_WORKSPACE, cb
     for cb in (1, 5, 8, -1):
         assert call(good_desc(code_bits=cb)) == akv.AKV_ERR_UNSUPPORTED, cb
-    assert call(good_desc(Tq=4, code_bits=2), chunk=True) == akv.AKV_ERR_UNSUPPORTED
-    assert "4-bit" in akv.akv_last_error()
+    for cb in (2, 3):
+        assert call(good_desc(Tq=4, code_bits=cb), chunk=True, ws=0) == akv.AKV_ERR_WORKSPACE, cb
+    assert call(good_desc(Tq=4, code_bits=5), chunk=True) == akv.AKV_ERR_UNSUPPORTED
     assert akv.akv_compress_evicted(compress_desc(code_bits=5)) == akv.AKV_ERR_UNSUPPORTED
     assert akv.akv_compress_evicted(compress_desc(code_bits=3, n_tokens=0)) == akv.AKV_OK
     assert akv.akv_append_evict(append_desc(code_bits=1)) == akv.AKV_ERR_UNSUPPORTED

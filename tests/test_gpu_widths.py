@@ -5,8 +5,8 @@ Codes and fp16 scales bit-exact against the oracle's encoder at the same
 width (read back through the width's documented byte layout); attention
 within the method's tolerances against the oracle's float64 attention over
 the dequantized history; the fused per-step append / evict, the host-staged
-decode and the checkpoint keep working at every width; the chunk refuses a
-width other than 4.
+decode, the checkpoint and the prefill chunk (also with a QR rotation) work
+at every width.
 """
 import copy
 
@@ -195,14 +195,41 @@ def test_narrow_checkpoint_round_trip():
     _say("width 2 checkpoint: restored bit-identically; width mismatch refused")
 
 
-def test_narrow_chunk_refused():
+@pytest.mark.parametrize("width", [2, 3])
+@pytest.mark.parametrize("cfg", [
+    # 160 rows: two row groups, the second ragged; several splits per tier
+    dict(B=1, Hq=8, Hkv=2, d=128, quant=[1000], exact=[300], Tq=40, split_exact=128, split_quant=256),
+    # head dim 64, a second sequence without a compressed tier
+    dict(B=2, Hq=4, Hkv=1, d=64, quant=[383, 0], exact=[129, 70], Tq=33, split_exact=64, split_quant=128),
+])
+def test_narrow_chunk_parity(width, cfg):
     akv, harness = _mods()
-    w = synth.make_small("narrow_chunk", B=1, Hq=8, Hkv=2, d=128, quant=[256], exact=[128], causal_tail=64)
-    dw = harness.DeviceWorkload(w, width=2)
-    desc = dw.desc()
-    dw.ensure_ws(desc, chunk=False)
-    st = akv.akv_attend_chunk(desc, harness.ptr(dw.ws), dw.ws_bytes, harness.stream_handle())
-    assert st == akv.AKV_ERR_UNSUPPORTED, akv.akv_last_error()
+    cfg = dict(cfg)
+    kw = {k: cfg.pop(k) for k in ("split_exact", "split_quant") if k in cfg}
+    w = synth.make_small("narrow_chunk", causal_tail=cfg["Tq"], outlier_frac=0.01, **cfg)
+    _say(f"width {width} chunk: B={w.B} Tq={w.Tq} Hq={w.Hq} Hkv={w.Hkv} d={w.d} quant={list(w.quant_len)} "
+         f"exact={list(w.exact_len)} {kw}")
+    dw = harness.DeviceWorkload(w, width=width)
+    akv.check(dw.attend(**kw))
+    torch.cuda.synchronize()
+    ek, ev = _enc(w, width)
+    assert_codes(dw, w, ek, ev, f"width {width} chunk")
+    o_ref, lse_ref = _ref(w, width, ek, ev)
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, f"width {width} chunk {cfg}")
+
+
+def test_narrow_chunk_with_qr_rotation():
+    akv, harness = _mods()
+    R = synth.qr_rotation(128, seed=9)
+    w = synth.make_small("narrow_chunk_qr", B=1, Hq=12, Hkv=2, d=128, quant=[700], exact=[90], Tq=20,
+                         causal_tail=20)
+    dw = harness.DeviceWorkload(w, rotation=R, width=3)
+    akv.check(dw.attend(split_quant=128))
+    torch.cuda.synchronize()
+    ek, ev = _enc(w, 3, R)
+    assert_codes(dw, w, ek, ev, "width 3 chunk, QR")
+    o_ref, lse_ref = _ref(w, 3, ek, ev, R)
+    assert_attention(dw.o.cpu().numpy(), dw.lse.cpu().numpy(), o_ref, lse_ref, "width 3 chunk, QR")
 
 
 @pytest.mark.slow
