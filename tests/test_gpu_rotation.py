@@ -141,6 +141,8 @@ def test_qr_staged_equals_resident():
     # head dim 64, outlier channels
     dict(B=1, Hq=4, Hkv=1, d=64, quant=[383], exact=[129], Tq=33, split_exact=64, split_quant=128,
          outlier_frac=0.02),
+    # one query (the chunk degenerates to decode; its queries are rotated one per workgroup)
+    dict(B=2, Hq=32, Hkv=4, d=128, quant=[1500, 64], exact=[100, 1], Tq=1),
 ])
 def test_qr_chunk_parity(cfg):
     akv, harness = _mods()
