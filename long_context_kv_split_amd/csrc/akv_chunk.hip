@@ -28,6 +28,11 @@
 // log-sum-exp) is written straight from registers.  A second kernel merges
 // each row's splits in ascending order: compressed-tier splits in rotated
 // space, one inverse rotation, exact-tier splits, then both tiers.
+// Variants (compile-time, so the 4-bit Walsh-Hadamard kernels are unchanged):
+// a caller-given rotation R (the query is rotated by R in a small kernel
+// before the splits and the merge applies R^T in place of the butterflies),
+// and code widths 2 and 3 (the narrow planes are turned into the same
+// two-code table fields, with 4^W-entry tables).
 #include "akv_common.h"
 #include "akv_params.h"
 
