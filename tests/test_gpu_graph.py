@@ -80,10 +80,14 @@ def test_decode_graph_replays(qr):
     _say(f"decode graph (qr={qr}): 5 replays bit-identical to eager")
 
 
-def test_chunk_graph_replays():
+@pytest.mark.parametrize("variant", ["hadamard", "qr_width3"])
+def test_chunk_graph_replays(variant):
     akv, harness = _mods()
     w = synth.make_small("graph_chunk", B=1, Hq=8, Hkv=2, d=128, quant=[700], exact=[300], causal_tail=96)
-    dw = harness.DeviceWorkload(w)
+    if variant == "hadamard":
+        dw = harness.DeviceWorkload(w)
+    else:  # the rotated-query kernel, the R^T merge and the 3-bit staging inside the capture
+        dw = harness.DeviceWorkload(w, rotation=synth.qr_rotation(128, seed=4), width=3)
     desc = dw.desc()
     dw.ensure_ws(desc, chunk=True)
 
@@ -95,8 +99,8 @@ def test_chunk_graph_replays():
     o_ref, l_ref = dw.o.clone(), dw.lse.clone()
     assert torch.isfinite(o_ref).all()
     g = _capture(call)
-    _replays_match(g, dw, o_ref, l_ref, 3, "chunk")
-    _say("chunk graph: 3 replays bit-identical to eager")
+    _replays_match(g, dw, o_ref, l_ref, 3, f"chunk {variant}")
+    _say(f"chunk graph ({variant}): 3 replays bit-identical to eager")
 
 
 def test_serving_step_graph_tracks_eager():
