@@ -435,12 +435,13 @@ def chunk_flops(w) -> float:
     return 4.0 * w.Tq * w.Hq * w.d * (hist / w.B + (w.Tq + 1) / 2.0) * w.B
 
 
-def bench_chunk(steps, warmup, stream, min_bytes=2 * MALL_BYTES):
-    """akv_attend_chunk on the 512-query chunk over a 32,768-token hybrid history."""
+def bench_chunk(steps, warmup, stream, min_bytes=2 * MALL_BYTES, rotation=None, width=4):
+    """akv_attend_chunk on the 512-query chunk over a 32,768-token hybrid history
+    (optionally with a given rotation or at code width 2 or 3)."""
     from long_context_kv_split_amd import akv, harness, synth
     w = synth.make("chunk")
-    dw = harness.DeviceWorkload(w)
-    kv_bytes = w.kv_bytes()
+    dw = harness.DeviceWorkload(w, rotation=rotation, width=width)
+    kv_bytes = w.kv_bytes(width)
     n_rep = max(1, -(-min_bytes // kv_bytes))
     dw.add_replicas(n_rep)
     descs = [dw.desc(r) for r in range(n_rep)]
@@ -521,6 +522,10 @@ def main():
                     help="skip the host-staged, checkpoint, per-step, rotation and code-width legs")
     ap.add_argument("--split-quant", type=int, default=0, help="compressed-tier split tokens (0 = library default)")
     ap.add_argument("--split-exact", type=int, default=0, help="exact-tier split tokens (0 = library default)")
+    ap.add_argument("--rotation", choices=("hadamard", "qr"), default="hadamard",
+                    help="with --only: the compressed tier's rotation (qr: a seeded random orthogonal one)")
+    ap.add_argument("--width", type=int, choices=(2, 3, 4), default=4,
+                    help="with --only: the compressed tier's code width")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -567,9 +572,13 @@ def main():
             log(f"bench: copied {args.copy_mb} MiB x3 (counter calibration)")
 
     if args.only:
+        from long_context_kv_split_amd import synth
+        variant = {"width": args.width}
+        if args.rotation == "qr":
+            variant["rotation"] = synth.qr_rotation(64 if args.only == "tiny" else 128, seed=0)
         with torch.cuda.stream(stream):
             if args.only == "chunk":
-                line = bench_chunk(args.steps, args.warmup, stream)
+                line = bench_chunk(args.steps, args.warmup, stream, **variant)
                 line.pop("_workload")
             else:
                 over = dict(OTHER_DECODE).get(args.only, {})
@@ -579,11 +588,13 @@ def main():
                     over["split_quant"] = args.split_quant
                 warm = 0.0 if args.only == "hybrid128k" else AUX_WARM_MS
                 w, dw, kvb, n_rep, ev_ms, wall_ms = bench_decode(args.only, args.steps, args.warmup, stream,
-                                                                 warm_ms=warm, **over)
+                                                                 warm_ms=warm, **over, **variant)
                 line = decode_line(args.only, w, dw, kvb, n_rep, ev_ms, wall_ms, args.steps)
             copy_calibration()
+        if (args.rotation != "hadamard" or args.width != 4) and line.get("roofline"):
+            line["roofline"]["traffic"] = None  # the counter records are for the 4-bit Walsh-Hadamard call
         log(f"bench: {args.only} {line['us_per_call']:.2f} us/call")
-        print(json.dumps({"only": args.only, **line}), flush=True)
+        print(json.dumps({"only": args.only, "rotation": args.rotation, "width": args.width, **line}), flush=True)
         return
 
     workloads = {}
