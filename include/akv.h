@@ -366,14 +366,16 @@ akv_status akv_attend_decode_staged(const akv_attn_desc* desc, const akv_staging
 
 /* Prefill-chunk attention: Tq causal queries per sequence over the two-tier
  * history (the prefill side of ActiveKV's two-tier cache; causal rule in the
- * akv_attn_desc comment).  Enqueues two kernels: a split kernel on 16x16x32
+ * akv_attn_desc comment).  Enqueues two kernels (three with a given
+ * rotation: the queries are rotated by R first): a split kernel on 16x16x32
  * matrix-core tiles in which every (128 (query, head) rows of a kv head,
  * split, sequence) workgroup expands each block of its split into LDS once
  * (compressed K as fp16 hi + lo parts against a hi + lo rotated query; exact
  * K/V as bf16) and writes one partial per row, then a merge kernel that per
  * (sequence, query, head) merges the partials in ascending split order,
- * inverse-rotates the compressed-tier result once and merges the tiers.
- * Repeated calls give identical bytes.  A sequence whose exact length is
+ * inverse-rotates the compressed-tier result once (R^T with a given
+ * rotation) and merges the tiers.  Every code width of "Code width" is
+ * served.  Repeated calls give identical bytes.  A sequence whose exact length is
  * below Tq (the chunk must be in the exact tier) or whose lengths are out of
  * range gets NaN outputs.  ws as for decode, with
  * akv_chunk_workspace_bytes(desc) bytes. */
